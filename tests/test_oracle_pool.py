@@ -1,0 +1,150 @@
+"""Pins of the pool model and the memory arithmetic: the worked example's printed values, a trace
+derived by hand from the pool sketch, and invariants under random operation sequences."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (UnifiedPoolModel, adapter_bytes, gather_page_ids, expected_page_rows,
+                    h2d_seconds, kv_bytes_per_token, kv_pages_per_token, pages_for_adapter,
+                    tp_comm_base, tp_comm_lora)
+
+KiB, MiB, GiB = 1024, 1024 ** 2, 1024 ** 3
+
+
+@pytest.fixture
+def worked(golden_dir):
+    with open(os.path.join(golden_dir, "slora_worked_example.json")) as f:
+        return json.load(f)
+
+
+@pytest.fixture
+def traces(golden_dir):
+    with open(os.path.join(golden_dir, "pool_trace.json")) as f:
+        return json.load(f)["traces"]
+
+
+def test_worked_example_kv(worked):
+    m = worked["model"]
+    assert kv_pages_per_token(m["layers"]) == worked["kv_vectors_per_token"]
+    assert kv_bytes_per_token(m["layers"], m["hidden"], m["elem_bytes"]) == worked["kv_bytes_per_token"]
+    assert worked["kv_bytes_per_token"] == 512 * KiB
+
+
+def test_worked_example_adapter(worked):
+    m, a = worked["model"], worked["adapter"]
+    assert pages_for_adapter(a["rank"], 1, a["projections"]) == worked["adapter_vectors_per_layer"]
+    assert pages_for_adapter(a["rank"], m["layers"], a["projections"]) == worked["adapter_vectors_total"]
+    nbytes = adapter_bytes(a["rank"], m["layers"], a["projections"], m["hidden"], m["elem_bytes"])
+    assert nbytes == worked["adapter_bytes"] == 32 * MiB
+    kv = kv_bytes_per_token(m["layers"], m["hidden"], m["elem_bytes"])
+    assert nbytes // kv == worked["kv_tokens_per_adapter"] and nbytes % kv == 0
+
+
+def test_worked_example_rounded_figures(worked):
+    m, a = worked["model"], worked["adapter"]
+    nbytes = adapter_bytes(a["rank"], m["layers"], a["projections"], m["hidden"], m["elem_bytes"])
+    kv = kv_bytes_per_token(m["layers"], m["hidden"], m["elem_bytes"])
+    per_ctx = worked["context_tokens"] * kv / nbytes           # 31.25: "about 31"
+    assert round(per_ctx) == worked["adapters_per_context_approx"]
+    total_gib = worked["n_adapters"] * nbytes / GiB              # 62.5: "about 62"
+    assert int(total_gib) == worked["all_adapters_gib_approx"]
+    p = worked["prefetch"]
+    ms = 1e3 * h2d_seconds(p["adapter_bytes"], p["link_bytes_per_s"])   # 1.68: "roughly 1.6 ms"
+    assert abs(ms - p["copy_ms_approx"]) < 0.1
+
+
+def test_tensor_parallel_ratio(worked):
+    tp = worked["tensor_parallel"]
+    for n in (2, 4, 8):
+        ratio = tp_comm_lora(n, 64, tp["rank"]) / tp_comm_base(n, 64, tp["hidden"])
+        assert ratio == pytest.approx(5 * 16 / (2 * 4096)) and ratio < tp["ratio_bound"]
+
+
+def test_rank_slot_ratio(worked):
+    r = worked["rank_slot_ratio"]
+    assert pages_for_adapter(r["big_rank"], 32, 4) == r["ratio"] * pages_for_adapter(r["small_rank"], 32, 4)
+
+
+def _apply(pool, step, n_slots):
+    op = step["op"]
+    if op == "load":
+        before = list(pool.free)
+        st = pool.ensure_adapter(step["aid"], step["rank"], n_slots)
+        taken = [] if st != "ok" or step["aid"] in pool.adapter_pages and pool.adapter_refs[step["aid"]] > 1 \
+            else pool.adapter_pages[step["aid"]]
+        return st, taken, before
+    if op == "kv":
+        n0 = len(pool.kv_pages.get(step["rid"], []))
+        st = pool.grow_kv(step["rid"], step["layers"])
+        return st, pool.kv_pages.get(step["rid"], [])[n0:], None
+    if op == "free_kv":
+        return pool.free_kv(step["rid"]), None, None
+    if op == "release":
+        return pool.release(step["aid"]), None, None
+    if op == "evict":
+        return pool.evict(step["aid"]), None, None
+    raise ValueError(op)
+
+
+def test_hand_derived_traces(traces):
+    for tr in traces:
+        pool = UnifiedPoolModel(tr["num_pages"])
+        for step in tr["steps"]:
+            st, taken, _ = _apply(pool, step, tr["n_slots"])
+            assert st == step["status"], step
+            if "pages" in step:
+                assert list(taken or []) == step["pages"], step
+        fin = tr["final"]
+        assert pool.free == fin["free"]
+        assert list(pool.adapter_pages) == fin["resident_in_load_order"]
+        assert {str(k): v for k, v in pool.kv_pages.items()} == fin["kv"]
+        for key in [k for k in fin if k.startswith("page_table_slot")]:
+            slot = int(key[len("page_table_slot"):])
+            pt = pool.page_table(slot, tr["max_adapters"], tr["max_rank"])
+            for a, row in fin[key].items():
+                assert list(pt[int(a)]) == row, (key, a)
+
+
+def test_random_ops_invariants():
+    rng = np.random.default_rng(0)
+    for trial in range(20):
+        n = int(rng.integers(10, 200))
+        pool = UnifiedPoolModel(n, rng.permutation(n))
+        n_slots = int(rng.integers(1, 4))
+        for _ in range(200):
+            k = rng.integers(0, 5)
+            if k == 0:
+                pool.ensure_adapter(int(rng.integers(0, 8)), int(rng.integers(0, 5)), n_slots)
+            elif k == 1:
+                pool.grow_kv(int(rng.integers(0, 6)), int(rng.integers(1, 3)))
+            elif k == 2:
+                pool.free_kv(int(rng.integers(0, 6)))
+            elif k == 3:
+                pool.release(int(rng.integers(0, 8)))
+            else:
+                pool.evict(int(rng.integers(0, 8)))
+            used = [p for v in pool.adapter_pages.values() for p in v] + [p for v in pool.kv_pages.values() for p in v]
+            every = used + pool.free
+            assert sorted(every) == list(range(n))          # conserved and pairwise distinct
+            for aid, pages in pool.adapter_pages.items():
+                assert len(pages) == 2 * pool.adapter_rank[aid] * n_slots
+                assert pool.adapter_refs[aid] >= 0
+
+
+def test_gather_ids_hand_table():
+    pt = np.array([[5, 9, 2, 7], [-1, -1, -1, -1], [3, 4, -1, -1]])
+    ranks = np.array([2, 0, 1])
+    got = gather_page_ids(pt, np.array([2, -1, 0, 1, 0]), ranks, max_rank=2)
+    want = np.array([[3, 4, -1, -1], [-1] * 4, [5, 9, 2, 7], [-1] * 4, [5, 9, 2, 7]])
+    assert np.array_equal(got, want)
+
+
+def test_expected_page_rows():
+    pt = np.array([[5, 9, 2, 7]])
+    At = np.arange(8).reshape(2, 4)
+    B = 100 + np.arange(8).reshape(2, 4)
+    rows = expected_page_rows(pt, 0, 2, At, B)
+    assert [p for p, _ in rows] == [5, 9, 2, 7]
+    assert np.array_equal(rows[0][1], At[0]) and np.array_equal(rows[3][1], B[1])
