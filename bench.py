@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the unmerged multi-LoRA projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|many|tiny]
+
+A step is one pass of the whole projection (token grouping, shrink, base GEMM + expand) over one
+batch of the workload, with every input already resident in HBM.  The default workload is the
+Llama-7B-shaped q_proj decode batch: H = 4096, bf16, 32 adapters of ranks {8, 16, 32, 64},
+64 tokens (one per request), pages scattered through a pool that is 60 % KV pages.
+
+HBM honesty: the 256 MiB Infinity Cache would hold one replica of the decode working set, so the
+timed loop rotates through enough independent replicas (pool, page table, W, x, y) to touch
+>= 1 GiB between reuses.
+
+Prints one JSON line: the throughput, the dominant kernel's roofline fraction (its algorithmic
+bytes or flops over its average device time, from HIP events recorded on its launch stream), and
+the fp64 CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "multi-LoRA proj tokens/s + %HBM/%MFMA roofline, H=4096, 32 adapters, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, T_ids, slots):
+    """Bytes and flops the method itself must move/compute per step, and the main kernel's share.
+
+    Per projection call: W once (H^2 e), x in and y out (2 T H e), each A and B page of every
+    distinct adapter the batch uses once (2 r H e), the ids (4 T).  Flops: 2 T H^2 + 4 H r per
+    token with an adapter.  The main kernel (base GEMM + expand) reads W, x, the B pages and
+    writes y; it computes 2 T H^2 + 2 H r per adapter token.
+    """
+    H, e = w.hidden, w.elem
+    ids = T_ids
+    distinct = sorted({int(a) for a in ids if a >= 0 and w.ranks[a] > 0})
+    r_sum_distinct = sum(int(w.ranks[a]) for a in distinct)
+    r_sum_tokens = sum(int(w.ranks[a]) for a in ids if a >= 0)
+    T = len(ids)
+    per_call_bytes = H * H * e + 2 * T * H * e + 2 * r_sum_distinct * H * e + 4 * T
+    per_call_flops = 2 * T * H * H + 4 * H * r_sum_tokens
+    main_bytes = H * H * e + 2 * T * H * e + r_sum_distinct * H * e
+    main_flops = 2 * T * H * H + 2 * H * r_sum_tokens
+    return {
+        "bytes": per_call_bytes * slots, "flops": per_call_flops * slots,
+        "main_bytes": main_bytes, "main_flops": main_flops,
+        "distinct_adapters": len(distinct), "r_sum_distinct": r_sum_distinct,
+    }
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key, src_file, launches_bytes_ok=True):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were taken on the
+    current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256_16") != source_hash(src_file):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds, slots):
+    """The fp64 oracle, as it stands, on this host's cores: full batch of one projection, repeated."""
+    import numpy as np
+    import oracle
+    from workloads import storage_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    slot = 0
+    x64 = storage_to_f64(w.x_for_slot(slot))
+    W64 = storage_to_f64(w.W(slot)).T
+    A, B = {}, {}
+    for a in sorted({int(a) for a in w.ids if a >= 0 and w.ranks[a] > 0}):
+        at, b = w.adapter(a)
+        A[a], B[a] = storage_to_f64(at[slot]).T, storage_to_f64(b[slot])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.project(x64, W64, A, B, w.ids, w.scales)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    tokens_per_s = n * w.T / el / slots      # a step pushes T tokens through `slots` projections
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"full {w.T}-token batch of one projection (slot 0), {n} repeats in {el:.1f} s, "
+                      f"scaled to {slots} projection(s) per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny"])
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
+    ap.add_argument("--profile-calls", type=int, default=400)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    rank = int(os.environ.get("RANK", "0"))
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        if rank == 0:
+            print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the projection is "
+                  "data-parallel over tokens and its multi-GPU sharding is a design note, not a run", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import rank_gemm_unified_amd as rg
+    from workloads import build
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = build(args.workload, device="cuda")
+    slots = list(range(w.n_slots))
+    info = algorithmic(w, w.ids, len(slots))
+    log(f"workload {w.name}: H={w.hidden} T={w.T} slots={len(slots)} adapters={w.max_adapters} "
+        f"distinct={info['distinct_adapters']} step bytes={info['bytes'] / 2**20:.1f} MiB "
+        f"flops={info['flops'] / 1e9:.2f} G")
+
+    if args.replicas:
+        R = args.replicas
+    else:
+        R = max(2, math.ceil(2 ** 30 / max(info["bytes"], 1)))
+    R = min(R, 64)
+    dcode = rg.LORA_F32 if w.dtype == "f32" else rg.LORA_BF16
+    d_ids = torch.as_tensor(w.ids, device=dev)
+    d_ranks = torch.as_tensor(w.ranks, device=dev)
+    d_scale = torch.as_tensor(w.scales, device=dev)
+    reps = []
+    for i in range(R):
+        pool = rg.Pool(w.num_pages, w.hidden, dcode, n_slots=w.n_slots, max_adapters=w.max_adapters,
+                       free_order=w.free_order)
+        st = pool.run_ops(w.ops, w.ranks, w.adapter)
+        assert all(s == 0 for s in st), rg.lora_last_error()
+        Ws = [w.W(s).clone() for s in slots]
+        xs = [w.x(i2).clone() for i2 in range(w.n_x)]
+        ys = [torch.empty_like(xs[0]) for _ in slots]
+        ws = pool.workspace(w.T)
+        reps.append((pool, Ws, xs, ys, ws))
+        if w.name == "many":
+            w.drop_cache("AB")
+    wsb = reps[0][4].numel()
+    log(f"replicas: {R}")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        pool, Ws, xs, ys, ws = reps[i % R]
+        for s in slots:
+            rg._lib.lora_project(pool.handle, xs[w.slot_x[s]].data_ptr(), Ws[s].data_ptr(), pool.table[s].data_ptr(),
+                                 d_ids.data_ptr(), d_ranks.data_ptr(), d_scale.data_ptr(), w.T, ys[s].data_ptr(),
+                                 ws.data_ptr(), wsb, sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(reps[0][0].handle, check=False) == 0, rg.lora_last_error()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    tokens_per_s = w.T / (ms_per_step / 1e3)
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
+        f"step algorithmic {info['bytes'] / (ms_per_step / 1e3) / 1e9:.0f} GB/s")
+
+    # per-kernel device time from HIP events on the launch stream (separate loop: events add gaps)
+    calls_per_rep = max(1, args.profile_calls // R)
+    for pool, *_ in reps:
+        rg.lora_profile_start(pool.handle, calls_per_rep * len(slots))
+    for i in range(calls_per_rep * R):
+        step(i)
+    torch.cuda.synchronize()
+    prof = {"calls": 0, "ms_segments": 0.0, "ms_shrink": 0.0, "ms_main": 0.0}
+    for pool, *_ in reps:
+        pr = rg.lora_profile_stop(pool.handle)
+        for k in prof:
+            prof[k] += pr[k]
+    n = max(prof["calls"], 1)
+    avg = {k: prof[k] / n * 1e3 for k in ("ms_segments", "ms_shrink", "ms_main")}   # microseconds
+    log(f"kernel avg (us): segments {avg['ms_segments']:.2f} shrink {avg['ms_shrink']:.2f} "
+        f"main {avg['ms_main']:.2f}  over {prof['calls']} calls")
+
+    main_s = avg["ms_main"] / 1e6
+    decode_like = w.T <= 256
+    if decode_like:
+        achieved = info["main_bytes"] / main_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "kernel": "k_base_expand (base GEMM + fused expand)",
+                "algorithmic_bytes_per_launch": info["main_bytes"], "avg_launch_us": avg["ms_main"],
+                "traffic": traffic_from_profiles("decode_main", os.path.join(ROOT, "rank_gemm_unified_amd", "csrc",
+                                                                              "k_decode.hip"))}
+    else:
+        achieved = info["main_flops"] / main_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)",
+                "algorithmic_flops_per_launch": info["main_flops"], "avg_launch_us": avg["ms_main"],
+                "traffic": traffic_from_profiles("prefill_main", os.path.join(ROOT, "rank_gemm_unified_amd", "csrc",
+                                                                               "k_prefill.hip"))}
+
+    cpu = None
+    if not args.no_cpu_baseline and rank == 0:
+        log("timing the fp64 oracle on the host ...")
+        cpu = cpu_baseline(w, args.cpu_seconds, len(slots))
+
+    desc = {
+        "decode": "Llama-7B-shaped q_proj decode: H=4096 bf16, 32 adapters ranks U{8,16,32,64}, 64 tokens "
+                  "(1 per request), pool 60% KV pages",
+        "prefill": "prefill grouped GEMM: H=4096 bf16, 8 requests x 512 tokens, ranks {8,8,16,16,32,32,64,64}",
+        "many": "2000 adapters, q/k/v/o of one layer, H=4096 bf16, 256 decode tokens Zipf(1.0), 10% identity",
+        "tiny": "tiny: H=256 fp32, 4 adapters, 16 tokens",
+    }[w.name]
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": desc, "hidden": w.hidden, "tokens": w.T, "projections_per_step": len(slots),
+                   "adapters": w.max_adapters, "distinct_adapters_in_batch": info["distinct_adapters"],
+                   "replicas_rotated": R, "parallelism": "single GPU"},
+        "step_algorithmic_bytes": info["bytes"], "step_algorithmic_flops": info["flops"],
+        "step_hbm_GBps": info["bytes"] / (ms_per_step / 1e3) / 1e9,
+        "step_hbm_frac": info["bytes"] / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "kernel_avg_us": avg,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+/*
+ * lorapool.h -- unmerged multi-LoRA projection over a unified page pool, for AMD Instinct MI355X
+ * (gfx950).  Plain C ABI: opaque pool handle, plain pointers and sizes, int status codes.
+ *
+ * What it computes ("S-LoRA, in depth", section "Merge or keep adapters separate"): a LoRA adapter
+ * turns an h-by-h weight W into W + AB with A h-by-r and B r-by-h; a token with activation x gets
+ * xW + (xA)B.  Unmerged serving keeps W shared, batches xW over every token whatever its adapter,
+ * and adds the low-rank term per token.  This library computes, for T tokens in one call,
+ *
+ *     y[t] = x[t] W + s[a] * (x[t] A_a) B_a        a = adapter_ids[t]
+ *
+ * and y[t] = x[t] W when a == -1 or the adapter has rank 0 (the weightless "identity" adapter of
+ * "Switch Adapters by Routing Requests Through Resident, Verified State", its adapter registry).
+ * The per-adapter float scale s[a] is this library's reading of the usual LoRA scaling; s = 1
+ * gives the page's formula.
+ *
+ * Where A and B live ("S-LoRA, in depth", section "Unified paging: adapters and KV cache in one
+ * pool"): a pool of pages, each one vector of H elements, shared by KV cache and adapters through
+ * one free list.  An adapter of rank r on one projection takes 2r pages: the r columns of A and
+ * the r rows of B.  Pages need not be contiguous or in order; a per-projection page table maps
+ * (adapter, j) to a page, and the projection's gather reads each token's pages wherever they sit
+ * (same page, section "The architecture").
+ *
+ * Conventions for every function returning int:
+ *   0 = LORA_OK, negative = error (below).  No C++ exception crosses this boundary.  On error,
+ *   lora_last_error() returns a message for the calling thread, valid until its next call.
+ *   Arguments are validated on the host before any device work; an invalid call leaves every
+ *   caller buffer untouched.
+ * Streams: `stream` arguments are hipStream_t values passed as void* (NULL = the null stream).
+ *   All device work of a call is enqueued on that stream, in call order, so a load followed by a
+ *   projection on the same stream sees the new weights.  Ordering across streams is the caller's
+ *   job (events).
+ * Memory ownership: the caller owns every device buffer (pool pages, page table, x, W, y, ids,
+ *   ranks, scales, workspace).  The library owns only host bookkeeping plus two small device
+ *   buffers it allocates at pool creation (a staging buffer for loads and a device error word),
+ *   freed by lora_pool_free.
+ * Threads: calls that change a pool (load, release, evict, KV) take the pool's mutex.
+ *   lora_project changes no pool state and holds no "active adapter": adapter choice is per token,
+ *   carried by adapter_ids (the routing page's warning against a shared mutable active adapter).
+ */
+#ifndef LORAPOOL_H
+#define LORAPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lora_status {
+    LORA_OK = 0,
+    LORA_EINVAL = -1,   /* bad argument: null/misaligned pointer, size, dtype, range            */
+    LORA_ENOMEM = -2,   /* not enough free pages (or a library allocation failed)              */
+    LORA_ENOENT = -3,   /* unknown adapter / request id                                        */
+    LORA_ERANK = -4,    /* rank out of range, or not the rank the adapter was loaded at        */
+    LORA_EBUSY = -5,    /* adapter still has users                                             */
+    LORA_EEXIST = -6,   /* adapter already resident at another rank                            */
+    LORA_EHIP = -7,     /* a HIP runtime call failed (message has the HIP error string)        */
+    LORA_EDEVICE = -8   /* an earlier projection found bad ids/ranks/pages on the device       */
+};
+
+enum lora_dtype {
+    LORA_F32 = 0,       /* pages, x, W, A, B, y in IEEE float32                                 */
+    LORA_BF16 = 1       /* ... in bfloat16; products accumulate in float32                      */
+};
+
+#define LORA_MAX_RANK 64        /* largest rank a pool can be created for                       */
+#define LORA_MAX_ADAPTERS 8192  /* largest adapter id + 1                                       */
+
+typedef struct lora_pool lora_pool;
+
+typedef struct lora_pool_stats {
+    int64_t num_pages;          /* pool size                                                    */
+    int64_t free_pages;         /* on the free list                                             */
+    int64_t kv_pages;           /* held by KV requests                                          */
+    int64_t adapter_pages;      /* held by resident adapters                                    */
+    int32_t resident_adapters;  /* adapters holding pages (rank-0 adapters count, with 0 pages) */
+    int32_t idle_adapters;      /* resident adapters with no users                              */
+    int64_t kv_requests;        /* requests holding KV pages                                    */
+    int64_t loads;              /* adapter loads that allocated pages (not refcount bumps)      */
+    int64_t evictions;          /* adapters whose pages were reclaimed                          */
+    int64_t bytes_loaded;       /* bytes copied into pages by loads                             */
+} lora_pool_stats_t;
+
+/* ---- pool lifecycle ("Unified paging" section and its pool sketch) ------------------------- */
+
+/*
+ * Create a pool over caller-owned device memory.
+ *   pages        device, num_pages * hidden elements of `dtype`, 16-byte aligned.  Page p is the
+ *                hidden-element vector at pages + p * hidden.
+ *   num_pages    >= 1.
+ *   hidden       H, the page length and the projection's input and output width; a multiple of
+ *                64, 64 <= H <= 65536.
+ *   dtype        LORA_F32 or LORA_BF16.
+ *   max_rank     1..LORA_MAX_RANK; every adapter's rank must be <= max_rank.
+ *   n_slots      projections per adapter (layers * projections, e.g. 32 * 4 for q/k/v/o of a
+ *                7B model); each slot has its own page-table block.
+ *   max_adapters adapter ids are 0..max_adapters-1 (<= LORA_MAX_ADAPTERS).
+ *   page_table   device int32 [n_slots][max_adapters][2*max_rank], caller-owned, 4-byte aligned.
+ *                Row (slot, a) lists adapter a's pages for that slot: entries 0..r-1 the columns
+ *                of A, r..2r-1 the rows of B, -1 after that.  The library writes it (set to -1
+ *                here, synchronously); callers only read it.
+ *   free_order   host int64 [num_pages], a permutation of 0..num_pages-1 giving the initial free
+ *                list, or NULL for 0..num_pages-1.  Allocation takes pages from the END of the
+ *                list and frees append to it (the sketch's pop and extend), so the default hands
+ *                out num_pages-1 first.
+ *   out          receives the handle.
+ * pages and page_table may both be NULL: a bookkeeping-only pool that allocates and accounts
+ * pages but touches no device memory (loads copy nothing; projections are refused).
+ * Errors: LORA_EINVAL (bad argument, free_order not a permutation), LORA_EHIP.
+ */
+int lora_pool_create(void *pages, int64_t num_pages, int32_t hidden, int32_t dtype,
+                     int32_t max_rank, int32_t n_slots, int32_t max_adapters, int32_t *page_table,
+                     const int64_t *free_order, lora_pool **out);
+
+/* Destroy the pool's bookkeeping and library-owned device buffers; waits for the pool's pending
+ * loads first.  Caller buffers are untouched.  NULL is accepted.  Returns LORA_OK or LORA_EHIP. */
+int lora_pool_free(lora_pool *pool);
+
+/*
+ * Make adapter `adapter_id` resident at `rank` (0..max_rank), as the sketch's ensure_adapter:
+ *   - already resident at the same rank: one more user (refcount + 1); nothing is copied;
+ *   - already resident at another rank: LORA_EEXIST;
+ *   - otherwise it needs 2 * rank * n_slots pages; if fewer are free, idle adapters (no users)
+ *     are evicted oldest-load first until enough are free; if even that is not enough the call
+ *     returns LORA_ENOMEM with no pages taken (idle adapters evicted on the way stay evicted,
+ *     as in the sketch).  On success the adapter has one user.
+ * The adapter's page list takes pages from the free list in order; list entry i belongs to slot
+ * i / (2r), entry i % (2r) of that slot's table row.
+ *   A_t  [n_slots][rank][hidden] of the pool dtype: row j of slot s is column j of that slot's A.
+ *   B    [n_slots][rank][hidden]: row j of slot s is row j of that slot's B.
+ * A_t and B may be host (pageable or pinned) or device memory; they are read during the call
+ * for pageable memory and, otherwise, by work on `stream`: keep them alive and unchanged until
+ * the stream has passed this call.  Both may be NULL when rank == 0 or the pool is
+ * bookkeeping-only.  The copies and the page-table update are enqueued on `stream`.
+ * Errors: LORA_EINVAL, LORA_ERANK (rank > max_rank), LORA_EEXIST, LORA_ENOMEM, LORA_EHIP.
+ */
+int lora_pool_load_adapter(lora_pool *pool, int32_t adapter_id, int32_t rank, const void *A_t,
+                           const void *B, void *stream);
+
+/* One user of the adapter finished (refcount - 1).  At zero users it stays resident but idle and
+ * becomes evictable.  Errors: LORA_ENOENT (not resident), LORA_EINVAL (already idle). */
+int lora_pool_release_adapter(lora_pool *pool, int32_t adapter_id);
+
+/* Reclaim an idle adapter's pages ("When an adapter has no active requests left, its pages can be
+ * reclaimed", section "The architecture"): they return to the end of the free list in page-list
+ * order, and the adapter's page-table rows are reset to -1 on `stream`.  The caller must not
+ * evict an adapter that queued, unfinished projections still read.
+ * Errors: LORA_ENOENT, LORA_EBUSY (has users). */
+int lora_pool_evict_adapter(lora_pool *pool, int32_t adapter_id, void *stream);
+
+/* Grow request `request_id`'s KV cache by one token: 2 * layers pages (K and V per layer), as the
+ * sketch's grow_kv.  If page_ids_out is not NULL it receives the 2*layers page ids (host int64).
+ * Errors: LORA_ENOMEM (caller must preempt or abort a request), LORA_EINVAL. */
+int lora_pool_grow_kv(lora_pool *pool, int64_t request_id, int32_t layers, int64_t *page_ids_out);
+
+/* Request finished: its KV pages return to the end of the free list.  Errors: LORA_ENOENT. */
+int lora_pool_free_kv(lora_pool *pool, int64_t request_id);
+
+/* ---- queries (host only, no device work) ----------------------------------------------------- */
+
+/* Pages for an adapter of `rank` on `projections` projections of `layers` layers:
+ * rank * 2 * projections * layers (A and B per projection).  Negative input gives -1. */
+int64_t lora_pool_pages_for(int32_t rank, int32_t projections, int32_t layers);
+
+/* KV pages one token takes: 2 * layers (K and V per layer).  Negative input gives -1. */
+int64_t lora_kv_pages_per_token(int32_t layers);
+
+int lora_pool_stats(const lora_pool *pool, lora_pool_stats_t *out);
+
+/* Device pointer to `slot`'s page-table block [max_adapters][2*max_rank] and its row stride in
+ * elements (2*max_rank).  Errors: LORA_EINVAL (slot out of range, bookkeeping-only pool). */
+int lora_pool_page_table(const lora_pool *pool, int32_t slot, const int32_t **table,
+                         int32_t *row_stride);
+
+/* Copy adapter `adapter_id`'s page list (2 * rank * n_slots ids, in list order) into out[cap];
+ * *n_out = its length, *rank_out = its rank, *users_out = its refcount (each may be NULL).
+ * Errors: LORA_ENOENT, LORA_EINVAL (cap too small: *n_out still set). */
+int lora_pool_adapter_pages(const lora_pool *pool, int32_t adapter_id, int64_t *out, int64_t cap,
+                            int64_t *n_out, int32_t *rank_out, int32_t *users_out);
+
+/* Copy request `request_id`'s KV page list into out[cap]; *n_out = its length.
+ * Errors: LORA_ENOENT, LORA_EINVAL (cap too small). */
+int lora_pool_kv_pages(const lora_pool *pool, int64_t request_id, int64_t *out, int64_t cap,
+                       int64_t *n_out);
+
+/* Copy the free list (front to end; allocation takes from the end) into out[cap]. */
+int lora_pool_free_list(const lora_pool *pool, int64_t *out, int64_t cap, int64_t *n_out);
+
+/* Resident adapter ids in load order (oldest first), the order idle eviction follows. */
+int lora_pool_resident(const lora_pool *pool, int32_t *out, int32_t cap, int32_t *n_out);
+
+/* ---- the projection --------------------------------------------------------------------------- */
+
+/* Bytes of device workspace lora_project needs for T tokens on this pool (256-byte aligned). */
+size_t lora_project_workspace_size(const lora_pool *pool, int64_t T);
+
+/*
+ * y = x W + s * (x A) B for T tokens, each on its own adapter (sections "Merge or keep adapters
+ * separate" and "The architecture" of "S-LoRA, in depth").
+ *   x            device [T][H], pool dtype, row-major, 16-byte aligned.
+ *   W            device [H][H], pool dtype, OUT-MAJOR: element (k, n) of W (input k, output n)
+ *                is W[n * H + k] -- the layout of a linear layer's weight matrix.  16-byte aligned.
+ *   page_table   device: one slot's block [max_adapters][2*max_rank] (lora_pool_page_table).
+ *   adapter_ids  device int32 [T]: adapter per token, -1 = none.
+ *   ranks        device int32 [max_adapters]: rank per adapter; must equal the loaded rank for
+ *                every adapter a token uses (entries of unused adapters are not read).
+ *   scale        device float32 [max_adapters]: s per adapter.
+ *   y            device [T][H], pool dtype, 16-byte aligned; must not overlap x.  Each element is
+ *                accumulated in float32 (base and low-rank parts together) and rounded once to the
+ *                pool dtype (round to nearest even).
+ *   workspace    device, >= lora_project_workspace_size(pool, T) bytes, 256-byte aligned; its
+ *                contents on entry do not matter.  Calls that share a workspace must be ordered
+ *                (same stream, or events).
+ * T == 0 is a no-op.  Ids, ranks and page ids are checked on the device: a token whose adapter id
+ * is out of range, whose rank is out of range or differs from the page table, or whose page ids
+ * are out of range gets the base product only, and the pool's device error word records the
+ * fault; lora_check_device_errors() reports and clears it.
+ * Errors (host-side, before any device work): LORA_EINVAL, LORA_EHIP.
+ */
+int lora_project(lora_pool *pool, const void *x, const void *W, const int32_t *page_table,
+                 const int32_t *adapter_ids, const int32_t *ranks, const float *scale, int64_t T,
+                 void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Debug view of the gather: for every token t (input order) writes the pages its projection reads
+ * into page_ids_out[t][0..2*max_rank) (device int32): entries 0..r-1 its A columns, r..2r-1 its B
+ * rows, -1 elsewhere and for tokens with no adapter or rank 0.  Same inputs and device checks as
+ * lora_project (an invalid token gets all -1).  Enqueued on `stream`.
+ */
+int lora_debug_gather(lora_pool *pool, const int32_t *page_table, const int32_t *adapter_ids,
+                      const int32_t *ranks, int64_t T, int32_t *page_ids_out, void *stream);
+
+/* Wait for all device work, then report and clear the pool's device error word:
+ * LORA_OK, or LORA_EDEVICE with a message naming the kinds of fault seen. */
+int lora_check_device_errors(lora_pool *pool);
+
+/* ---- per-kernel timing (opt-in, for measurement) ---------------------------------------------- */
+
+typedef struct lora_profile {
+    int64_t calls;              /* projections recorded                                          */
+    double ms_segments;         /* summed device time of the token-grouping kernel               */
+    double ms_shrink;           /* ... of the shrink kernel (x A)                                */
+    double ms_main;             /* ... of the base GEMM + expand kernel                          */
+    double ms_main_min, ms_main_max;
+} lora_profile_t;
+
+/* Start recording HIP events around each kernel of the next `max_calls` projections on this
+ * pool, on the stream each kernel is launched on.  Recording adds event records between the
+ * kernels; time the throughput without it.  Errors: LORA_EINVAL, LORA_EHIP. */
+int lora_profile_start(lora_pool *pool, int32_t max_calls);
+
+/* Wait for the recorded work, fill *out with per-kernel sums, and stop recording. */
+int lora_profile_stop(lora_pool *pool, lora_profile_t *out);
+
+/* Message for the calling thread's last error ("" if none). */
+const char *lora_last_error(void);
+
+/* Library version string. */
+const char *lora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORAPOOL_H */

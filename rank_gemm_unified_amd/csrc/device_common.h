@@ -1,0 +1,73 @@
+// Device-side helpers shared by the kernels: element conversions, vector types, wave reductions,
+// and the page-table row check used by every kernel that gathers pages.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace lorapool {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even float32 -> bfloat16 bits; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// 8 bf16 values (one 16-byte load) -> 8 floats
+__device__ __forceinline__ void unpack_bf16x8(const u32x4_t &v, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ u32x4_t pack_bf16x8(const float *f) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+    return v;
+}
+
+__device__ __forceinline__ u32x4_t load16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+__device__ __forceinline__ void store16(void *p, const u32x4_t &v) { *reinterpret_cast<u32x4_t *>(p) = v; }
+
+// Sum over the 64 lanes of a wave; every lane gets the total.  Fixed butterfly order, so the
+// result does not depend on anything but the 64 inputs.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Check adapter a's page-table row against rank r: entries [0, 2r) must be page ids in
+// [0, num_pages) and, when 2r < stride, entry 2r must be -1 (so r is the loaded rank).
+// `j` is this thread's entry (threads of a group cover the row together); returns error bits.
+__device__ __forceinline__ int check_row_entry(const int32_t *row, int32_t j, int32_t r, int32_t stride,
+                                               int64_t num_pages) {
+    if (j < 2 * r) {
+        const int32_t pg = row[j];
+        if (pg == -1) return 4;                                   // DEV_ERR_TABLE
+        if (pg < 0 || (int64_t)pg >= num_pages) return 8;         // DEV_ERR_PAGE
+    } else if (j == 2 * r && j < stride) {
+        if (row[j] != -1) return 4;                               // DEV_ERR_TABLE
+    }
+    return 0;
+}
+
+}  // namespace lorapool

@@ -1,0 +1,209 @@
+// lora_project: host-side validation, workspace planning and kernel dispatch.
+//
+// Per call:  segment kernel (validate ids/ranks/pages, group tokens by adapter)
+//            -> shrink  v = s * x A        (gathered A columns)
+//            -> base + expand  y = x W + v B  (gathered B rows, one rounding)
+// Decode-shaped calls (T <= 256) stream W once with a split-K MFMA kernel; prefill-shaped calls
+// use the tiled MFMA GEMM.  The choice depends only on T and the dtype, both known on the host.
+#include <algorithm>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace lorapool;
+
+namespace lorapool {
+
+constexpr int64_t MAX_TOKENS = int64_t(1) << 22;
+constexpr int64_t DECODE_MAX_T = 256;
+
+static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
+    if (!p || T < 0 || T > MAX_TOKENS) return false;
+    memset(pl, 0, sizeof *pl);
+    pl->T = T;
+    const int64_t R = p->max_rank, H = p->hidden;
+    if (p->dtype == LORA_F32) {
+        pl->path = PATH_F32;
+    } else if (T <= DECODE_MAX_T) {
+        pl->path = PATH_DECODE;
+    } else {
+        pl->path = PATH_PREFILL;
+    }
+    pl->chunk = pl->path == PATH_PREFILL ? 64 : 16;
+    pl->n_items_max = (int32_t)((T + pl->chunk - 1) / pl->chunk + std::min<int64_t>(T, p->max_adapters));
+    pl->vsplit = 1;
+    pl->ysplit = 1;
+    pl->n_tiles = 0;
+    if (pl->path == PATH_DECODE) {
+        if (T <= 64) {
+            pl->wm = 1;
+            pl->mb = (int32_t)std::max<int64_t>(1, (T + 15) / 16);
+        } else if (T <= 128) {
+            pl->wm = 2;
+            pl->mb = 4;
+        } else {
+            pl->wm = 4;
+            pl->mb = 4;
+        }
+        pl->n_tiles = (int32_t)(H / 64);
+        pl->ysplit = (int32_t)std::min<int64_t>(8, std::max<int64_t>(1, (256 + pl->n_tiles - 1) / pl->n_tiles));
+    } else if (pl->path == PATH_PREFILL) {
+        pl->vsplit = 8;
+        pl->n_tiles = 0;
+    }
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
+    pl->off_tok_a = take(T * 4);
+    pl->off_tok_r = take(T * 4);
+    pl->off_perm = take(T * 4);
+    pl->off_seg_a = take((T + 1) * 4);
+    pl->off_seg_start = take((T + 2) * 4);
+    pl->off_item_seg = take((size_t)pl->n_items_max * 4);
+    pl->off_item_row = take((size_t)pl->n_items_max * 4);
+    pl->off_ctrl = take(CTRL_WORDS * 4);
+    pl->off_counters = take((size_t)std::max(pl->n_tiles, 1) * 4);
+    pl->off_v = take((size_t)pl->vsplit * T * R * 4);
+    pl->off_ypart = take(pl->path == PATH_DECODE && pl->ysplit > 1 ? (size_t)pl->ysplit * T * H * 4 : 0);
+    pl->total = o;
+    return true;
+}
+
+Ws carve(void *base, const Plan &pl) {
+    char *b = (char *)base;
+    Ws w;
+    w.tok_a = (int32_t *)(b + pl.off_tok_a);
+    w.tok_r = (int32_t *)(b + pl.off_tok_r);
+    w.perm = (int32_t *)(b + pl.off_perm);
+    w.seg_a = (int32_t *)(b + pl.off_seg_a);
+    w.seg_start = (int32_t *)(b + pl.off_seg_start);
+    w.item_seg = (int32_t *)(b + pl.off_item_seg);
+    w.item_row = (int32_t *)(b + pl.off_item_row);
+    w.ctrl = (int32_t *)(b + pl.off_ctrl);
+    w.counters = (int32_t *)(b + pl.off_counters);
+    w.v = (float *)(b + pl.off_v);
+    w.ypart = (float *)(b + pl.off_ypart);
+    return w;
+}
+
+static bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+}  // namespace lorapool
+
+extern "C" size_t lora_project_workspace_size(const lora_pool *p, int64_t T) {
+    Plan pl;
+    if (!make_plan(p, T, &pl)) return 0;
+    return pl.total;
+}
+
+extern "C" int lora_project(lora_pool *p, const void *x, const void *W, const int32_t *pt, const int32_t *ids,
+                            const int32_t *ranks, const float *scale, int64_t T, void *y, void *ws,
+                            size_t ws_bytes, void *stream) {
+    if (!p) return set_error(LORA_EINVAL, "lora_project: pool is NULL");
+    if (p->bookkeeping_only) return set_error(LORA_EINVAL, "lora_project: bookkeeping-only pool");
+    if (T < 0 || T > MAX_TOKENS)
+        return set_error(LORA_EINVAL, "lora_project: T = %lld not in [0, %lld]", (long long)T, (long long)MAX_TOKENS);
+    if (T == 0) return LORA_OK;
+    if (!x || !W || !pt || !ids || !ranks || !scale || !y || !ws)
+        return set_error(LORA_EINVAL, "lora_project: NULL pointer argument");
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(ranks, 4) ||
+        !aligned(scale, 4) || !aligned(pt, 4) || !aligned(ws, 256))
+        return set_error(LORA_EINVAL, "lora_project: misaligned pointer (x, W, y: 16 B; ids, ranks, scale, "
+                                      "page_table: 4 B; workspace: 256 B)");
+    const size_t xbytes = (size_t)T * p->hidden * p->elem;
+    const char *xb = (const char *)x, *yb = (const char *)y;
+    if (xb < yb + xbytes && yb < xb + xbytes) return set_error(LORA_EINVAL, "lora_project: y overlaps x");
+    Plan pl;
+    make_plan(p, T, &pl);
+    if (ws_bytes < pl.total)
+        return set_error(LORA_EINVAL, "lora_project: workspace %zu bytes < %zu needed", ws_bytes, pl.total);
+    DeviceGuard g(p->device);
+    if (!g.ok) return set_error(LORA_EHIP, "lora_project: cannot select the pool's device");
+    hipStream_t s = (hipStream_t)stream;
+    Ws w = carve(ws, pl);
+    hipEvent_t *ev = nullptr;
+    if (p->prof_max > 0) {
+        const int32_t slot = p->prof_next.fetch_add(1);
+        if (slot < p->prof_max) ev = &p->prof_events[(size_t)slot * 4];
+    }
+    if (ev) LP_HIP(hipEventRecord(ev[0], s));
+    hipError_t e = launch_segments(p, pl, w, ids, ranks, pt, s);
+    if (e != hipSuccess) return hip_error(e, "segment kernel launch");
+    if (ev) LP_HIP(hipEventRecord(ev[1], s));
+    switch (pl.path) {
+        case PATH_DECODE: e = launch_decode(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
+        case PATH_PREFILL: e = launch_prefill(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
+        case PATH_F32: e = launch_f32(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
+    }
+    if (e != hipSuccess) return hip_error(e, "projection kernel launch");
+    if (ev) LP_HIP(hipEventRecord(ev[3], s));
+    return LORA_OK;
+}
+
+extern "C" int lora_profile_start(lora_pool *p, int32_t max_calls) {
+    if (!p || p->bookkeeping_only || max_calls < 1 || max_calls > (1 << 20))
+        return set_error(LORA_EINVAL, "lora_profile_start: bad pool or max_calls");
+    DeviceGuard g(p->device);
+    for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+    p->prof_events.assign((size_t)max_calls * 4, nullptr);
+    for (auto &e : p->prof_events) LP_HIP(hipEventCreate(&e));
+    p->prof_next.store(0);
+    p->prof_max = max_calls;
+    return LORA_OK;
+}
+
+extern "C" int lora_profile_stop(lora_pool *p, lora_profile_t *out) {
+    if (!p || !out) return set_error(LORA_EINVAL, "lora_profile_stop: NULL argument");
+    DeviceGuard g(p->device);
+    memset(out, 0, sizeof *out);
+    const int32_t n = std::min(p->prof_next.load(), p->prof_max);
+    p->prof_max = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        hipEvent_t *ev = &p->prof_events[(size_t)i * 4];
+        LP_HIP(hipEventSynchronize(ev[3]));
+        float a = 0, b = 0, c = 0;
+        LP_HIP(hipEventElapsedTime(&a, ev[0], ev[1]));
+        LP_HIP(hipEventElapsedTime(&b, ev[1], ev[2]));
+        LP_HIP(hipEventElapsedTime(&c, ev[2], ev[3]));
+        out->ms_segments += a;
+        out->ms_shrink += b;
+        out->ms_main += c;
+        out->ms_main_min = i == 0 ? c : std::min<double>(out->ms_main_min, c);
+        out->ms_main_max = std::max<double>(out->ms_main_max, c);
+    }
+    out->calls = n;
+    for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+    p->prof_events.clear();
+    return LORA_OK;
+}
+
+extern "C" int lora_debug_gather(lora_pool *p, const int32_t *pt, const int32_t *ids, const int32_t *ranks,
+                                 int64_t T, int32_t *out, void *stream) {
+    if (!p) return set_error(LORA_EINVAL, "lora_debug_gather: pool is NULL");
+    if (p->bookkeeping_only) return set_error(LORA_EINVAL, "lora_debug_gather: bookkeeping-only pool");
+    if (T < 0 || T > MAX_TOKENS) return set_error(LORA_EINVAL, "lora_debug_gather: bad T %lld", (long long)T);
+    if (T == 0) return LORA_OK;
+    if (!pt || !ids || !ranks || !out) return set_error(LORA_EINVAL, "lora_debug_gather: NULL pointer argument");
+    if (!aligned(pt, 4) || !aligned(ids, 4) || !aligned(ranks, 4) || !aligned(out, 4))
+        return set_error(LORA_EINVAL, "lora_debug_gather: misaligned pointer");
+    DeviceGuard g(p->device);
+    hipError_t e = launch_debug_gather(p, pt, ids, ranks, T, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_error(e, "debug gather launch");
+    return LORA_OK;
+}
+
+extern "C" int lora_check_device_errors(lora_pool *p) {
+    if (!p) return set_error(LORA_EINVAL, "lora_check_device_errors: pool is NULL");
+    if (p->bookkeeping_only) return LORA_OK;
+    DeviceGuard g(p->device);
+    LP_HIP(hipDeviceSynchronize());
+    int word = 0;
+    LP_HIP(hipMemcpy(&word, p->dev_err, sizeof word, hipMemcpyDeviceToHost));
+    if (!word) return LORA_OK;
+    LP_HIP(hipMemset(p->dev_err, 0, sizeof word));
+    return set_error(LORA_EDEVICE, "device check failed:%s%s%s%s", word & DEV_ERR_ID ? " adapter-id-out-of-range" : "",
+                     word & DEV_ERR_RANK ? " rank-out-of-range" : "",
+                     word & DEV_ERR_TABLE ? " adapter-not-loaded-at-this-rank" : "",
+                     word & DEV_ERR_PAGE ? " page-id-out-of-range" : "");
+}

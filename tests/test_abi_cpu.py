@@ -1,0 +1,222 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its host-side pool
+bookkeeping matches the oracle's pool model bit for bit.  No device work is done here (pools are
+bookkeeping-only: no pages, no page table)."""
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import rank_gemm_unified_amd as rg
+from oracle import UnifiedPoolModel, kv_pages_per_token, pages_for_adapter
+from workloads import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lorapool.h")
+
+_STATUS = {"ok": 0, "enomem": -2, "enoent": -3, "ebusy": -5, "eexist": -6, "einval": -1}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lora_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 20, names
+    out = subprocess.run(["nm", "-D", "--defined-only", rg.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(lora_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(rg.EXPORTED) == set(names)
+
+
+def test_version_and_constants():
+    assert "gfx950" in rg.lora_version()
+    text = open(HEADER).read()
+    assert f"#define LORA_MAX_RANK {rg.LORA_MAX_RANK}" in text
+    assert re.search(rf"#define LORA_MAX_ADAPTERS {rg.LORA_MAX_ADAPTERS}\b", text)
+
+
+def test_page_arithmetic_matches_worked_example(golden_dir):
+    w = json.load(open(os.path.join(golden_dir, "slora_worked_example.json")))
+    m, a = w["model"], w["adapter"]
+    assert rg.lora_pool_pages_for(a["rank"], a["projections"], m["layers"]) == w["adapter_vectors_total"]
+    assert rg.lora_pool_pages_for(a["rank"], a["projections"], 1) == w["adapter_vectors_per_layer"]
+    assert rg.lora_kv_pages_per_token(m["layers"]) == w["kv_vectors_per_token"]
+    for r in (0, 1, 8, 64, 128):
+        for p in (1, 4):
+            for L in (1, 32, 40):
+                assert rg.lora_pool_pages_for(r, p, L) == pages_for_adapter(r, L, p)
+    assert rg.lora_pool_pages_for(-1, 4, 32) == -1 and rg.lora_kv_pages_per_token(-2) == -1
+    assert rg.lora_kv_pages_per_token(40) == kv_pages_per_token(40)
+
+
+def _bk_pool(num_pages, n_slots=1, max_adapters=16, max_rank=64, free_order=None):
+    return rg.lora_pool_create(None, num_pages, 64, rg.LORA_BF16, max_rank, n_slots, max_adapters, None, free_order)
+
+
+def _apply_c(pool, step, n_slots):
+    op = step["op"]
+    if op == "load":
+        before = rg.lora_pool_free_list(pool)
+        rc = rg.lora_pool_load_adapter(pool, step["aid"], step["rank"], None, None, stream=0, check=False)
+        after = rg.lora_pool_free_list(pool)
+        taken = []
+        if rc == 0:
+            pages, _, users = rg.lora_pool_adapter_pages(pool, step["aid"])
+            taken = pages if users == 1 else []
+        return rc, taken, (before, after)
+    if op == "kv":
+        r = rg.lora_pool_grow_kv(pool, step["rid"], step["layers"], check=False)
+        return (r, [], None) if isinstance(r, int) else (0, r, None)
+    if op == "free_kv":
+        return rg.lora_pool_free_kv(pool, step["rid"], check=False), None, None
+    if op == "release":
+        return rg.lora_pool_release_adapter(pool, step["aid"], check=False), None, None
+    if op == "evict":
+        return rg.lora_pool_evict_adapter(pool, step["aid"], stream=0, check=False), None, None
+    raise ValueError(op)
+
+
+def test_hand_derived_trace_through_abi(golden_dir):
+    traces = json.load(open(os.path.join(golden_dir, "pool_trace.json")))["traces"]
+    for tr in traces:
+        pool = _bk_pool(tr["num_pages"], tr["n_slots"], tr["max_adapters"], tr["max_rank"])
+        try:
+            for step in tr["steps"]:
+                rc, taken, _ = _apply_c(pool, step, tr["n_slots"])
+                assert rc == _STATUS[step["status"]], (step, rg.lora_last_error())
+                if "pages" in step and step["status"] == "ok":
+                    assert list(taken) == step["pages"], step
+            fin = tr["final"]
+            assert rg.lora_pool_free_list(pool) == fin["free"]
+            assert rg.lora_pool_resident(pool) == fin["resident_in_load_order"]
+            for rid, pages in fin["kv"].items():
+                assert rg.lora_pool_kv_pages(pool, int(rid)) == pages
+        finally:
+            rg.lora_pool_free(pool)
+
+
+def _model_status(s):
+    return _STATUS[s]
+
+
+def test_random_ops_match_model():
+    rng = np.random.default_rng(1)
+    for trial in range(30):
+        n = int(rng.integers(8, 300))
+        n_slots = int(rng.integers(1, 4))
+        order = rng.permutation(n) if trial % 2 else None
+        model = UnifiedPoolModel(n, order)
+        pool = _bk_pool(n, n_slots, max_adapters=10, max_rank=8, free_order=order)
+        try:
+            for _ in range(300):
+                k = int(rng.integers(0, 5))
+                aid, rid = int(rng.integers(0, 10)), int(rng.integers(0, 6))
+                if k == 0:
+                    rank = int(rng.integers(0, 9))
+                    want = _model_status(model.ensure_adapter(aid, rank, n_slots))
+                    got = rg.lora_pool_load_adapter(pool, aid, rank, None, None, stream=0, check=False)
+                elif k == 1:
+                    layers = int(rng.integers(1, 4))
+                    want = _model_status(model.grow_kv(rid, layers))
+                    r = rg.lora_pool_grow_kv(pool, rid, layers, check=False)
+                    got = r if isinstance(r, int) else 0
+                elif k == 2:
+                    want = _model_status(model.free_kv(rid))
+                    got = rg.lora_pool_free_kv(pool, rid, check=False)
+                elif k == 3:
+                    want = _model_status(model.release(aid))
+                    got = rg.lora_pool_release_adapter(pool, aid, check=False)
+                else:
+                    want = _model_status(model.evict(aid))
+                    got = rg.lora_pool_evict_adapter(pool, aid, stream=0, check=False)
+                assert got == want, (trial, k, rg.lora_last_error())
+                assert rg.lora_pool_free_list(pool) == model.free
+            assert rg.lora_pool_resident(pool) == list(model.adapter_pages)
+            for a, pages in model.adapter_pages.items():
+                got_pages, rank, users = rg.lora_pool_adapter_pages(pool, a)
+                assert got_pages == pages and rank == model.adapter_rank[a] and users == model.adapter_refs[a]
+            st = rg.lora_pool_stats(pool)
+            ms = model.stats()
+            for key in ("num_pages", "free_pages", "kv_pages", "adapter_pages", "resident_adapters"):
+                assert st[key] == ms[key], key
+        finally:
+            rg.lora_pool_free(pool)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "many"])
+def test_workload_plans_match_model(name):
+    w = build(name)
+    model = UnifiedPoolModel(w.num_pages, w.free_order)
+    want = model.run(w.ops, w.ranks, w.n_slots)
+    pool = _bk_pool(w.num_pages, w.n_slots, w.max_adapters, 64, w.free_order)
+    try:
+        got = rg.run_pool_ops(pool, w.ops, w.ranks, lambda a: (None, None), stream=0)
+        assert [_STATUS[s] for s in want] == got
+        assert rg.lora_pool_free_list(pool) == model.free
+        for a in list(model.adapter_pages)[:: max(1, len(model.adapter_pages) // 50)]:
+            assert rg.lora_pool_adapter_pages(pool, a)[0] == model.adapter_pages[a]
+    finally:
+        rg.lora_pool_free(pool)
+
+
+def test_error_codes():
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_pool_create(None, 10, 100, rg.LORA_BF16, 64, 1, 4, None)     # hidden not a multiple of 64
+    assert e.value.code == rg.LORA_EINVAL
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_pool_create(None, 10, 64, 7, 64, 1, 4, None)
+    assert e.value.code == rg.LORA_EINVAL
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_pool_create(None, 10, 64, rg.LORA_BF16, 65, 1, 4, None)
+    assert e.value.code == rg.LORA_ERANK
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_pool_create(None, 4, 64, rg.LORA_BF16, 8, 1, 4, None, free_order=[0, 1, 1, 3])
+    assert e.value.code == rg.LORA_EINVAL and "permutation" in str(e.value)
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_pool_create(None, 10, 64, rg.LORA_BF16, 8, 1, rg.LORA_MAX_ADAPTERS + 1, None)
+    assert e.value.code == rg.LORA_EINVAL
+    pool = _bk_pool(20, 1, 4, 8)
+    try:
+        assert rg.lora_pool_load_adapter(pool, 0, 9, None, None, 0, check=False) == rg.LORA_ERANK
+        assert rg.lora_pool_load_adapter(pool, 4, 1, None, None, 0, check=False) == rg.LORA_EINVAL
+        assert rg.lora_pool_load_adapter(pool, -1, 1, None, None, 0, check=False) == rg.LORA_EINVAL
+        assert rg.lora_pool_load_adapter(pool, 0, 8, None, None, 0, check=False) == 0
+        assert rg.lora_pool_load_adapter(pool, 1, 8, None, None, 0, check=False) == rg.LORA_ENOMEM
+        assert rg.lora_pool_load_adapter(pool, 0, 4, None, None, 0, check=False) == rg.LORA_EEXIST
+        assert rg.lora_pool_evict_adapter(pool, 0, 0, check=False) == rg.LORA_EBUSY
+        assert rg.lora_pool_evict_adapter(pool, 2, 0, check=False) == rg.LORA_ENOENT
+        assert rg.lora_pool_release_adapter(pool, 2, check=False) == rg.LORA_ENOENT
+        assert rg.lora_pool_free_kv(pool, 5, check=False) == rg.LORA_ENOENT
+        assert rg.lora_pool_grow_kv(pool, 0, 0, check=False) == rg.LORA_EINVAL
+        assert len(rg.lora_pool_grow_kv(pool, 0, 2, check=False)) == 4
+        assert rg.lora_pool_grow_kv(pool, 0, 1, check=False) == rg.LORA_ENOMEM
+        with pytest.raises(rg.LoraError) as e:
+            rg.lora_pool_page_table(pool, 0)
+        assert e.value.code == rg.LORA_EINVAL
+        # a projection on a bookkeeping-only pool is refused before any device work
+        assert rg._lib.lora_project(pool, 16, 16, 16, 16, 16, 16, 4, 16, 256, 1 << 20, None) == rg.LORA_EINVAL
+        assert rg._lib.lora_project(None, 16, 16, 16, 16, 16, 16, 4, 16, 256, 1 << 20, None) == rg.LORA_EINVAL
+        st = rg.lora_pool_stats(pool)
+        assert st["adapter_pages"] == 16 and st["kv_pages"] == 4 and st["free_pages"] == 0
+        assert st["loads"] == 1 and st["resident_adapters"] == 1
+    finally:
+        rg.lora_pool_free(pool)
+    assert rg.lora_pool_free(None) == 0
+
+
+def test_workspace_size_grows_with_tokens():
+    pool = _bk_pool(100, 1, 32, 64)
+    try:
+        sizes = [rg.lora_project_workspace_size(pool, T) for T in (1, 16, 64, 256, 257, 4096)]
+        assert all(s > 0 and s % 256 == 0 for s in sizes)
+        assert sizes == sorted(sizes) or sizes[3] > sizes[4]     # decode keeps split-K partials
+        assert rg.lora_project_workspace_size(pool, -1) == 0
+    finally:
+        rg.lora_pool_free(pool)
