@@ -39,12 +39,14 @@ def log(*a):
 
 
 def algorithmic(w, T_ids, slots):
-    """Bytes and flops the method itself must move/compute per step, and the main kernel's share.
+    """Bytes and flops the method itself must move/compute per step, and each kernel's share.
 
     Per projection call: W once (H^2 e), x in and y out (2 T H e), each A and B page of every
     distinct adapter the batch uses once (2 r H e), the ids (4 T).  Flops: 2 T H^2 + 4 H r per
-    token with an adapter.  The main kernel (base GEMM + expand) reads W, x, the B pages and
-    writes y; it computes 2 T H^2 + 2 H r per adapter token.
+    token with an adapter.  Per kernel (decode path): the first launch reads W, x, the ids and the
+    A pages (base partials and the shrink); the second reads the B pages and writes y.  Prefill
+    path: the shrink reads x and the A pages; the tiled GEMM reads x, W, the B pages, writes y.
+    Partial sums the kernels exchange through the workspace are not algorithmic bytes.
     """
     H, e = w.hidden, w.elem
     ids = T_ids
@@ -52,13 +54,15 @@ def algorithmic(w, T_ids, slots):
     r_sum_distinct = sum(int(w.ranks[a]) for a in distinct)
     r_sum_tokens = sum(int(w.ranks[a]) for a in ids if a >= 0)
     T = len(ids)
-    per_call_bytes = H * H * e + 2 * T * H * e + 2 * r_sum_distinct * H * e + 4 * T
+    pages = r_sum_distinct * H * e           # all A pages (or all B pages) of the batch
+    per_call_bytes = H * H * e + 2 * T * H * e + 2 * pages + 4 * T
     per_call_flops = 2 * T * H * H + 4 * H * r_sum_tokens
-    main_bytes = H * H * e + 2 * T * H * e + r_sum_distinct * H * e
-    main_flops = 2 * T * H * H + 2 * H * r_sum_tokens
     return {
         "bytes": per_call_bytes * slots, "flops": per_call_flops * slots,
-        "main_bytes": main_bytes, "main_flops": main_flops,
+        "decode_first_bytes": H * H * e + T * H * e + pages + 4 * T,
+        "decode_second_bytes": pages + T * H * e,
+        "prefill_second_flops": 2 * T * H * H + 2 * H * r_sum_tokens,
+        "prefill_first_flops": 2 * H * r_sum_tokens,
         "distinct_adapters": len(distinct), "r_sum_distinct": r_sum_distinct,
     }
 
@@ -203,32 +207,36 @@ def main():
     for i in range(calls_per_rep * R):
         step(i)
     torch.cuda.synchronize()
-    prof = {"calls": 0, "ms_segments": 0.0, "ms_shrink": 0.0, "ms_main": 0.0}
+    prof = {"calls": 0, "ms_group": 0.0, "ms_first": 0.0, "ms_second": 0.0}
     for pool, *_ in reps:
         pr = rg.lora_profile_stop(pool.handle)
         for k in prof:
             prof[k] += pr[k]
     n = max(prof["calls"], 1)
-    avg = {k: prof[k] / n * 1e3 for k in ("ms_segments", "ms_shrink", "ms_main")}   # microseconds
-    log(f"kernel avg (us): segments {avg['ms_segments']:.2f} shrink {avg['ms_shrink']:.2f} "
-        f"main {avg['ms_main']:.2f}  over {prof['calls']} calls")
+    avg = {k.replace("ms_", "") + "_us": prof[k] / n * 1e3 for k in ("ms_group", "ms_first", "ms_second")}
+    log(f"kernel avg (us): {avg}  over {prof['calls']} calls")
 
-    main_s = avg["ms_main"] / 1e6
-    decode_like = w.T <= 256
+    src = os.path.join(ROOT, "rank_gemm_unified_amd", "csrc")
+    decode_like = w.dtype == "bf16" and w.T <= 256
     if decode_like:
-        achieved = info["main_bytes"] / main_s / 1e9
+        t_s = avg["first_us"] / 1e6
+        achieved = info["decode_first_bytes"] / t_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "kernel": "k_base_expand (base GEMM + fused expand)",
-                "algorithmic_bytes_per_launch": info["main_bytes"], "avg_launch_us": avg["ms_main"],
-                "traffic": traffic_from_profiles("decode_main", os.path.join(ROOT, "rank_gemm_unified_amd", "csrc",
-                                                                              "k_decode.hip"))}
+                "frac": achieved / HBM_PEAK_GBS,
+                "kernel": "k_decode_main (W stream + MFMA partials, gathered-A shrink)",
+                "algorithmic_bytes_per_launch": info["decode_first_bytes"], "avg_launch_us": avg["first_us"],
+                "traffic": traffic_from_profiles("decode_main", os.path.join(src, "k_decode.hip")),
+                "second_kernel": {"kernel": "k_decode_finish (partials + gathered-B expand + rounding)",
+                                  "avg_launch_us": avg["second_us"],
+                                  "achieved_GBps": info["decode_second_bytes"] / (avg["second_us"] / 1e6) / 1e9}}
     else:
-        achieved = info["main_flops"] / main_s / 1e12
+        t_s = avg["second_us"] / 1e6
+        achieved = info["prefill_second_flops"] / t_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)",
-                "algorithmic_flops_per_launch": info["main_flops"], "avg_launch_us": avg["ms_main"],
-                "traffic": traffic_from_profiles("prefill_main", os.path.join(ROOT, "rank_gemm_unified_amd", "csrc",
-                                                                               "k_prefill.hip"))}
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)",
+                "algorithmic_flops_per_launch": info["prefill_second_flops"], "avg_launch_us": avg["second_us"],
+                "traffic": traffic_from_profiles("prefill_main", os.path.join(src, "k_prefill.hip"))}
 
     cpu = None
     if not args.no_cpu_baseline and rank == 0:

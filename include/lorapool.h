@@ -240,10 +240,12 @@ int lora_check_device_errors(lora_pool *pool);
 
 typedef struct lora_profile {
     int64_t calls;              /* projections recorded                                          */
-    double ms_segments;         /* summed device time of the token-grouping kernel               */
-    double ms_shrink;           /* ... of the shrink kernel (x A)                                */
-    double ms_main;             /* ... of the base GEMM + expand kernel                          */
-    double ms_main_min, ms_main_max;
+    double ms_group;            /* summed device time of the token-grouping kernel (prefill and
+                                   float32 paths; the decode path groups inside its first kernel) */
+    double ms_first;            /* ... of the first compute launch: decode = shrink + base GEMM
+                                   partials; prefill and float32 = shrink                          */
+    double ms_second;           /* ... of the second: decode = partial sum + expand + rounding;
+                                   prefill and float32 = base GEMM + fused expand                  */
 } lora_profile_t;
 
 /* Start recording HIP events around each kernel of the next `max_calls` projections on this

@@ -40,8 +40,8 @@ class lora_pool_stats_t(ctypes.Structure):
 
 
 class lora_profile_t(ctypes.Structure):
-    _fields_ = [("calls", _i64), ("ms_segments", ctypes.c_double), ("ms_shrink", ctypes.c_double),
-                ("ms_main", ctypes.c_double), ("ms_main_min", ctypes.c_double), ("ms_main_max", ctypes.c_double)]
+    _fields_ = [("calls", _i64), ("ms_group", ctypes.c_double), ("ms_first", ctypes.c_double),
+                ("ms_second", ctypes.c_double)]
 
 
 _SIGS = {

@@ -90,9 +90,12 @@ struct Plan {
     int32_t n_tiles;        // decode: column tiles (one arrival counter each)
     int32_t mb;             // decode: 16-row blocks per wave
     int32_t wm;             // decode: waves along M (4 / wm along K)
+    int32_t n_shrink;       // decode: shrink workgroups beside the base workgroups
+    int32_t n_counters;     // arrival counters the grouping kernel zeroes
+    int32_t rp;             // prefill: row stride of v (max_rank rounded up to 16)
     // byte offsets into the workspace
     size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row,
-        off_ctrl, off_counters, off_v, off_ypart, total;
+        off_ctrl, off_counters, off_v, off_ypart, off_sorted_tok, off_v16, total;
 };
 
 bool make_plan(const lora_pool *p, int64_t T, Plan *plan);
@@ -100,6 +103,8 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *plan);
 struct Ws {
     int32_t *tok_a, *tok_r, *perm, *seg_a, *seg_start, *item_seg, *item_row, *ctrl, *counters;
     float *v, *ypart;
+    int32_t *sorted_tok;    // decode: int4 {token, adapter or -1, rank, 0} per sorted position
+    uint16_t *v16;          // prefill: v = s x A in bfloat16, [T][rp]
 };
 Ws carve(void *base, const Plan &plan);
 
@@ -122,8 +127,8 @@ hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws,
 hipError_t launch_debug_gather(const lora_pool *p, const int32_t *pt, const int32_t *ids,
                                const int32_t *ranks, int64_t T, int32_t *out, hipStream_t s);
 hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
-                         const void *W, const int32_t *pt, const float *scale, void *y,
-                         hipStream_t s, hipEvent_t mid);
+                         const void *W, const int32_t *ids, const int32_t *ranks, const int32_t *pt,
+                         const float *scale, void *y, hipStream_t s, hipEvent_t mid);
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
                           const void *W, const int32_t *pt, const float *scale, void *y,
                           hipStream_t s, hipEvent_t mid);

@@ -1,12 +1,362 @@
-// Prefill-shaped projection (long per-request segments): MFMA-bound tiled GEMM.
+// Prefill-shaped projection (many tokens per request, T > 256): MFMA-bound.
+//
+//   k_shrink_mfma    v = s_a X_seg A_a for every 64-row chunk of every adapter segment (tokens
+//                    grouped by the grouping kernel), as a bf16 MFMA GEMM against the r gathered A
+//                    pages, split over K; the last split to arrive for a chunk sums the float32
+//                    partials in split order, scales, and stores v in bfloat16.
+//   k_prefill_main   y = x W for a 256x256 output tile (bf16 MFMA 32x32x16, LDS double buffer),
+//                    then the low-rank term as extra K: for each adapter that owns rows of the
+//                    tile, [x | v_a] [W ; B_a] with v_a zero outside its rows and B_a's rows
+//                    gathered from their pages; one rounding to bfloat16 at the end.
+// ("S-LoRA, in depth", sections "Merge or keep adapters separate" and "Kernels for a batch of
+// mixed ranks": the base product is batched over all tokens; the low-rank work follows tokens and
+// their ranks.)
 #include "device_common.h"
 #include "internal.h"
 
 namespace lorapool {
 
-hipError_t launch_prefill(const lora_pool *, const Plan &, const Ws &, const void *, const void *, const int32_t *,
-                          const float *, void *, hipStream_t, hipEvent_t) {
-    return hipErrorNotSupported;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---- shrink ------------------------------------------------------------------------------------
+constexpr int SH_ROWS = 64;   // rows per work item (4 waves x 16)
+constexpr int VSPLIT = 8;     // K-splits of the shrink
+
+// One wave: 16 rows x (NBR*16 pages) over K range [kb, ke); partial sums to vpart[split].
+// NBR is a template parameter so the MFMA loop carries no per-block conditions; pages j >= r are
+// read from a clamped valid page and zeroed by select.
+template <int NBR>
+__device__ __forceinline__ void shrink_rows(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages,
+                                            int32_t H, const int32_t *__restrict__ prow, int32_t r,
+                                            const int32_t *__restrict__ prm, int n, int kb, int ke, int lane,
+                                            int wave, float *__restrict__ vout, int32_t T, int32_t R) {
+    const int lrow = lane & 15, lk = (lane >> 4) * 8;
+    const int my = wave * 16 + lrow;
+    const bool xv = my < n;
+    const uint16_t *xr = x + (int64_t)prm[xv ? my : 0] * H + lk;
+    const uint16_t *ap[NBR];
+    bool av[NBR];
+#pragma unroll
+    for (int nb = 0; nb < NBR; ++nb) {
+        const int j = nb * 16 + lrow;
+        av[nb] = j < r;
+        ap[nb] = pages + (int64_t)prow[min(j, r - 1)] * H + lk;
+    }
+    f32x4_t acc[NBR];
+#pragma unroll
+    for (int nb = 0; nb < NBR; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 4;
+    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+    int k = kb;
+    for (; k + 32 * U <= ke; k += 32 * U) {
+        u32x4_t xa[U], bb[U][NBR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xa[u] = load16(xr + k + 32 * u);
+#pragma unroll
+            for (int nb = 0; nb < NBR; ++nb) bb[u][nb] = load16(ap[nb] + k + 32 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4_t xs = xv ? xa[u] : zero;
+#pragma unroll
+            for (int nb = 0; nb < NBR; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs),
+                                                                  __builtin_bit_cast(bf16x8_t, av[nb] ? bb[u][nb] : zero),
+                                                                  acc[nb], 0, 0, 0);
+        }
+    }
+    for (; k < ke; k += 32) {
+        const u32x4_t xs = xv ? load16(xr + k) : zero;
+#pragma unroll
+        for (int nb = 0; nb < NBR; ++nb) {
+            const u32x4_t bb = load16(ap[nb] + k);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs),
+                                                              __builtin_bit_cast(bf16x8_t, av[nb] ? bb : zero), acc[nb],
+                                                              0, 0, 0);
+        }
+    }
+    // lane holds rows 4*(lane/16)+i of column lane%16 of each 16x16 block
+#pragma unroll
+    for (int nb = 0; nb < NBR; ++nb) {
+        const int j = nb * 16 + lrow;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = wave * 16 + (lane >> 4) * 4 + i;
+            if (rr < n && j < r) vout[(int64_t)prm[rr] * R + j] = acc[nb][i];
+        }
+    }
+}
+
+// Grid (work items, VSPLIT).  Writes float32 partials vpart[split][t][0..r); k_v_finalize adds
+// them.  (No in-kernel cross-workgroup reduction: on this chip a device-scope fence writes back
+// and invalidates the whole L2.)
+__global__ __launch_bounds__(256) void k_shrink_mfma(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H, const int32_t *__restrict__ pt,
+    int32_t stride, const int32_t *__restrict__ perm, const int32_t *__restrict__ seg_a,
+    const int32_t *__restrict__ seg_start, const int32_t *__restrict__ item_seg, const int32_t *__restrict__ item_row,
+    const int32_t *__restrict__ ctrl, const int32_t *__restrict__ tok_r, float *__restrict__ vpart, int32_t T,
+    int32_t R) {
+    const int item = blockIdx.x;
+    if (item >= ctrl[CTRL_NITEMS]) return;
+    __shared__ int32_t s_perm[SH_ROWS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int split = blockIdx.y;
+    const int32_t s = item_seg[item], row0 = item_row[item];
+    const int32_t n = min(seg_start[s + 1] - row0, SH_ROWS);
+    if (threadIdx.x < SH_ROWS) s_perm[threadIdx.x] = perm[row0 + min((int)threadIdx.x, n - 1)];
+    const int32_t a = seg_a[s];
+    __syncthreads();
+    const int32_t r = tok_r[s_perm[0]];
+    const int32_t *prow = pt + (int64_t)a * stride;
+    const int ksteps = H / 32;
+    const int kb = (int)((int64_t)ksteps * split / VSPLIT) * 32, ke = (int)((int64_t)ksteps * (split + 1) / VSPLIT) * 32;
+    float *vout = vpart + (int64_t)split * T * R;
+    switch ((r + 15) / 16) {
+        case 1: shrink_rows<1>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
+        case 2: shrink_rows<2>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
+        case 3: shrink_rows<3>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
+        default: shrink_rows<4>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
+    }
+}
+
+// v16[t][j] = bf16(s_a * sum_split vpart[split][t][j]) for tokens with an adapter; zero for
+// j in [r, roundup(r, 4)).  One thread per (token, 4 consecutive j).
+__global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vpart, const int32_t *__restrict__ tok_a,
+                                                    const int32_t *__restrict__ tok_r, const float *__restrict__ scale,
+                                                    int32_t T, int32_t R, uint16_t *__restrict__ v16) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = idx / (R / 4);
+    const int j0 = (int)(idx % (R / 4)) * 4;
+    if (t >= T) return;
+    const int32_t a = tok_a[t], r = tok_r[t];
+    if (a < 0 || j0 >= r) return;
+    f32x4_t pv[VSPLIT];
+#pragma unroll
+    for (int q = 0; q < VSPLIT; ++q) pv[q] = *reinterpret_cast<const f32x4_t *>(vpart + ((int64_t)q * T + t) * R + j0);
+    f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < VSPLIT; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] += pv[q][e];
+    const float sc = scale[a];
+    uint32_t w0 = (j0 < r ? f32_to_bf16_bits(sc * sum[0]) : 0u) | ((j0 + 1 < r ? f32_to_bf16_bits(sc * sum[1]) : 0u) << 16);
+    uint32_t w1 = (j0 + 2 < r ? f32_to_bf16_bits(sc * sum[2]) : 0u) | ((j0 + 3 < r ? f32_to_bf16_bits(sc * sum[3]) : 0u) << 16);
+    *reinterpret_cast<uint2 *>(v16 + t * R + j0) = make_uint2(w0, w1);
+}
+
+// ---- base GEMM + fused expand --------------------------------------------------------------------
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int LDK = BK + 8;                         // padded LDS row (elements): conflict-free 16-B reads
+constexpr int STAGE = (BM + BN) * LDK;              // elements per pipeline stage
+constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
+
+__global__ __launch_bounds__(256, 1) void k_prefill_main(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
+    const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
+    int32_t n_tiles_n, uint16_t *__restrict__ y) {
+    extern __shared__ __align__(16) uint16_t sm[];
+    __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[4], s_nlist;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int mt = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    // global -> LDS mapping: thread covers 8 rows (tid/8 + 32 i), 8 elements at column (tid%8)*8
+    const int gr = tid >> 3, gc = (tid & 7) * 8;
+    const uint16_t *ga[8], *gb[8];
+    bool va[8], vb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = gr + 32 * i;
+        va[i] = m0 + row < T;
+        vb[i] = n0 + row < H;
+        ga[i] = x + (int64_t)(va[i] ? m0 + row : 0) * H + gc;
+        gb[i] = W + (int64_t)(vb[i] ? n0 + row : 0) * H + gc;
+    }
+    u32x4_t ra[8], rb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ra[i] = va[i] ? load16(ga[i]) : u32x4_t{0, 0, 0, 0};
+        rb[i] = vb[i] ? load16(gb[i]) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        store16(sm + (gr + 32 * i) * LDK + gc, ra[i]);
+        store16(sm + BM * LDK + (gr + 32 * i) * LDK + gc, rb[i]);
+    }
+    __syncthreads();
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+
+    const int frow = lane & 31, fk = (lane >> 5) * 8;   // 32x32x16 operand: row lane%32, k 8*(lane/32)
+    const int nk = H / BK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t *As = sm + (kt & 1) * STAGE;
+        const uint16_t *Bs = As + BM * LDK;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int k = (kt + 1) * BK;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ra[i] = va[i] ? load16(ga[i] + k) : u32x4_t{0, 0, 0, 0};
+                rb[i] = vb[i] ? load16(gb[i] + k) : u32x4_t{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            u32x4_t af[4], bf[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[mi] = load16(As + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                bf[ni] = load16(Bs + (wn * 128 + ni * 32 + frow) * LDK + ks * 16 + fk);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[mi]),
+                                                                          __builtin_bit_cast(bf16x8_t, bf[ni]),
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+        if (more) {
+            uint16_t *An = sm + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                store16(An + (gr + 32 * i) * LDK + gc, ra[i]);
+                store16(An + BM * LDK + (gr + 32 * i) * LDK + gc, rb[i]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- low-rank term: one K-extension per adapter owning rows of this tile
+    {
+        const int row = tid;
+        const int32_t key = m0 + row < T ? tok_a[m0 + row] : -1;
+        s_key[row] = key;
+        __syncthreads();
+        int first = key >= 0;
+        for (int u = 0; u < row && first; ++u) first = s_key[u] != key;
+        // exclusive scan of `first` over the 256 threads
+        int incl = first;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int yv = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += yv;
+        }
+        if (lane == 63) s_wsum[wave] = incl;
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += s_wsum[w];
+        if (first) {
+            s_list[before + incl - 1] = key;
+            s_lr[before + incl - 1] = tok_r[m0 + row];
+        }
+        if (tid == 255) s_nlist = before + incl;
+        __syncthreads();
+    }
+    const int nlist = s_nlist;
+    uint16_t *Bt = sm;                 // [BN][LDK]: B_a transposed, columns x j
+    uint16_t *Vs = sm + BN * LDK;      // [BM][LDK]: v rows of this adapter, zero elsewhere
+    for (int li = 0; li < nlist; ++li) {
+        const int32_t a = s_list[li], r = s_lr[li];
+        const int rp = (r + 15) & ~15;
+        const int32_t *prow = pt + (int64_t)a * stride + r;
+        for (int idx = tid; idx < rp * (BN / 8); idx += 256) {
+            const int j = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+            u32x4_t b = u32x4_t{0, 0, 0, 0};
+            if (j < r && n0 + c < H) b = load16(pages + (int64_t)prow[j] * H + n0 + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Bt[(c + 2 * e) * LDK + j] = (uint16_t)(b[e] & 0xffffu);
+                Bt[(c + 2 * e + 1) * LDK + j] = (uint16_t)(b[e] >> 16);
+            }
+        }
+        {
+            const int row = tid;
+            const bool mine = s_key[row] == a;
+            const uint16_t *vr = v16 + (int64_t)(mine ? m0 + row : 0) * R;
+            for (int j = 0; j < rp; j += 8) {
+                u32x4_t vv = mine ? load16(vr + j) : u32x4_t{0, 0, 0, 0};
+                if (j + 8 > r) {   // clear entries j >= r of a partial group
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = j + 2 * e < r ? 0xffffu : 0u, hi = j + 2 * e + 1 < r ? 0xffff0000u : 0u;
+                        vv[e] &= lo | hi;
+                    }
+                }
+                store16(Vs + row * LDK + j, vv);
+            }
+        }
+        __syncthreads();
+        for (int ks = 0; ks < rp / 16; ++ks) {
+            u32x4_t af[4], bf[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) af[mi] = load16(Vs + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) bf[ni] = load16(Bt + (wn * 128 + ni * 32 + frow) * LDK + ks * 16 + fk);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[mi]),
+                                                                          __builtin_bit_cast(bf16x8_t, bf[ni]),
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // ---- one rounding, store.  32x32 block layout: lane holds column lane%32 and, in register e,
+    //      row 8*(e/4) + 4*(lane/32) + e%4.
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int col = n0 + wn * 128 + ni * 32 + (lane & 31);
+            if (col >= H) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 128 + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+                if (row < T) y[(int64_t)row * H + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][e]);
+            }
+        }
+}
+
+hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
+                          const int32_t *pt, const float *scale, void *y, hipStream_t s, hipEvent_t mid) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_prefill_main, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)MAIN_LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (plan.vsplit != VSPLIT) return hipErrorInvalidValue;
+    dim3 g1(plan.n_items_max, VSPLIT);
+    hipLaunchKernelGGL(k_shrink_mfma, g1, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)p->pages, p->hidden,
+                       pt, 2 * p->max_rank, ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.ctrl,
+                       ws.tok_r, ws.v, (int32_t)plan.T, plan.rp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nthr = plan.T * (plan.rp / 4);
+    hipLaunchKernelGGL(k_v_finalize, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, ws.v, ws.tok_a, ws.tok_r,
+                       scale, (int32_t)plan.T, plan.rp, ws.v16);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
+    const int tn = (p->hidden + BN - 1) / BN, tm = (int)((plan.T + BM - 1) / BM);
+    hipLaunchKernelGGL(k_prefill_main, dim3(tm * tn), dim3(256), MAIN_LDS, s, (const uint16_t *)x, (const uint16_t *)W,
+                       (const uint16_t *)p->pages, pt, 2 * p->max_rank, ws.tok_a, ws.tok_r, ws.v16,
+                       plan.rp, (int32_t)plan.T, p->hidden, tn, (uint16_t *)y);
+    return hipGetLastError();
 }
 
 }  // namespace lorapool

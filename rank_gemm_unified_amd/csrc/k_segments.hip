@@ -49,7 +49,13 @@ __device__ int32_t block_exclusive_scan(int32_t *a, int32_t n, int32_t *scratch)
     return total;
 }
 
-// LDS: hist[max_adapters] | segf[max_adapters] | seglen[max_adapters] | scratch[32]
+// One workgroup of 1024 threads.  LDS: hist[max_adapters] | segf[max_adapters] | seglen[max_adapters]
+// | scratch[32].  Each thread keeps up to KPT of its tokens (t = tid + 1024 u) in registers, so a
+// batch of up to 8192 tokens costs one read of the ids; longer batches re-read them from tok_a.
+// Tokens of one adapter land in perm in an unspecified order (LDS atomics): no result depends on
+// the order of tokens within a segment.
+constexpr int KPT = 8;
+
 __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const int32_t *__restrict__ pt,
     int32_t stride, int32_t T, int32_t max_adapters, int32_t max_rank, int64_t num_pages, int32_t chunk,
@@ -61,7 +67,8 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     int32_t *hist = lds, *segf = lds + max_adapters, *seglen = lds + 2 * max_adapters;
     int32_t *scratch = lds + 3 * max_adapters;
     __shared__ int s_err;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
+    const bool cached = T <= KPT * SEG_THREADS;
     int my_err = 0;
     if (tid == 0) s_err = 0;
     for (int i = tid; i < n_counters; i += SEG_THREADS) counters[i] = 0;
@@ -69,54 +76,102 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     __syncthreads();
 
     // 1. id and rank range checks; count tokens per adapter with rank > 0
-    for (int t = tid; t < T; t += SEG_THREADS) {
-        const int32_t a = ids[t];
-        int32_t key = -1, r = 0;
-        if (a != -1) {
-            if (a < -1 || a >= max_adapters) {
-                my_err |= DEV_ERR_ID;
-            } else {
-                r = ranks[a];
-                if (r < 0 || r > max_rank) {
+    int32_t key[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) key[u] = -1;
+    for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
+        int32_t a[KPT], rr[KPT];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) a[u] = ids[min(t0 + u * SEG_THREADS + tid, T - 1)];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) rr[u] = ranks[a[u] >= 0 && a[u] < max_adapters ? a[u] : 0];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int t = t0 + u * SEG_THREADS + tid;
+            int32_t k = -1, r = 0;
+            if (t < T && a[u] != -1) {
+                if (a[u] < -1 || a[u] >= max_adapters) {
+                    my_err |= DEV_ERR_ID;
+                } else if (rr[u] < 0 || rr[u] > max_rank) {
                     my_err |= DEV_ERR_RANK;
-                    r = 0;
-                } else if (r > 0) {
-                    key = a;
-                    atomicAdd(&hist[a], 1);
+                } else if (rr[u] > 0) {
+                    k = a[u];
+                    r = rr[u];
+                    atomicAdd(&hist[k], 1);
                 }
             }
+            if (t < T) {
+                tok_a[t] = k;
+                tok_r[t] = r;
+            }
+            if (cached) key[u] = k;
         }
-        tok_a[t] = key;
-        tok_r[t] = key >= 0 ? r : 0;
     }
     __syncthreads();
 
-    // 2. each adapter in use: its page-table row must hold exactly 2r in-range pages
-    for (int a = tid; a < max_adapters; a += SEG_THREADS) {
-        if (hist[a] <= 0) continue;
-        const int32_t r = ranks[a];
-        const int32_t *row = pt + (int64_t)a * stride;
-        int bad = 0;
-        const int lim = min(2 * r + 1, stride);
-        for (int j = 0; j < lim; ++j) bad |= check_row_entry(row, j, r, stride, num_pages);
-        if (bad) {
-            my_err |= bad;
-            hist[a] = -hist[a];
+    // 2. each adapter in use: its page-table row must hold exactly 2r in-range pages.  The entries
+    //    of all used adapters are checked by all threads together (flattened list, 4 loads in flight).
+    for (int a = tid; a < max_adapters; a += SEG_THREADS) segf[a] = hist[a] > 0;
+    __syncthreads();
+    const int32_t nused = block_exclusive_scan(segf, max_adapters, scratch);   // segf := used index
+    for (int a = tid; a < max_adapters; a += SEG_THREADS)
+        if (hist[a] > 0) seglen[segf[a]] = a;                                   // seglen := used list
+    __syncthreads();
+    for (int u = tid; u < max_adapters; u += SEG_THREADS)
+        segf[u] = u < nused ? min(2 * ranks[seglen[u]] + 1, stride) : 0;
+    __syncthreads();
+    const int32_t nchk = block_exclusive_scan(segf, max_adapters, scratch);    // segf := entry offsets
+    for (int e0 = tid; e0 < nchk; e0 += 4 * SEG_THREADS) {
+        int ua[4], j[4];
+        int32_t ent[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = min(e0 + u * SEG_THREADS, nchk - 1);
+            int lo = 0, hi = nused - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (segf[mid] <= e) lo = mid; else hi = mid - 1;
+            }
+            ua[u] = seglen[lo];
+            j[u] = e - segf[lo];
+            ent[u] = pt[(int64_t)ua[u] * stride + j[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (e0 + u * SEG_THREADS >= nchk) continue;
+            const int32_t r = ranks[ua[u]];
+            int bad = 0;
+            if (j[u] < 2 * r) {
+                if (ent[u] == -1) bad = DEV_ERR_TABLE;
+                else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad = DEV_ERR_PAGE;
+            } else if (ent[u] != -1) {
+                bad = DEV_ERR_TABLE;
+            }
+            if (bad) {
+                my_err |= bad;
+                atomicOr(&hist[ua[u]], 0x40000000);
+            }
         }
     }
     __syncthreads();
 
     // 3. tokens of a faulty adapter get the base product only
-    for (int t = tid; t < T; t += SEG_THREADS) {
-        const int32_t key = tok_a[t];
-        if (key >= 0 && hist[key] < 0) {
-            tok_a[t] = -1;
-            tok_r[t] = 0;
+    for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int t = t0 + u * SEG_THREADS + tid;
+            if (t >= T) continue;
+            const int32_t k = cached ? key[u] : tok_a[t];
+            if (k >= 0 && (hist[k] & 0x40000000)) {
+                tok_a[t] = -1;
+                tok_r[t] = 0;
+                if (cached) key[u] = -1;
+            }
         }
     }
     __syncthreads();
     for (int a = tid; a < max_adapters; a += SEG_THREADS) {
-        const int32_t c = max(hist[a], 0);
+        const int32_t c = (hist[a] & 0x40000000) ? 0 : hist[a];
         hist[a] = c;
         segf[a] = c > 0;
         seglen[a] = c;
@@ -127,8 +182,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
 
     // 4. segments in adapter order
     for (int a = tid; a < max_adapters; a += SEG_THREADS) {
-        const int32_t c = seglen[a];
-        if (c > 0) {
+        if (seglen[a] > 0) {
             seg_a[segf[a]] = a;
             seg_start[segf[a]] = hist[a];
         }
@@ -140,40 +194,25 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     }
     __syncthreads();
 
-    // 5. stable scatter into perm: token chunks in order, waves of a chunk in order, lanes of a
-    //    wave ranked among equal keys by ballot
-    for (int c0 = 0; c0 < T; c0 += SEG_THREADS) {
-        const int t = c0 + tid;
-        const int32_t key = t < T ? tok_a[t] : -1;
-        int rank_in = 0, cnt = 0;
-        uint64_t remaining = __ballot(key >= 0);
-        while (remaining) {
-            const int leader = __ffsll((unsigned long long)remaining) - 1;
-            const int32_t lk = __shfl(key, leader, 64);
-            const uint64_t m = __ballot(key == lk);
-            if (key == lk) {
-                rank_in = __popcll(m & ((1ull << lane) - 1ull));
-                cnt = __popcll(m);
-            }
-            remaining &= ~m;
-        }
-        for (int w = 0; w < SEG_THREADS / 64; ++w) {
-            if (wave == w && key >= 0) {
-                const int32_t base = hist[key];
-                perm[base + rank_in] = t;
-                if (rank_in == cnt - 1) hist[key] = base + cnt;
-            }
-            __syncthreads();
+    // 5. scatter token ids into their segments
+    for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int t = t0 + u * SEG_THREADS + tid;
+            if (t >= T) continue;
+            const int32_t k = cached ? key[u] : tok_a[t];
+            if (k >= 0) perm[atomicAdd(&hist[k], 1)] = t;
         }
     }
+    __syncthreads();
 
     // 6. shrink work items: each segment split into runs of `chunk` tokens
     for (int s = tid; s < max_adapters; s += SEG_THREADS)
-        segf[s] = s < nseg ? (seg_start[s + 1] - seg_start[s] + chunk - 1) / chunk : 0;
+        segf[s] = s < nseg ? (seglen[seg_a[s]] + chunk - 1) / chunk : 0;
     __syncthreads();
     const int32_t nitems = block_exclusive_scan(segf, max_adapters, scratch);
     for (int s = tid; s < nseg; s += SEG_THREADS) {
-        const int32_t b = seg_start[s], e = seg_start[s + 1];
+        const int32_t b = seg_start[s], e = b + seglen[seg_a[s]];
         int32_t it = segf[s];
         for (int32_t r0 = b; r0 < e; r0 += chunk, ++it) {
             item_seg[it] = s;
@@ -238,7 +277,7 @@ hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws, c
     hipLaunchKernelGGL(k_segments, dim3(1), dim3(SEG_THREADS), lds, s, ids, ranks, pt, 2 * p->max_rank,
                        (int32_t)plan.T, p->max_adapters, p->max_rank, p->num_pages, plan.chunk, ws.tok_a, ws.tok_r,
                        ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.ctrl, ws.counters,
-                       plan.n_tiles, p->dev_err);
+                       plan.n_counters, p->dev_err);
     return hipGetLastError();
 }
 

@@ -48,11 +48,17 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
             pl->mb = 4;
         }
         pl->n_tiles = (int32_t)(H / 64);
-        pl->ysplit = (int32_t)std::min<int64_t>(8, std::max<int64_t>(1, (256 + pl->n_tiles - 1) / pl->n_tiles));
+        // splits of K so that the base workgroups cover the 256 CUs: a power of two in [1, 8]
+        int32_t sp = 1;
+        while (sp < 8 && (int64_t)pl->n_tiles * sp < 256) sp *= 2;
+        pl->ysplit = sp;
+        pl->n_shrink = (int32_t)std::min<int64_t>(256, std::max<int64_t>(16, 8 * T));
     } else if (pl->path == PATH_PREFILL) {
         pl->vsplit = 8;
         pl->n_tiles = 0;
     }
+    pl->rp = (int32_t)((R + 15) / 16 * 16);
+    pl->n_counters = 0;   // no kernel uses arrival counters (cross-workgroup sums go through kernel boundaries)
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
     pl->off_tok_a = take(T * 4);
@@ -63,9 +69,11 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     pl->off_item_seg = take((size_t)pl->n_items_max * 4);
     pl->off_item_row = take((size_t)pl->n_items_max * 4);
     pl->off_ctrl = take(CTRL_WORDS * 4);
-    pl->off_counters = take((size_t)std::max(pl->n_tiles, 1) * 4);
-    pl->off_v = take((size_t)pl->vsplit * T * R * 4);
-    pl->off_ypart = take(pl->path == PATH_DECODE && pl->ysplit > 1 ? (size_t)pl->ysplit * T * H * 4 : 0);
+    pl->off_counters = take((size_t)std::max(pl->n_counters, 1) * 4);
+    pl->off_v = take((size_t)pl->vsplit * T * (pl->path == PATH_PREFILL ? pl->rp : R) * 4);
+    pl->off_ypart = take(pl->path == PATH_DECODE ? (size_t)pl->ysplit * T * H * 4 : 0);
+    pl->off_sorted_tok = take(pl->path == PATH_DECODE ? (size_t)T * 16 : 0);
+    pl->off_v16 = take(pl->path == PATH_PREFILL ? (size_t)T * pl->rp * 2 : 0);
     pl->total = o;
     return true;
 }
@@ -84,6 +92,8 @@ Ws carve(void *base, const Plan &pl) {
     w.counters = (int32_t *)(b + pl.off_counters);
     w.v = (float *)(b + pl.off_v);
     w.ypart = (float *)(b + pl.off_ypart);
+    w.sorted_tok = (int32_t *)(b + pl.off_sorted_tok);
+    w.v16 = (uint16_t *)(b + pl.off_v16);
     return w;
 }
 
@@ -128,11 +138,16 @@ extern "C" int lora_project(lora_pool *p, const void *x, const void *W, const in
         if (slot < p->prof_max) ev = &p->prof_events[(size_t)slot * 4];
     }
     if (ev) LP_HIP(hipEventRecord(ev[0], s));
-    hipError_t e = launch_segments(p, pl, w, ids, ranks, pt, s);
-    if (e != hipSuccess) return hip_error(e, "segment kernel launch");
+    hipError_t e = hipSuccess;
+    if (pl.path != PATH_DECODE) {   // the decode path groups tokens inside its first kernel
+        e = launch_segments(p, pl, w, ids, ranks, pt, s);
+        if (e != hipSuccess) return hip_error(e, "segment kernel launch");
+    }
     if (ev) LP_HIP(hipEventRecord(ev[1], s));
     switch (pl.path) {
-        case PATH_DECODE: e = launch_decode(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
+        case PATH_DECODE:
+            e = launch_decode(p, pl, w, x, W, ids, ranks, pt, scale, y, s, ev ? ev[2] : nullptr);
+            break;
         case PATH_PREFILL: e = launch_prefill(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
         case PATH_F32: e = launch_f32(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
     }
@@ -166,11 +181,9 @@ extern "C" int lora_profile_stop(lora_pool *p, lora_profile_t *out) {
         LP_HIP(hipEventElapsedTime(&a, ev[0], ev[1]));
         LP_HIP(hipEventElapsedTime(&b, ev[1], ev[2]));
         LP_HIP(hipEventElapsedTime(&c, ev[2], ev[3]));
-        out->ms_segments += a;
-        out->ms_shrink += b;
-        out->ms_main += c;
-        out->ms_main_min = i == 0 ? c : std::min<double>(out->ms_main_min, c);
-        out->ms_main_max = std::max<double>(out->ms_main_max, c);
+        out->ms_group += a;
+        out->ms_first += b;
+        out->ms_second += c;
     }
     out->calls = n;
     for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
