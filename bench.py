@@ -168,17 +168,19 @@ def main():
         Ws = [w.W(s).clone() for s in slots]
         xs = [w.x(i2).clone() for i2 in range(w.n_x)]
         ys = [torch.empty_like(xs[0]) for _ in slots]
-        ws = pool.workspace(w.T)
-        reps.append((pool, Ws, xs, ys, ws))
+        reps.append((pool, Ws, xs, ys))
         if w.name == "many":
             w.drop_cache("AB")
-    wsb = reps[0][4].numel()
+    # one workspace shared by every replica, as a caller issuing the calls on one stream would
+    ws = torch.empty(max(rg.lora_project_workspace_size(p.handle, w.T) for p, *_ in reps), dtype=torch.uint8,
+                     device=dev)
+    wsb = ws.numel()
     log(f"replicas: {R}")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def step(i):
-        pool, Ws, xs, ys, ws = reps[i % R]
+        pool, Ws, xs, ys = reps[i % R]
         for s in slots:
             rg._lib.lora_project(pool.handle, xs[w.slot_x[s]].data_ptr(), Ws[s].data_ptr(), pool.table[s].data_ptr(),
                                  d_ids.data_ptr(), d_ranks.data_ptr(), d_scale.data_ptr(), w.T, ys[s].data_ptr(),

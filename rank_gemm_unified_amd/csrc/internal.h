@@ -92,10 +92,13 @@ struct Plan {
     int32_t wm;             // decode: waves along M (4 / wm along K)
     int32_t n_shrink;       // decode: shrink workgroups beside the base workgroups
     int32_t n_counters;     // arrival counters the grouping kernel zeroes
-    int32_t rp;             // prefill: row stride of v (max_rank rounded up to 16)
+    int32_t rp;             // row stride of v and per-token page lists (max_rank rounded up to 16)
+    int32_t stream;         // decode: 1 = streaming kernel (T <= 64), 0 = shrink/base workgroups
+    int32_t ks;             // decode streaming kernel: max K steps of 32 per split
+    int32_t nw;             // decode streaming kernel: W-waves (16 columns each) per workgroup
     // byte offsets into the workspace
     size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row,
-        off_ctrl, off_counters, off_v, off_ypart, off_sorted_tok, off_v16, total;
+        off_ctrl, off_counters, off_v, off_ypart, off_sorted_tok, off_v16, off_spages, total;
 };
 
 bool make_plan(const lora_pool *p, int64_t T, Plan *plan);
@@ -105,6 +108,7 @@ struct Ws {
     float *v, *ypart;
     int32_t *sorted_tok;    // decode: int4 {token, adapter or -1, rank, 0} per sorted position
     uint16_t *v16;          // prefill: v = s x A in bfloat16, [T][rp]
+    int32_t *spages;        // decode: B page ids per sorted position, [T][rp]
 };
 Ws carve(void *base, const Plan &plan);
 

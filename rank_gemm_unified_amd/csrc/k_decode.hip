@@ -1,24 +1,22 @@
 // Decode-shaped projection (T <= 256 tokens, typically one per request): memory-bound, so the
 // kernels are organised to stream W and the gathered A/B pages from HBM once, with as few
-// dependent global round trips as possible.
+// dependent global round trips as possible and no in-kernel cross-workgroup waits (on this chip a
+// device-scope fence writes back and invalidates the whole L2).
 //
 // Two launches per call:
-//   k_decode_main    two kinds of workgroup side by side, no waiting on each other:
-//                    * shrink workgroups: group the tokens by adapter in LDS (every one of them
-//                      derives the same grouping from the ids), then one wave per gathered A page
-//                      computes v[t][j] = s_a <x_t, A_a[:, j]> for the tokens of that adapter
-//                      (the first of the "two skinny matmuls", "S-LoRA, in depth", section "Merge
-//                      or keep adapters separate").  Workgroup 0 also validates the page-table
-//                      rows in use and publishes the sorted token list.
-//                    * base workgroups: y0 = x W with bf16 MFMA, split over K; each writes a
-//                      float32 partial for its 64-column tile.
-//   k_decode_finish  per (64-column tile, 8 sorted tokens): sums the K partials in split order,
-//                    adds the expand sum_j v[t][j] B_a[j, n] from B rows gathered from their
-//                    pages, and rounds once to bfloat16.
+//   T <= 64:       k_decode_stream   W, x and the batch's A pages in one streaming MFMA pass
+//                                    (the shrink x A is extra MFMA columns of the same contraction)
+//   64 < T <= 256: k_decode_main     shrink workgroups (one wave per gathered A page) beside split-K
+//                                    base workgroups
+//   then           k_decode_finish   partial sums in split order + the expand sum_j v_j B_a[j, :]
+//                                    from B rows gathered from their pages + one rounding
+// ("S-LoRA, in depth", section "Merge or keep adapters separate": xW batched over all tokens
+// whatever their adapter, plus two skinny products per adapter; section "Kernels for a batch of
+// mixed ranks": low-rank work follows tokens and ranks, adapter traffic follows distinct adapters.)
 // Every sum has a fixed order, so results are bitwise reproducible.
 //
-// The float32 path (parity-only, small shapes) keeps the grouping kernel, a gathered shrink and
-// a plain VALU kernel.
+// The float32 path (parity-only, small shapes) keeps the grouping kernel, a gathered shrink and a
+// plain VALU kernel.
 #include "device_common.h"
 #include "internal.h"
 
@@ -26,8 +24,19 @@ namespace lorapool {
 
 constexpr int CHUNK = 16;      // tokens per shrink work item
 constexpr int DEC_T = 256;     // most tokens on the decode path
-constexpr int NT = 64;         // columns per base tile
+constexpr int NT = 64;         // columns per base tile (64 < T <= 256 kernel)
 constexpr int NB = NT / 16;    // 16-column MFMA blocks per tile
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glob_void;
+
+// s_barrier with no memory fence; the asm statements keep the compiler from moving memory
+// accesses across it.  Callers make their own LDS writes complete first.
+__device__ __forceinline__ void workgroup_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // One wave: v[tok[i]][j] = sc * <x[tok[i]], page> for i < n (1 <= n <= CHUNK).
 // Tokens go in groups of G; for each group the page is read in blocks of BLK 16-byte vectors per
@@ -98,22 +107,25 @@ __device__ __forceinline__ void shrink_page_wave(const char *__restrict__ x, con
     }
 }
 
-// ---- in-LDS grouping of <= 256 tokens by adapter (256 threads, thread = token) -------------------
+// ---- in-LDS grouping of <= 256 tokens by adapter (thread t handles token t) ---------------------
 struct DecGroup {
     int32_t key[DEC_T];        // adapter id, or -1 (none, rank 0, id or rank out of range)
     int32_t r[DEC_T];
     int32_t seg[DEC_T];        // segment of a token with key >= 0
     int32_t seg_a[DEC_T], seg_r[DEC_T], seg_n[DEC_T], seg_bad[DEC_T];
     int32_t seg_off[DEC_T + 1];    // first sorted position of each segment
-    int32_t item_off[DEC_T + 1];   // first shrink item of each segment
-    int32_t chk_off[DEC_T + 1];    // first page-table entry to check of each segment (workgroup 0)
+    int32_t item_off[DEC_T + 1];   // first 16-token shrink item of each segment
+    int32_t page_off[DEC_T + 1];   // first page of each segment in the batch's page list
+    int32_t chk_off[DEC_T + 1];    // first page-table entry to check of each segment
     int32_t sorted[DEC_T];     // sorted position -> token
     int32_t wsum[8];
-    int32_t n_seg, n_valid, n_items, n_chk;
+    int32_t n_seg, n_valid, n_items, n_pages, n_chk;
 };
 
-// exclusive prefix of v over the 256 threads; *total gets the sum (all threads)
-__device__ int32_t scan256(int32_t v, int32_t *wsum, int32_t *total) {
+// exclusive prefix of v over the NTH threads; *total gets the sum (all threads)
+template <int NTH>
+__device__ int32_t scan_block(int32_t v, int32_t *wsum, int32_t *total) {
+    constexpr int NW = NTH / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int32_t incl = v;
 #pragma unroll
@@ -124,9 +136,13 @@ __device__ int32_t scan256(int32_t v, int32_t *wsum, int32_t *total) {
     __syncthreads();
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        before += w < wave ? wsum[w] : 0;
+        tot += wsum[w];
+    }
+    *total = tot;
     return before + incl - v;
 }
 
@@ -140,27 +156,30 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int32_t i) {
     return lo;
 }
 
+// Every workgroup that needs the grouping derives it from the ids; all derive the same one.
+// Returns the id/rank error bits this thread saw.
+template <int NTH>
 __device__ int dec_group(DecGroup &g, const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks,
                          int32_t T, int32_t max_adapters, int32_t max_rank, int32_t stride) {
     const int t = threadIdx.x;
+    const bool tok_thread = t < DEC_T;
     int err = 0;
     int32_t key = -1, r = 0;
     if (t < T) {
         const int32_t a = ids[t];
+        const int32_t rr = ranks[a >= 0 && a < max_adapters ? a : 0];
         if (a != -1) {
-            if (a < -1 || a >= max_adapters) {
-                err |= DEV_ERR_ID;
-            } else {
-                const int32_t rr = ranks[a];
-                if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
-                else if (rr > 0) { key = a; r = rr; }
-            }
+            if (a < -1 || a >= max_adapters) err |= DEV_ERR_ID;
+            else if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
+            else if (rr > 0) { key = a; r = rr; }
         }
     }
-    g.key[t] = key;
-    g.r[t] = r;
-    g.seg_n[t] = 0;
-    g.seg_bad[t] = 0;
+    if (tok_thread) {
+        g.key[t] = key;
+        g.r[t] = r;
+        g.seg_n[t] = 0;
+        g.seg_bad[t] = 0;
+    }
     __syncthreads();
     int32_t first = t, rank_in = 0;
     if (key >= 0) {
@@ -173,7 +192,7 @@ __device__ int dec_group(DecGroup &g, const int32_t *__restrict__ ids, const int
     }
     const int is_first = key >= 0 && rank_in == 0;
     int32_t nseg;
-    const int32_t sid = scan256(is_first, g.wsum, &nseg);
+    const int32_t sid = scan_block<NTH>(is_first, g.wsum, &nseg);
     if (is_first) {
         g.seg[t] = sid;
         g.seg_a[sid] = key;
@@ -186,28 +205,32 @@ __device__ int dec_group(DecGroup &g, const int32_t *__restrict__ ids, const int
         atomicAdd(&g.seg_n[my_seg], 1);
     }
     __syncthreads();
-    // per segment (thread s): token offsets, shrink items, entries to check
-    const int32_t n_s = t < nseg ? g.seg_n[t] : 0;
-    const int32_t r_s = t < nseg ? g.seg_r[t] : 0;
-    int32_t nvalid, nitems, nchk;
-    const int32_t off = scan256(n_s, g.wsum, &nvalid);
-    const int32_t ioff = scan256(r_s * ((n_s + CHUNK - 1) / CHUNK), g.wsum, &nitems);
-    const int32_t coff = scan256(t < nseg ? min(2 * r_s + 1, stride) : 0, g.wsum, &nchk);
-    if (t < nseg) {
+    // per segment (thread s): token offsets, shrink items, pages, entries to check
+    const bool seg_thread = t < nseg;
+    const int32_t n_s = seg_thread ? g.seg_n[t] : 0;
+    const int32_t r_s = seg_thread ? g.seg_r[t] : 0;
+    int32_t nvalid, nitems, npages, nchk, nid;
+    const int32_t off = scan_block<NTH>(n_s, g.wsum, &nvalid);
+    const int32_t ioff = scan_block<NTH>(r_s * ((n_s + CHUNK - 1) / CHUNK), g.wsum, &nitems);
+    const int32_t poff = scan_block<NTH>(r_s, g.wsum, &npages);
+    const int32_t coff = scan_block<NTH>(seg_thread ? min(2 * r_s + 1, stride) : 0, g.wsum, &nchk);
+    // identity / invalid tokens go after the grouped ones, in token order
+    const int32_t idpos = scan_block<NTH>(t < T && key < 0, g.wsum, &nid);
+    if (seg_thread) {
         g.seg_off[t] = off;
         g.item_off[t] = ioff;
+        g.page_off[t] = poff;
         g.chk_off[t] = coff;
     }
-    // identity / invalid tokens go after the grouped ones, in token order
-    int32_t nid;
-    const int32_t idpos = scan256(t < T && key < 0, g.wsum, &nid);
     if (t == 0) {
         g.n_seg = nseg;
         g.n_valid = nvalid;
         g.n_items = nitems;
+        g.n_pages = npages;
         g.n_chk = nchk;
         g.seg_off[nseg] = nvalid;
         g.item_off[nseg] = nitems;
+        g.page_off[nseg] = npages;
         g.chk_off[nseg] = nchk;
     }
     __syncthreads();
@@ -216,73 +239,310 @@ __device__ int dec_group(DecGroup &g, const int32_t *__restrict__ ids, const int
     return err;
 }
 
-// ---- launch 1: shrink workgroups + base workgroups -------------------------------------------------
+// Workgroup 0's extra duty: check every page-table row in use (exactly 2r in-range pages, -1 after),
+// publish the sorted token list {token, adapter or -1, rank, 0} and, per sorted position, the token's
+// B page ids (row entries r..2r-1) for the finishing kernel; report errors.
+template <int NTH>
+__device__ void dec_publish(DecGroup &g, int err, const int32_t *__restrict__ pt, int32_t stride,
+                            int64_t num_pages, int32_t T, int32_t RP, int4 *__restrict__ sorted_tok,
+                            int32_t *__restrict__ spages, int *__restrict__ err_word) {
+    const int nseg = g.n_seg;
+    for (int e0 = threadIdx.x; e0 < g.n_chk; e0 += NTH * 4) {
+        int32_t ent[4];
+        int sg[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = min(e0 + u * NTH, g.n_chk - 1);
+            sg[u] = find_seg(g.chk_off, nseg, e);
+            ent[u] = pt[(int64_t)g.seg_a[sg[u]] * stride + (e - g.chk_off[sg[u]])];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * NTH;
+            if (e >= g.n_chk) continue;
+            const int s = sg[u], j = e - g.chk_off[s], r = g.seg_r[s];
+            int bad = 0;
+            if (j < 2 * r) {
+                if (ent[u] == -1) bad = DEV_ERR_TABLE;
+                else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad = DEV_ERR_PAGE;
+            } else if (ent[u] != -1) {
+                bad = DEV_ERR_TABLE;
+            }
+            if (bad) {
+                atomicOr(&g.seg_bad[s], bad);
+                err |= bad;
+            }
+            if (j >= r && j < 2 * r) {   // a B page: give it to every sorted position of the segment
+                for (int q = g.seg_off[s]; q < g.seg_off[s + 1]; ++q) spages[(int64_t)q * RP + (j - r)] = ent[u];
+            }
+        }
+    }
+    __syncthreads();
+    const int p = threadIdx.x;
+    if (p < T) {
+        const int32_t tt = g.sorted[p];
+        int32_t a = -1, r = 0;
+        if (p < g.n_valid) {
+            const int s = find_seg(g.seg_off, nseg, p);
+            if (!g.seg_bad[s]) {
+                a = g.seg_a[s];
+                r = g.seg_r[s];
+            }
+        }
+        sorted_tok[p] = int4{tt, a, r, 0};
+    }
+    if (err) atomicOr(err_word, err);
+}
+
+// ---- decode, T <= 64: streaming kernel ----------------------------------------------------------
+//
+// Grid n_tiles x S workgroups, about one per CU.  Workgroup (tile, split) owns output columns
+// [16 NW tile, 16 NW (tile + 1)) and the K chunk [kb, ke) of split.  A wave's vector-memory loads
+// retire in issue order, so a wave that waits on a dependent chain (ids -> ranks -> page table ->
+// pages) must not also have the W stream queued in front of it.  Hence two kinds of wave:
+//  * NW W-waves: each issues its whole W slice (16 output columns x the K chunk) at once, stages its
+//    share of x's K chunk in LDS (the MFMA A operand of every wave), and writes x W partials;
+//  * one meta-wave: reads the ids and ranks, groups the <= 64 tokens by adapter with wave ballots,
+//    takes this tile's blocks of 16 pages from the batch's A-page list (adapters in order of first
+//    token, pages 0..r-1 each), computes s x A for them over the same K chunk as extra MFMA columns
+//    (the shrink), and validates and publishes its share of the adapters' page-table rows.
+// Outputs: float32 partials of x W and of s x A, one per split; k_decode_finish adds them in split
+// order.  The workgroup has a single barrier (x staged).
+template <int MB, int KS, int NW>   // T <= 16 MB; K chunk <= 32 KS; NW W-waves of 16 columns
+__global__ __launch_bounds__((NW + 1) * 64, 1) void k_decode_stream(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
+    int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
+    float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
+    int *__restrict__ err_word) {
+    constexpr int TP = MB * 16;
+    constexpr int XS = KS * 32;        // LDS row of x (elements), swizzled in 16-byte pieces
+    extern __shared__ __align__(16) char lds_raw[];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds_raw);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tile = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
+    const int ksteps = H / 32;
+    const int kb = (int)((int64_t)ksteps * split / S) * 32, ke = (int)((int64_t)ksteps * (split + 1) / S) * 32;
+    const int nst = (ke - kb) / 32;
+    const int lrow = lane & 15, lk = (lane >> 4) * 8;
+    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+
+    if (wave < NW) {
+        // ------------------------------------------------------------------ W-wave
+        // x's K chunk goes straight to LDS (no registers); 16-byte piece c of row `row` lands in
+        // slot c ^ (row & 15), so the 16 rows an MFMA operand read touches hit distinct banks.
+        // Rows >= T and pieces past the chunk hold copies of valid data: their results are never
+        // stored and their K steps are never read.
+        constexpr int XI = TP * KS * 4 / 64;   // wave-wide direct-to-LDS loads
+        for (int i = wave; i < XI; i += NW) {
+            const int L = i * 64 + lane;
+            const int row = L / (KS * 4), c = (L % (KS * 4)) ^ (row & 15);
+            const bool live = row < T && c * 8 < ke - kb;
+            const uint16_t *src = x + (int64_t)(live ? row : 0) * H + kb + (live ? c * 8 : 0);
+            __builtin_amdgcn_global_load_lds((glob_void *)src, (lds_void *)(xs + i * 64 * 8), 16, 0, 0);
+        }
+        const int wn = tile * NW * 16 + wave * 16 + lrow;   // output column this lane loads
+        const bool wlive = wn < H;
+        const uint16_t *wr = W + (int64_t)(wlive ? wn : 0) * H + kb + lk;
+        u32x4_t wreg[KS];
+#pragma unroll
+        for (int st = 0; st < KS; ++st) wreg[st] = load16(wr + 32 * min(st, max(nst - 1, 0)));
+        __builtin_amdgcn_sched_barrier(0);   // keep every W load ahead of the barrier
+        // vector-memory ops retire in order: waiting until only the KS W loads are outstanding
+        // means this wave's x pieces are in LDS.  A plain barrier follows (a __syncthreads
+        // fence would wait for the W loads too).
+        __builtin_amdgcn_s_waitcnt((KS & 15) | ((KS >> 4) << 14) | 0xF70);
+        workgroup_barrier();
+        f32x4_t acc[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {   // branch-free: steps past the chunk multiply by zero
+            const u32x4_t wb = st < nst ? wreg[st] : zero;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const int row = m * 16 + lrow;
+                const u32x4_t xa = load16(xs + row * XS + (((st * 4 + (lk >> 3)) ^ (row & 15)) << 3));
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                                 __builtin_bit_cast(bf16x8_t, wb), acc[m], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep each K step's LDS reads next to its MFMAs
+        }
+        // accumulator layout: lane holds rows 4*(lane/16)+i of column lane%16
+        if (wlive) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = m * 16 + (lane >> 4) * 4 + i;
+                    if (t < T) ypart[((int64_t)split * T + t) * H + wn] = acc[m][i];
+                }
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------------- meta-wave (lane = token)
+    int err = 0;
+    int32_t key = -1, r = 0;
+    {
+        const int32_t a = lane < T ? ids[lane] : -1;
+        const int32_t rr = ranks[a >= 0 && a < max_adapters ? a : 0];
+        if (a != -1) {
+            if (a < -1 || a >= max_adapters) err |= DEV_ERR_ID;
+            else if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
+            else if (rr > 0) { key = a; r = rr; }
+        }
+    }
+    // group by key with ballots: rank within key, count, first lane; segments in first-lane order
+    int rank_in = 0, cnt = 0, first = lane;
+    {
+        uint64_t remaining = __ballot(key >= 0);
+        while (remaining) {
+            const int leader = __ffsll((unsigned long long)remaining) - 1;
+            const int32_t lkey = __shfl(key, leader, 64);
+            const uint64_t m = __ballot(key == lkey);
+            if (key == lkey) {
+                rank_in = __popcll(m & ((1ull << lane) - 1ull));
+                cnt = __popcll(m);
+                first = leader;
+            }
+            remaining &= ~m;
+        }
+    }
+    const uint64_t first_mask = __ballot(key >= 0 && rank_in == 0);
+    const int nseg = __popcll(first_mask);
+    const int my_seg = key >= 0 ? __popcll(first_mask & ((1ull << first) - 1ull)) : -1;
+    // lane s < nseg describes segment s: the s-th first lane
+    int32_t seg_lane = 0;
+    {
+        uint64_t fm = first_mask;
+        for (int s = 0; s < nseg; ++s) {
+            const int l = __ffsll((unsigned long long)fm) - 1;
+            if (lane == s) seg_lane = l;
+            fm &= fm - 1;
+        }
+    }
+    const int32_t seg_a = __shfl(key, seg_lane, 64), seg_r = __shfl(r, seg_lane, 64), seg_n = __shfl(cnt, seg_lane, 64);
+    const bool segl = lane < nseg;
+    // prefix sums over segments: pages (r) and tokens (n)
+    int32_t poff = segl ? seg_r : 0, toff = segl ? seg_n : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y1 = __shfl_up(poff, off, 64), y2 = __shfl_up(toff, off, 64);
+        if (lane >= off) { poff += y1; toff += y2; }
+    }
+    const int32_t npages = __shfl(poff, 63, 64), nvalid = __shfl(toff, 63, 64);
+    poff -= segl ? seg_r : 0;   // exclusive
+    toff -= segl ? seg_n : 0;
+    // sorted position of this lane's token: grouped tokens first (segments in order), then the rest
+    const int idrank = __popcll(__ballot(lane < T && key < 0) & ((1ull << lane) - 1ull));
+    const int32_t seg_first_pos = __shfl(toff, max(my_seg, 0), 64);   // every lane shuffles
+    const int my_pos = key >= 0 ? seg_first_pos + rank_in : nvalid + idrank;
+
+    // this tile's page blocks: pages [16 b, 16 b + 16) of the list, b = tile + k * n_tiles
+    f32x4_t pacc[MB];
+    for (int b = tile; b * 16 < npages; b += n_tiles) {
+        const int p = min(b * 16 + lrow, npages - 1);
+        const bool plive = b * 16 + lrow < npages;
+        int sg = 0;   // segment of page p: last s with poff[s] <= p
+        for (int s = 1; s < nseg; ++s) sg += __shfl(poff, s, 64) <= p ? 1 : 0;
+        const int32_t pa = __shfl(seg_a, sg, 64), pj = p - __shfl(poff, sg, 64);
+        int32_t pid = pt[(int64_t)pa * stride + pj];
+        if (pid < 0 || (int64_t)pid >= num_pages) pid = 0;   // the row is reported below; token dropped
+        const uint16_t *ap = pages + (int64_t)pid * H + kb + lk;
+        u32x4_t preg[KS];
+#pragma unroll
+        for (int st = 0; st < KS; ++st) preg[st] = load16(ap + 32 * min(st, max(nst - 1, 0)));
+        if (b == tile) workgroup_barrier();   // x staged (the workgroup's only barrier)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) pacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const u32x4_t bb = plive && st < nst ? preg[st] : zero;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const int row = m * 16 + lrow;
+                const u32x4_t xa = load16(xs + row * XS + (((st * 4 + (lk >> 3)) ^ (row & 15)) << 3));
+                pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                                  __builtin_bit_cast(bf16x8_t, bb), pacc[m], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float sc = scale[pa];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = m * 16 + (lane >> 4) * 4 + i;
+                const int32_t key_t = __shfl(key, t & 63, 64);   // outside any condition: all lanes active
+                if (plive && t < T && key_t == pa) vpart[((int64_t)t * RP + pj) * S + split] = sc * pacc[m][i];
+            }
+    }
+    if (tile * 16 >= npages) workgroup_barrier();   // no page block: still meet the barrier once
+
+    // publish: segments s = blockIdx.x + k * gridDim.x -- check the page-table row, then write the
+    // segment's sorted-token records and B page ids; workgroup 0 also writes the ungrouped tokens
+    for (int s = blockIdx.x; s < nseg; s += gridDim.x) {
+        const int32_t a = __shfl(seg_a, s, 64), rs = __shfl(seg_r, s, 64);
+        const int32_t q0 = __shfl(toff, s, 64), qn = __shfl(seg_n, s, 64);
+        const int lim = min(2 * rs + 1, stride);
+        int32_t ent[3];
+        int bad = 0;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int j = lane + 64 * u;
+            ent[u] = pt[(int64_t)a * stride + min(j, lim - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int j = lane + 64 * u;
+            if (j >= lim) continue;
+            if (j < 2 * rs) {
+                if (ent[u] == -1) bad |= DEV_ERR_TABLE;
+                else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad |= DEV_ERR_PAGE;
+            } else if (ent[u] != -1) {
+                bad |= DEV_ERR_TABLE;
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) bad |= __shfl_xor(bad, off, 64);
+        err |= bad;
+        // B page ids to every sorted position of the segment
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int j = lane + 64 * u;
+            if (j >= rs && j < 2 * rs)
+                for (int q = q0; q < q0 + qn; ++q) spages[(int64_t)q * RP + (j - rs)] = ent[u];
+        }
+        if (key == a) sorted_tok[my_pos] = int4{lane, bad ? -1 : a, bad ? 0 : rs, 0};
+    }
+    // id/rank faults are per lane and every workgroup sees them: workgroup 0 reports them; page-table
+    // faults were already OR-reduced over the wave by the workgroup that checked the row
+    for (int off = 32; off > 0; off >>= 1) err |= __shfl_xor(err, off, 64);
+    if (blockIdx.x == 0 && lane < T && key < 0) sorted_tok[my_pos] = int4{lane, -1, 0, 0};
+    if (lane == 0) {
+        const int mine = blockIdx.x == 0 ? err : err & (DEV_ERR_TABLE | DEV_ERR_PAGE);
+        if (mine) atomicOr(err_word, mine);
+    }
+}
+
+// ---- decode, 64 < T <= 256: shrink workgroups + base workgroups side by side ---------------------------
 template <int MB, int WM>
 __global__ __launch_bounds__(256, 2) void k_decode_main(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
-    int32_t T, int32_t H, int32_t n_shrink, float *__restrict__ v, int4 *__restrict__ sorted_tok,
-    float *__restrict__ ypart, int *__restrict__ err_word) {
+    int32_t T, int32_t H, int32_t n_shrink, int32_t RP, float *__restrict__ vpart, int4 *__restrict__ sorted_tok,
+    int32_t *__restrict__ spages, float *__restrict__ ypart, int *__restrict__ err_word) {
     extern __shared__ __align__(16) char lds_raw[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int R = max_rank;
 
     if ((int)blockIdx.x < n_shrink) {
         // ------------------------------------------------------------ shrink role
         DecGroup &g = *reinterpret_cast<DecGroup *>(lds_raw);
-        int err = dec_group(g, ids, ranks, T, max_adapters, max_rank, stride);
+        const int err = dec_group<256>(g, ids, ranks, T, max_adapters, max_rank, stride);
+        if (blockIdx.x == 0) dec_publish<256>(g, err, pt, stride, num_pages, T, RP, sorted_tok, spages, err_word);
         const int nseg = g.n_seg;
-        if (blockIdx.x == 0) {
-            // validate every page-table row in use; publish the sorted token list
-            for (int e0 = threadIdx.x; e0 < g.n_chk; e0 += 256 * 8) {
-                int32_t ent[8];
-                int sg[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int e = e0 + u * 256;
-                    sg[u] = -1;
-                    if (e < g.n_chk) {
-                        sg[u] = find_seg(g.chk_off, nseg, e);
-                        const int j = e - g.chk_off[sg[u]];
-                        ent[u] = pt[(int64_t)g.seg_a[sg[u]] * stride + j];
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    if (sg[u] < 0) continue;
-                    const int j = e0 + u * 256 - g.chk_off[sg[u]];
-                    const int r = g.seg_r[sg[u]];
-                    int bad = 0;
-                    if (j < 2 * r) {
-                        if (ent[u] == -1) bad = DEV_ERR_TABLE;
-                        else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad = DEV_ERR_PAGE;
-                    } else if (ent[u] != -1) {
-                        bad = DEV_ERR_TABLE;
-                    }
-                    if (bad) {
-                        atomicOr(&g.seg_bad[sg[u]], bad);
-                        err |= bad;
-                    }
-                }
-            }
-            __syncthreads();
-            const int p = threadIdx.x;
-            if (p < T) {
-                const int32_t tt = g.sorted[p];
-                int32_t a = -1, r = 0;
-                if (p < g.n_valid) {
-                    const int s = find_seg(g.seg_off, nseg, p);
-                    if (!g.seg_bad[s]) {
-                        a = g.seg_a[s];
-                        r = g.seg_r[s];
-                    }
-                }
-                sorted_tok[p] = int4{tt, a, r, 0};
-            }
-            if (err) atomicOr(err_word, err);
-        }
-        // one wave per (segment, token chunk, page j)
         const int nw = n_shrink * 4;
         for (int i = blockIdx.x * 4 + wave; i < g.n_items; i += nw) {
             const int s = find_seg(g.item_off, nseg, i);
@@ -296,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_main(
 #pragma unroll
             for (int u = 0; u < CHUNK; ++u) tok[u] = u < n ? g.sorted[g.seg_off[s] + chunk * CHUNK + u] : 0;
             shrink_page_wave<2>((const char *)x, (const char *)(pages + (int64_t)page * H), (int64_t)H * 2, tok, n,
-                                scale[a], j, v, R, lane);
+                                scale[a], j, vpart, RP, lane);
         }
         return;
     }
@@ -368,7 +628,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_main(
                                                                      __builtin_bit_cast(bf16x8_t, wb[nb]),
                                                                      acc[m][nb], 0, 0, 0);
     }
-    // accumulator layout (16x16 block): lane holds rows 4*(lane/16)+i of column lane%16
     float *mine = red + (size_t)wk * TP * NT;
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -394,68 +653,95 @@ __global__ __launch_bounds__(256, 2) void k_decode_main(
     }
 }
 
-// ---- launch 2: sum partials + expand + round --------------------------------------------------------
-// Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens).  Thread -> (token, 8 columns, quarter
-// of j); the four quarters meet by lane shuffles.  All loads are unconditional from valid addresses
-// (indices clamped into the token's own page row) so they issue together; only the sums select.
-template <int S>
+// ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
+// Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Round trip 1 reads, by
+// sorted position only, the token record and its B page ids; round trip 2 reads the B rows' column
+// slices, the v partials (summed in split order into LDS) and the x W partials.  Thread -> (token,
+// 8 columns, quarter of j: j in [16 q, 16 q + 16)); quarters meet by lane shuffles.
+template <int SY, int SV>
 __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ sorted_tok,
-                                                       const float *__restrict__ ypart,
-                                                       const float *__restrict__ v, int32_t R,
-                                                       const int32_t *__restrict__ pt, int32_t stride,
-                                                       const uint16_t *__restrict__ pages, int32_t H, int32_t T,
-                                                       uint16_t *__restrict__ y) {
+                                                       const int32_t *__restrict__ spages,
+                                                       const float *__restrict__ ypart, const float *__restrict__ vpart,
+                                                       int32_t RP, const uint16_t *__restrict__ pages, int32_t H,
+                                                       int32_t T, uint16_t *__restrict__ y) {
+    __shared__ float s_v[8][64];
     const int n0 = blockIdx.x * 64;
     const int i = threadIdx.x >> 5, c = ((threadIdx.x >> 2) & 7) * 8, q = threadIdx.x & 3;
-    const int sp = blockIdx.y * 8 + i;
-    if (sp >= T) return;   // whole quads leave together
+    const int sp = min((int)blockIdx.y * 8 + i, T - 1);
+    const bool live_tok = (int)blockIdx.y * 8 + i < T;
     const int4 st = sorted_tok[sp];
-    const int t = st.x, a = st.y, r = st.z;
-    f32x4_t part[S][2];
+    const int t = st.x, a = live_tok ? st.y : -1, r = st.z;
+    const bool has = a >= 0;
+    int32_t pid[16];
+    {
+        const int4 *pr = reinterpret_cast<const int4 *>(spages + (int64_t)sp * RP + 16 * min(q, RP / 16 - 1));
 #pragma unroll
-    for (int s = 0; s < S; ++s) {   // every lane loads; only quarter 0 adds them in
-        const float *src = ypart + ((int64_t)s * T + t) * H + n0 + c;
-        part[s][0] = *reinterpret_cast<const f32x4_t *>(src);
-        part[s][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
+        for (int u = 0; u < 4; ++u) {
+            const int4 v4 = pr[u];
+            pid[4 * u] = v4.x;
+            pid[4 * u + 1] = v4.y;
+            pid[4 * u + 2] = v4.z;
+            pid[4 * u + 3] = v4.w;
+        }
     }
+    // v[t][j] for j = 2 * (thread within token) + {0, 1}, summed over the SV partials in order
+    {
+        const int jj = (threadIdx.x & 31) * 2;
+        float v0 = 0.f, v1 = 0.f;
+        if (has && jj < RP) {
+            const float *src = vpart + ((int64_t)t * RP + jj) * SV;
+            float pv[2 * SV];
+#pragma unroll
+            for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
+#pragma unroll
+            for (int u = 0; u < SV; ++u) {
+                v0 += pv[u];
+                v1 += pv[SV + u];
+            }
+        }
+        s_v[i][jj] = jj < r ? v0 : 0.f;
+        s_v[i][jj + 1] = jj + 1 < r ? v1 : 0.f;
+    }
+    f32x4_t part[SY][2];
+    if (q == 0) {   // one lane of each quad needs the x W partials
+#pragma unroll
+        for (int s = 0; s < SY; ++s) {
+            const float *src = ypart + ((int64_t)s * T + t) * H + n0 + c;
+            part[s][0] = *reinterpret_cast<const f32x4_t *>(src);
+            part[s][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
+        }
+    }
+    const int j0 = 16 * q;
+    const bool qlive = has && j0 < r;
+    u32x4_t bv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int32_t pg = qlive && j0 + u < r ? pid[u] : pid[0];
+        bv[u] = load16(pages + (int64_t)(qlive ? pg : 0) * H + n0 + c);
+    }
+    __syncthreads();
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    if (a >= 0) {
-        const int j0 = q * r / 4, j1 = (q + 1) * r / 4;
-        const int32_t *prow = pt + (int64_t)a * stride + r;
-        const float *vt = v + (int64_t)t * R;
-        int32_t pid[16];
-        float vj[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int jj = min(j0 + u, r - 1);
-            pid[u] = prow[jj];
-            vj[u] = vt[jj];
-        }
-        u32x4_t bv[16];
+    for (int u = 0; u < 16; ++u) {
+        float bf[8];
+        unpack_bf16x8(bv[u], bf);
+        const float w = (qlive && j0 + u < r) ? s_v[i][j0 + u] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) bv[u] = load16(pages + (int64_t)pid[u] * H + n0 + c);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            float bf[8];
-            unpack_bf16x8(bv[u], bf);
-            const float w = j0 + u < j1 ? vj[u] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = j0 + u < j1 ? fmaf(w, bf[e], o[e]) : o[e];
-        }
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(w, bf[e], o[e]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         o[e] += __shfl_xor(o[e], 1, 64);
         o[e] += __shfl_xor(o[e], 2, 64);
     }
-    if (q == 0) {
+    if (q == 0 && live_tok) {
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int s = 0; s < S; ++s)   // base partials in split order, then the low-rank sum
+        for (int s = 0; s < SY; ++s)   // base partials in split order, then the low-rank sum
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 acc[e] += part[s][0][e];
@@ -526,6 +812,25 @@ __global__ __launch_bounds__(256) void k_project_f32(const float *__restrict__ x
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------
+template <int MB, int KS, int NW>
+static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
+                                const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
+                                hipStream_t s) {
+    const size_t lds = (size_t)MB * 16 * KS * 32 * 2;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_decode_stream<MB, KS, NW>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_decode_stream<MB, KS, NW>), dim3(plan.n_tiles * plan.ysplit), dim3((NW + 1) * 64), lds, s,
+                       (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)p->pages, p->num_pages, pt,
+                       2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden,
+                       plan.ysplit, plan.n_tiles, plan.rp, ws.ypart, ws.v, (int4 *)ws.sorted_tok, ws.spages, p->dev_err);
+    return hipGetLastError();
+}
+
 template <int MB, int WM>
 static hipError_t launch_main(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
                               const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
@@ -533,12 +838,30 @@ static hipError_t launch_main(const lora_pool *p, const Plan &plan, const Ws &ws
     constexpr int WK = 4 / WM;
     const size_t red = (size_t)WK * WM * MB * 16 * NT * sizeof(float);
     const size_t lds = red > sizeof(DecGroup) ? red : sizeof(DecGroup);
-    const int n_tiles = p->hidden / NT;
-    dim3 grid(plan.n_shrink + n_tiles * plan.ysplit);
+    dim3 grid(plan.n_shrink + plan.n_tiles * plan.ysplit);
     hipLaunchKernelGGL((k_decode_main<MB, WM>), grid, dim3(256), lds, s, (const uint16_t *)x, (const uint16_t *)W,
                        (const uint16_t *)p->pages, p->num_pages, pt, 2 * p->max_rank, ids, ranks, scale,
-                       p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.n_shrink, ws.v,
-                       (int4 *)ws.sorted_tok, ws.ypart, p->dev_err);
+                       p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.n_shrink, plan.rp, ws.v,
+                       (int4 *)ws.sorted_tok, ws.spages, ws.ypart, p->dev_err);
+    return hipGetLastError();
+}
+
+template <int SY, int SV>
+static void launch_finish_t(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
+    dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8));
+    hipLaunchKernelGGL((k_decode_finish<SY, SV>), grid, dim3(256), 0, s, (const int4 *)ws.sorted_tok, ws.spages,
+                       ws.ypart, ws.v, plan.rp, (const uint16_t *)p->pages, p->hidden, (int32_t)plan.T, (uint16_t *)y);
+}
+
+static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
+    const int sy = plan.ysplit, sv = plan.stream ? plan.ysplit : 1;
+    switch (sy * 16 + sv) {
+#define LP_CASE(A, B) case A * 16 + B: launch_finish_t<A, B>(p, plan, ws, y, s); break;
+        LP_CASE(1, 1) LP_CASE(2, 1) LP_CASE(4, 1) LP_CASE(8, 1)
+        LP_CASE(2, 2) LP_CASE(3, 3) LP_CASE(4, 4) LP_CASE(5, 5) LP_CASE(6, 6) LP_CASE(7, 7) LP_CASE(8, 8)
+#undef LP_CASE
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -546,31 +869,30 @@ hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, con
                          const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale, void *y,
                          hipStream_t s, hipEvent_t mid) {
     hipError_t e;
-    switch (plan.wm * 8 + plan.mb) {
-        case 1 * 8 + 1: e = launch_main<1, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-        case 1 * 8 + 2: e = launch_main<2, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-        case 1 * 8 + 3: e = launch_main<3, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-        case 1 * 8 + 4: e = launch_main<4, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-        case 2 * 8 + 4: e = launch_main<4, 2>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-        case 4 * 8 + 4: e = launch_main<4, 4>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-        default: return hipErrorInvalidValue;
+    if (plan.stream) {
+        switch (plan.nw * 4096 + plan.mb * 64 + plan.ks) {
+#define LP_CASE(M, K, N) case N * 4096 + M * 64 + K: e = launch_stream<M, K, N>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            LP_CASE(1, 8, 4) LP_CASE(1, 16, 4) LP_CASE(1, 32, 4) LP_CASE(1, 8, 8) LP_CASE(1, 16, 8) LP_CASE(1, 32, 8)
+            LP_CASE(2, 8, 4) LP_CASE(2, 16, 4) LP_CASE(2, 32, 4) LP_CASE(2, 8, 8) LP_CASE(2, 16, 8) LP_CASE(2, 32, 8)
+            LP_CASE(3, 8, 4) LP_CASE(3, 16, 4) LP_CASE(3, 32, 4) LP_CASE(3, 8, 8) LP_CASE(3, 16, 8) LP_CASE(3, 32, 8)
+            LP_CASE(4, 8, 4) LP_CASE(4, 16, 4) LP_CASE(4, 32, 4) LP_CASE(4, 8, 8) LP_CASE(4, 16, 8) LP_CASE(4, 32, 8)
+#undef LP_CASE
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (plan.wm * 8 + plan.mb) {
+            case 2 * 8 + 4: e = launch_main<4, 2>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            case 4 * 8 + 4: e = launch_main<4, 4>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            case 1 * 8 + 1: e = launch_main<1, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            case 1 * 8 + 2: e = launch_main<2, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            case 1 * 8 + 3: e = launch_main<3, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            case 1 * 8 + 4: e = launch_main<4, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            default: return hipErrorInvalidValue;
+        }
     }
     if (e != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
-    dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8));
-#define LP_FINISH(SS)                                                                                            \
-    hipLaunchKernelGGL(k_decode_finish<SS>, grid, dim3(256), 0, s, (const int4 *)ws.sorted_tok, ws.ypart, ws.v,     \
-                       p->max_rank, pt, 2 * p->max_rank, (const uint16_t *)p->pages, p->hidden, (int32_t)plan.T, \
-                       (uint16_t *)y)
-    switch (plan.ysplit) {
-        case 1: LP_FINISH(1); break;
-        case 2: LP_FINISH(2); break;
-        case 4: LP_FINISH(4); break;
-        case 8: LP_FINISH(8); break;
-        default: return hipErrorInvalidValue;
-    }
-#undef LP_FINISH
-    return hipGetLastError();
+    return launch_finish(p, plan, ws, y, s);
 }
 
 hipError_t launch_f32(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,

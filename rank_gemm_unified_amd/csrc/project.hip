@@ -36,28 +36,46 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     pl->vsplit = 1;
     pl->ysplit = 1;
     pl->n_tiles = 0;
+    pl->rp = (int32_t)((R + 15) / 16 * 16);
     if (pl->path == PATH_DECODE) {
-        if (T <= 64) {
-            pl->wm = 1;
+        const int64_t ksteps = H / 32;
+        if (T <= 64 && H <= 8192) {
+            // streaming kernel: tiles of 16 NW columns x S splits of K, about 200-256 workgroups
+            // (one per CU: x's K chunk fills most of the LDS); fewest splits that reach that count
+            pl->stream = 1;
             pl->mb = (int32_t)std::max<int64_t>(1, (T + 15) / 16);
-        } else if (T <= 128) {
-            pl->wm = 2;
-            pl->mb = 4;
+            for (int nw = 4; nw <= 8; nw *= 2) {
+                pl->nw = nw;
+                pl->n_tiles = (int32_t)((H + 16 * nw - 1) / (16 * nw));
+                const int64_t S = std::max<int64_t>(1, std::min<int64_t>(8, (200 + pl->n_tiles - 1) / pl->n_tiles));
+                pl->ysplit = (int32_t)S;
+                if ((ksteps + S - 1) / S <= 32) break;
+            }
+            const int64_t need = (ksteps + pl->ysplit - 1) / pl->ysplit;
+            pl->ks = need <= 8 ? 8 : need <= 16 ? 16 : 32;
         } else {
-            pl->wm = 4;
-            pl->mb = 4;
+            pl->stream = 0;
+            if (T <= 64) {
+                pl->wm = 1;
+                pl->mb = (int32_t)std::max<int64_t>(1, (T + 15) / 16);
+            } else if (T <= 128) {
+                pl->wm = 2;
+                pl->mb = 4;
+            } else {
+                pl->wm = 4;
+                pl->mb = 4;
+            }
+            pl->n_tiles = (int32_t)(H / 64);
+            // splits of K so that the base workgroups cover the 256 CUs: a power of two in [1, 8]
+            int32_t sp = 1;
+            while (sp < 8 && (int64_t)pl->n_tiles * sp < 256) sp *= 2;
+            pl->ysplit = sp;
+            pl->n_shrink = (int32_t)std::min<int64_t>(256, std::max<int64_t>(16, 8 * T));
         }
-        pl->n_tiles = (int32_t)(H / 64);
-        // splits of K so that the base workgroups cover the 256 CUs: a power of two in [1, 8]
-        int32_t sp = 1;
-        while (sp < 8 && (int64_t)pl->n_tiles * sp < 256) sp *= 2;
-        pl->ysplit = sp;
-        pl->n_shrink = (int32_t)std::min<int64_t>(256, std::max<int64_t>(16, 8 * T));
     } else if (pl->path == PATH_PREFILL) {
         pl->vsplit = 8;
         pl->n_tiles = 0;
     }
-    pl->rp = (int32_t)((R + 15) / 16 * 16);
     pl->n_counters = 0;   // no kernel uses arrival counters (cross-workgroup sums go through kernel boundaries)
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
@@ -70,10 +88,12 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     pl->off_item_row = take((size_t)pl->n_items_max * 4);
     pl->off_ctrl = take(CTRL_WORDS * 4);
     pl->off_counters = take((size_t)std::max(pl->n_counters, 1) * 4);
-    pl->off_v = take((size_t)pl->vsplit * T * (pl->path == PATH_PREFILL ? pl->rp : R) * 4);
+    const int64_t sv = pl->path == PATH_DECODE && pl->stream ? pl->ysplit : 1;
+    pl->off_v = take(pl->path == PATH_F32 ? (size_t)T * R * 4 : (size_t)pl->vsplit * T * pl->rp * sv * 4);
     pl->off_ypart = take(pl->path == PATH_DECODE ? (size_t)pl->ysplit * T * H * 4 : 0);
     pl->off_sorted_tok = take(pl->path == PATH_DECODE ? (size_t)T * 16 : 0);
     pl->off_v16 = take(pl->path == PATH_PREFILL ? (size_t)T * pl->rp * 2 : 0);
+    pl->off_spages = take(pl->path == PATH_DECODE ? (size_t)T * pl->rp * 4 : 0);
     pl->total = o;
     return true;
 }
@@ -94,6 +114,7 @@ Ws carve(void *base, const Plan &pl) {
     w.ypart = (float *)(b + pl.off_ypart);
     w.sorted_tok = (int32_t *)(b + pl.off_sorted_tok);
     w.v16 = (uint16_t *)(b + pl.off_v16);
+    w.spages = (int32_t *)(b + pl.off_spages);
     return w;
 }
 
