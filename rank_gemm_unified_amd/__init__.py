@@ -26,6 +26,11 @@ STATUS_NAMES = {0: "ok", -1: "einval", -2: "enomem", -3: "enoent", -4: "erank", 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first (python rank_gemm_unified_amd/build.py "
                       "or __graft_entry__.build()); there is no fallback path")
+# torch ships its own HIP runtime under the same soname as /opt/rocm's.  Whichever is loaded first
+# serves the whole process, and a process that loads this library before torch ends up with two
+# halves of different runtimes that see no device.  Load torch's first.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
