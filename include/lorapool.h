@@ -143,8 +143,8 @@ int lora_pool_load_adapter(lora_pool *pool, int32_t adapter_id, int32_t rank, co
  * becomes evictable.  Errors: LORA_ENOENT (not resident), LORA_EINVAL (already idle). */
 int lora_pool_release_adapter(lora_pool *pool, int32_t adapter_id);
 
-/* Reclaim an idle adapter's pages ("When an adapter has no active requests left, its pages can be
- * reclaimed", section "The architecture"): they return to the end of the free list in page-list
+/* Reclaim an idle adapter's pages (section "The architecture": an adapter that no active request
+ * uses may give its pages back): they return to the end of the free list in page-list
  * order, and the adapter's page-table rows are reset to -1 on `stream`.  The caller must not
  * evict an adapter that queued, unfinished projections still read.
  * Errors: LORA_ENOENT, LORA_EBUSY (has users). */

@@ -83,8 +83,8 @@ def gather_page_ids(page_table_slot, ids, ranks, max_rank: int) -> np.ndarray:
     """Pages each token's gather reads, in token order: int64 [T][2*max_rank], -1 where none.
 
     ``page_table_slot[a]`` lists adapter a's pages for one projection: entries 0..r-1 hold the r
-    columns of A, entries r..2r-1 the r rows of B ("each of A and B is just r vectors of length h",
-    section "Unified paging").  Tokens without an adapter (id -1) or on a rank-0 adapter read
+    columns of A, entries r..2r-1 the r rows of B (section "Unified paging": A and B of rank r are r
+    H-vectors each, one page per vector).  Tokens without an adapter (id -1) or on a rank-0 adapter read
     nothing.
     """
     pt = np.asarray(page_table_slot)

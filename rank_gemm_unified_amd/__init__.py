@@ -327,6 +327,9 @@ class Pool:
     def slot_table(self, slot):
         return self.table[slot]
 
+    def stats(self):
+        return lora_pool_stats(self.handle)
+
     def workspace(self, T):
         need = lora_project_workspace_size(self.handle, T)
         if self._ws is None or self._ws.numel() < need:

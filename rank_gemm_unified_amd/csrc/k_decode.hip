@@ -11,7 +11,7 @@
 //   then           k_decode_finish   partial sums in split order + the expand sum_j v_j B_a[j, :]
 //                                    from B rows gathered from their pages + one rounding
 // ("S-LoRA, in depth", section "Merge or keep adapters separate": xW batched over all tokens
-// whatever their adapter, plus two skinny products per adapter; section "Kernels for a batch of
+// whatever their adapter, plus two thin low-rank products per adapter; section "Kernels for a batch of
 // mixed ranks": low-rank work follows tokens and ranks, adapter traffic follows distinct adapters.)
 // Every sum has a fixed order, so results are bitwise reproducible.
 //

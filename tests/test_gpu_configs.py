@@ -1,0 +1,142 @@
+"""GPU parity at full size for the two largest workloads:
+
+* the many-adapter decode batch: H=4096, q/k/v/o of one layer, 2000 adapters plus a rank-0
+  identity adapter, 256 tokens with Zipf(1.0) ids (26 on the identity adapter), a 60 %-KV pool of
+  about 1.37 M pages (11 GB: page offsets beyond 4 GiB);
+* one layer (q/k/v/o) of the 13B-shaped stack: H=5120, 8448 rows (4 prefill requests of 2048 rows
+  and 256 decode rows, Zipf(1.2) ids), 1000 adapters, a pool fragmented by seeded alloc/free
+  churn.  All 40 layers are 40 independent copies of this case; the test builds one.
+
+Every gather index is compared bit for bit; outputs against the fp64 oracle, on every row (many)
+or on all decode rows plus 64 seeded rows of each prefill request (stack)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_gemm_unified_amd as rg
+from gpu_helpers import device_pool, errors, ids_ranks_scale, oracle_y, run, say
+from workloads import build, storage_to_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_REL, BF16_ABS = 1e-2, 5e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _gather_exact(w, pool, slot):
+    d_ids, d_ranks, _ = ids_ranks_scale(w)
+    out = torch.empty((w.T, 2 * w.max_rank), dtype=torch.int32, device="cuda")
+    rg.lora_debug_gather(pool.handle, pool.table[slot], d_ids, d_ranks, w.T, out)
+    want = oracle.gather_page_ids(pool.table[slot].cpu().numpy(), w.ids, w.ranks, w.max_rank)
+    got = out.cpu().numpy()
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, (bad[:10], w.ids[bad[:10]])
+
+
+def _delta_check(w, pool, slot, y, ref, rows=None):
+    """Per-token low-rank delta against the oracle's on the rows given: catches one token's wrong
+    or missing adapter, which the global relative error would dilute.  Rows on no adapter or on a
+    rank-0 adapter must equal the base-only run bit for bit."""
+    rows = np.arange(w.T) if rows is None else rows
+    none = np.full(w.T, -1, np.int32)
+    y0 = run(pool, w, slot, ids=none)
+    torch.cuda.synchronize()
+    base = oracle_y(w, slot, rows=rows, ids=none)
+    sel = torch.as_tensor(rows, device="cuda")
+    d_gpu = storage_to_f64(y[sel]) - storage_to_f64(y0[sel])
+    d_ref = ref - base
+    ids = w.ids[rows]
+    live = np.array([a >= 0 and w.ranks[a] > 0 for a in ids])
+    rel_t = np.linalg.norm(d_gpu[live] - d_ref[live], axis=1) / np.linalg.norm(d_ref[live], axis=1)
+    assert rel_t.max() <= 0.1, (int(rows[live][rel_t.argmax()]), float(rel_t.max()))
+    ident = torch.as_tensor(rows[~live], device="cuda")
+    assert torch.equal(y[ident].view(torch.int16), y0[ident].view(torch.int16))
+
+
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def many():
+    w = build("many", device="cuda")
+    say("case many: H", w.hidden, "T", w.T, "slots", w.n_slots, "pages", w.num_pages)
+    pool = device_pool(w)
+    say("many: pool ready", pool.stats())
+    yield w, pool
+    pool.close()
+    w.drop_cache()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("slot", [0, 1, 2, 3])
+def test_many_adapters_parity(many, slot):
+    w, pool = many
+    say("case many slot", slot)
+    assert w.num_pages * w.hidden * 2 > 2**32          # page offsets need 64 bits
+    _gather_exact(w, pool, slot)
+    y = run(pool, w, slot)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    ref = oracle_y(w, slot)
+    rel, mx = errors(y, ref)
+    say(f"many slot {slot}: relL2={rel:.3e} maxabs={mx:.3e}")
+    assert rel <= BF16_REL and mx <= BF16_ABS
+    _delta_check(w, pool, slot, y, ref)
+
+
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def stack_layer():
+    w = build("stack13b", device="cuda", layers=1)
+    say("case stack13b layer 0: H", w.hidden, "T", w.T, "slots", w.n_slots, "pages", w.num_pages)
+    pool = device_pool(w)
+    say("stack13b: pool ready", pool.stats())
+    w.drop_cache("AB")                 # re-drawn on demand for the rows the oracle checks
+    yield w, pool
+    pool.close()
+    w.drop_cache()
+    torch.cuda.empty_cache()
+
+
+def _stack_rows(w):
+    rng = np.random.default_rng(105)
+    rows = [np.arange(w.T - 256, w.T)]                  # every decode row
+    for start, n in w.segments:                          # 64 seeded rows of each prefill request
+        rows.append(start + np.sort(rng.choice(n, 64, replace=False)))
+    return np.concatenate(rows)
+
+
+def test_stack13b_pool_is_fragmented(stack_layer):
+    """The churned pool scatters each adapter's pages: at least 90 % of consecutive table entries
+    of a row are not neighbouring pages."""
+    w, pool = stack_layer
+    tab = pool.table[0].cpu().numpy()
+    steps = adj = 0
+    for a in range(w.max_adapters):
+        r = int(w.ranks[a])
+        row = tab[a, : 2 * r].astype(np.int64)
+        assert (row >= 0).all()
+        steps += max(2 * r - 1, 0)
+        adj += int(np.sum(np.abs(np.diff(row)) == 1))
+    say(f"stack13b: {adj} of {steps} consecutive entries are neighbouring pages")
+    assert adj <= 0.1 * steps
+
+
+@pytest.mark.parametrize("slot", [0, 3])             # q reads x, o reads its own x_o
+def test_stack13b_layer_parity(stack_layer, slot):
+    w, pool = stack_layer
+    say("case stack13b slot", slot)
+    _gather_exact(w, pool, slot)
+    y = run(pool, w, slot)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    rows = _stack_rows(w)
+    ref = oracle_y(w, slot, rows=rows)
+    rel, mx = errors(y[torch.as_tensor(rows, device="cuda")], ref)
+    say(f"stack13b slot {slot}: {rows.size} rows, relL2={rel:.3e} maxabs={mx:.3e}")
+    assert rel <= BF16_REL and mx <= BF16_ABS
+    _delta_check(w, pool, slot, y, ref, rows=rows)

@@ -234,8 +234,13 @@ def _churn_plan(rng, adapters, ranks, n_slots, kv_layers, rounds=4):
 # the five workloads
 # ---------------------------------------------------------------------------------------
 
-def build(name: str, device: str = "cpu") -> Workload:
+def build(name: str, device: str = "cpu", layers: int | None = None) -> Workload:
+    """One of the five named workloads.  ``layers`` (stack13b only) keeps the first ``layers``
+    of the 40 layers (4 q/k/v/o slots each); everything else -- ids, ranks, pool plan rules --
+    is the same."""
     m = _MASTER[name]
+    if layers is not None and name != "stack13b":
+        raise ValueError("layers applies to stack13b only")
     r_ids, r_ranks, r_pool = _rng(m, _K_IDS), _rng(m, _K_RANKS), _rng(m, _K_POOL)
     if name == "tiny":
         H, dt, n_slots, n_ad, T = 256, "f32", 1, 4, 16
@@ -272,7 +277,10 @@ def build(name: str, device: str = "cpu") -> Workload:
         adapters = list(range(n_ad))
         plan = _interleaved_plan(r_pool, adapters, ranks, n_slots, 0.60, 0.35, kv_layers=32)
     elif name == "stack13b":
-        H, dt, n_slots = 5120, "bf16", 160
+        H, dt = 5120, "bf16"
+        n_slots = 4 * (40 if layers is None else int(layers))
+        if not 1 <= n_slots // 4 <= 40:
+            raise ValueError("layers must be in 1..40")
         n_ad = 1000
         ranks = r_ranks.choice(np.array([8, 16, 32, 64], np.int32), n_ad).astype(np.int32)
         pre = _finite_zipf(r_ids, n_ad, 1.2, 4)
