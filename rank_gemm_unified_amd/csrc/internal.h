@@ -94,8 +94,7 @@ struct Plan {
     int32_t n_counters;     // arrival counters the grouping kernel zeroes
     int32_t rp;             // row stride of v and per-token page lists (max_rank rounded up to 16)
     int32_t stream;         // decode: 1 = streaming kernel (T <= 64), 0 = shrink/base workgroups
-    int32_t ks;             // decode streaming kernel: max K steps of 32 per split
-    int32_t nw;             // decode streaming kernel: W-waves (16 columns each) per workgroup
+    int32_t ks;             // decode streaming kernel: max K steps of 32 per wave (a quarter of a split)
     // byte offsets into the workspace
     size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row,
         off_ctrl, off_counters, off_v, off_ypart, off_sorted_tok, off_v16, off_spages, total;

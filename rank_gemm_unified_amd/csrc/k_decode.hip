@@ -294,208 +294,378 @@ __device__ void dec_publish(DecGroup &g, int err, const int32_t *__restrict__ pt
     if (err) atomicOr(err_word, err);
 }
 
-// ---- decode, T <= 64: streaming kernel ----------------------------------------------------------
-//
-// Grid n_tiles x S workgroups, about one per CU.  Workgroup (tile, split) owns output columns
-// [16 NW tile, 16 NW (tile + 1)) and the K chunk [kb, ke) of split.  A wave's vector-memory loads
-// retire in issue order, so a wave that waits on a dependent chain (ids -> ranks -> page table ->
-// pages) must not also have the W stream queued in front of it.  Hence two kinds of wave:
-//  * NW W-waves: each issues its whole W slice (16 output columns x the K chunk) at once, stages its
-//    share of x's K chunk in LDS (the MFMA A operand of every wave), and writes x W partials;
-//  * one meta-wave: reads the ids and ranks, groups the <= 64 tokens by adapter with wave ballots,
-//    takes this tile's blocks of 16 pages from the batch's A-page list (adapters in order of first
-//    token, pages 0..r-1 each), computes s x A for them over the same K chunk as extra MFMA columns
-//    (the shrink), and validates and publishes its share of the adapters' page-table rows.
-// Outputs: float32 partials of x W and of s x A, one per split; k_decode_finish adds them in split
-// order.  The workgroup has a single barrier (x staged).
-template <int MB, int KS, int NW>   // T <= 16 MB; K chunk <= 32 KS; NW W-waves of 16 columns
-__global__ __launch_bounds__((NW + 1) * 64, 1) void k_decode_stream(
+// ---- wave-level grouping helpers for the T <= 64 kernel (lane = token) --------------------------------
+// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 inside each row of 16 lanes (DPP;
+// lanes shifted in from outside the row read 0), then the row totals carried across rows.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// Lanes holding the same key >= 0 (itself included), through a wave-private open-addressing table of
+// 128 slots in LDS: each lane claims its key's slot by compare-and-swap, then sets its bit in the
+// slot's mask.  At most 64 keys, so a free slot always exists.  Lanes with key < 0 get 0.
+struct GroupTab {
+    int32_t key[128];
+    unsigned long long mask[128];
+};
+__device__ __forceinline__ uint64_t same_key_lanes(int32_t key, int lane, GroupTab *g) {
+    g->key[lane] = -1;
+    g->key[lane + 64] = -1;
+    g->mask[lane] = 0ull;
+    g->mask[lane + 64] = 0ull;
+    uint64_t m = 0;
+    uint32_t h = ((uint32_t)key * 0x9E3779B1u) >> 25;
+    if (key >= 0) {
+        for (int probe = 0; probe < 128; ++probe) {
+            const int32_t old = atomicCAS(&g->key[h], -1, key);
+            if (old == -1 || old == key) break;
+            h = (h + 1) & 127;
+        }
+        atomicOr(&g->mask[h], 1ull << lane);
+    }
+    if (key >= 0) m = g->mask[h];   // LDS operations of one wave complete in order
+    return m;
+}
+
+// ---- decode, T <= 64: one streaming pass over W, x and the batch's A pages ------------------------
+// Grid: n_tiles column tiles of 64 x S splits of K, 256 threads (four waves, one per SIMD).  Wave w
+// owns the w-th quarter of its split's K range for all 64 columns of the tile:
+//  * x: its T x (K quarter) slice is read with row-contiguous loads, written to a private LDS
+//    region and read back in the MFMA operand layout.  A load that covers 16 rows x 64 bytes (the
+//    operand layout) costs the CU's load path about twice what a row-contiguous one does;
+//  * W: 16 x 32 operand tiles, DS steps in flight.  A shallow queue streams W as fast as a deep
+//    one and keeps the latency of the metadata loads queued behind it near one microsecond;
+//  * the shrink: block `tile` of the batch's A-page list (adapters in order of first token, pages
+//    0..r-1 each, 16 pages a block) is 16 extra MFMA columns over the same K quarter.  Each wave
+//    works the block out itself (ids -> ranks -> grouping -> page table) at fixed steps of its W
+//    loop, so the dependent loads ride between W steps and no wave waits for another.
+// The four K-quarter partials are summed in LDS in wave order.  Outputs: float32 partials of x W
+// (ypart[split]) and of s x A (vpart[..][split]), and, from the workgroups that own a segment, its
+// checked page-table row as sorted-token records and B page ids for k_decode_finish.
+template <int MB, int KQ>
+struct StreamShape {
+    static constexpr int TP = MB * 16;                        // padded token rows
+    static constexpr int P = KQ * 4;                          // 16-byte x pieces per row of a K quarter
+    static constexpr int RS = 68, PS = 20;                    // row strides (floats) of the sum buffers
+    // per wave: its x slice, later overwritten by its x W partial and its block-0 page partial
+    static constexpr size_t XSLICE = (size_t)TP * P * 16, PART = (size_t)TP * (RS + PS) * 4;
+    static constexpr size_t REGION = XSLICE > PART ? XSLICE : PART;
+    static constexpr size_t PBYTES = (size_t)4 * TP * PS * 4;                 // further page blocks' partials
+    static constexpr size_t GBYTES = (size_t)4 * sizeof(GroupTab);            // grouping tables
+    static constexpr size_t LDS = 4 * REGION + PBYTES + GBYTES;
+};
+
+template <int MB, int KQ>
+__global__ __launch_bounds__(256, 1) void k_decode_stream(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
     int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
     float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
     int *__restrict__ err_word) {
-    constexpr int TP = MB * 16;
-    constexpr int XS = KS * 32;        // LDS row of x (elements), swizzled in 16-byte pieces
+    using SH = StreamShape<MB, KQ>;
+    constexpr int TP = SH::TP, P = SH::P, RS = SH::RS, PS = SH::PS;
+    constexpr int SWZ = P < 16 ? P - 1 : 15;          // piece c of row r sits in slot c ^ (r & SWZ)
+    constexpr int DS = KQ < 2 ? KQ : 2;               // W steps in flight ahead of the MFMA step
+    constexpr int S1 = KQ > 1 ? 1 : 0;                // step that consumes the ranks (grouping)
+    constexpr int S2 = KQ > 3 ? 3 : KQ - 1;           // step that consumes the page-table entries
+    constexpr int XI = TP * P / 64;                   // row-contiguous x loads per wave (= MB * KQ)
     extern __shared__ __align__(16) char lds_raw[];
-    uint16_t *xs = reinterpret_cast<uint16_t *>(lds_raw);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int tile = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
-    const int ksteps = H / 32;
-    const int kb = (int)((int64_t)ksteps * split / S) * 32, ke = (int)((int64_t)ksteps * (split + 1) / S) * 32;
-    const int nst = (ke - kb) / 32;
-    const int lrow = lane & 15, lk = (lane >> 4) * 8;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lrow = lane & 15, lq = lane >> 4;
     const u32x4_t zero = u32x4_t{0, 0, 0, 0};
 
-    if (wave < NW) {
-        // ------------------------------------------------------------------ W-wave
-        // x's K chunk goes straight to LDS (no registers); 16-byte piece c of row `row` lands in
-        // slot c ^ (row & 15), so the 16 rows an MFMA operand read touches hit distinct banks.
-        // Rows >= T and pieces past the chunk hold copies of valid data: their results are never
-        // stored and their K steps are never read.
-        constexpr int XI = TP * KS * 4 / 64;   // wave-wide direct-to-LDS loads
-        for (int i = wave; i < XI; i += NW) {
-            const int L = i * 64 + lane;
-            const int row = L / (KS * 4), c = (L % (KS * 4)) ^ (row & 15);
-            const bool live = row < T && c * 8 < ke - kb;
-            const uint16_t *src = x + (int64_t)(live ? row : 0) * H + kb + (live ? c * 8 : 0);
-            __builtin_amdgcn_global_load_lds((glob_void *)src, (lds_void *)(xs + i * 64 * 8), 16, 0, 0);
+    // XCD-aware order: consecutive workgroups go to the 8 XCDs in turn, so the splits are spread
+    // over XCDs and each XCD's L2 holds one or two K chunks of x
+    int tile, split;
+    if ((gridDim.x & 7) == 0 && 8 % S == 0) {
+        const int per = 8 / S;
+        split = (blockIdx.x & 7) / per;
+        tile = (blockIdx.x >> 3) * per + (blockIdx.x & 7) % per;
+    } else {
+        tile = blockIdx.x % n_tiles;
+        split = blockIdx.x / n_tiles;
+    }
+    const int ksteps = H / 32, G = 4 * S, gq = split * 4 + wave;
+    const int s0 = (int)((int64_t)ksteps * gq / G);
+    const int nst = (int)((int64_t)ksteps * (gq + 1) / G) - s0;   // K steps of this wave, <= KQ
+    const int kq = s0 * 32;
+    const int n0 = tile * 64;
+    char *region = lds_raw + (size_t)wave * SH::REGION;
+    uint16_t *xs = reinterpret_cast<uint16_t *>(region);
+    float *pred = reinterpret_cast<float *>(lds_raw + 4 * SH::REGION);
+    GroupTab *gtab = reinterpret_cast<GroupTab *>(lds_raw + 4 * SH::REGION + SH::PBYTES) + wave;
+
+    // ---- issue the ids, then x (row-contiguous).  Every CU of an XCD reads the same x chunk, so each
+    // workgroup starts at its own piece (rotation by tile) and the first misses spread over many lines
+    // instead of queueing on one.  Rows >= T and pieces past the wave's K steps load valid stand-in
+    // data: the MFMA rows and K steps they feed are never stored or never run.
+    const int32_t a_raw = ids[min(lane, T - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t xv[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int L = ((i + tile) % XI) * 64 + lane, row = L / P, c = (L % P) ^ (row & SWZ);
+        const bool live = row < T && c < nst * 4;
+        xv[i] = load16(x + (int64_t)(live ? row : 0) * H + kq + (live ? c * 8 : 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- ids -> key, then the ranks
+    int err = 0;
+    const int32_t a_tok = lane < T ? a_raw : -1;
+    const int32_t rr = ranks[a_tok >= 0 && a_tok < max_adapters ? a_tok : 0];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- x slice to LDS (the wave's own region: no barrier), then the first DS steps of W.  W waits
+    // for x: issued together, the W misses delay x, and nothing can use W before x is in LDS.
+#pragma unroll
+    for (int i = 0; i < XI; ++i) store16(xs + (size_t)(((i + tile) % XI) * 64 + lane) * 8, xv[i]);
+    const uint16_t *wr = W + (int64_t)(n0 + lrow) * H + kq + lq * 8;
+    const int slast = max(nst - 1, 0);
+    u32x4_t wv[KQ][4];
+#pragma unroll
+    for (int st = 0; st < DS; ++st)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) wv[st][nb] = load16(wr + (int64_t)(16 * nb) * H + 32 * min(st, slast));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // metadata produced at steps S1 / S2
+    int32_t key = -1, seg_a = 0, seg_r = 0, seg_n = 0, poff = 0, toff = 0, my_pos = 0, nseg = 0, npages = 0;
+    int32_t pa = 0, pj = 0, pid = 0, ent[2] = {-1, -1};
+    int64_t pidx = 0;
+    float sc = 0.f;
+    bool plive = false;
+    const int32_t *ptc = pt;   // page-table entry of this lane's page (lane % 16)
+    u32x4_t pv[KQ];
+    f32x4_t acc[MB][4];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto xop = [&](int st, int m) {   // MFMA A operand: rows m*16 + lrow, K step st
+        const int row = m * 16 + lrow;
+        return load16(xs + (size_t)(row * P + ((st * 4 + lq) ^ (row & SWZ))) * 8);
+    };
+
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < KQ; ++st) {
+        if (st + DS < KQ) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                wv[st + DS][nb] = load16(wr + (int64_t)(16 * nb) * H + 32 * min(st + DS, slast));
         }
-        const int wn = tile * NW * 16 + wave * 16 + lrow;   // output column this lane loads
-        const bool wlive = wn < H;
-        const uint16_t *wr = W + (int64_t)(wlive ? wn : 0) * H + kb + lk;
-        u32x4_t wreg[KS];
-#pragma unroll
-        for (int st = 0; st < KS; ++st) wreg[st] = load16(wr + 32 * min(st, max(nst - 1, 0)));
-        __builtin_amdgcn_sched_barrier(0);   // keep every W load ahead of the barrier
-        // vector-memory ops retire in order: waiting until only the KS W loads are outstanding
-        // means this wave's x pieces are in LDS.  A plain barrier follows (a __syncthreads
-        // fence would wait for the W loads too).
-        __builtin_amdgcn_s_waitcnt((KS & 15) | ((KS >> 4) << 14) | 0xF70);
-        workgroup_barrier();
-        f32x4_t acc[MB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {   // branch-free: steps past the chunk multiply by zero
-            const u32x4_t wb = st < nst ? wreg[st] : zero;
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const int row = m * 16 + lrow;
-                const u32x4_t xa = load16(xs + row * XS + (((st * 4 + (lk >> 3)) ^ (row & 15)) << 3));
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
-                                                                 __builtin_bit_cast(bf16x8_t, wb), acc[m], 0, 0, 0);
+        if (st == S1) {
+            // validate the ids and ranks; key = adapter of a token with a nonzero rank, else -1
+            int32_t r = 0, rk = rr;
+            asm volatile("" : "+v"(rk));   // keep the first use of the ranks at this step
+            if (a_tok != -1) {
+                if (a_tok < -1 || a_tok >= max_adapters) err |= DEV_ERR_ID;
+                else if (rk < 0 || rk > max_rank) err |= DEV_ERR_RANK;
+                else if (rk > 0) { key = a_tok; r = rk; }
             }
-            __builtin_amdgcn_sched_barrier(0);   // keep each K step's LDS reads next to its MFMAs
+            // group: the lanes sharing this lane's key, its first lane, this lane's rank among them
+            const uint64_t same = same_key_lanes(key, lane, gtab);
+            const int first = key >= 0 ? __ffsll((unsigned long long)same) - 1 : lane;
+            const int rank_in = __popcll(same & ((1ull << lane) - 1ull)), cnt = __popcll(same);
+            const uint64_t first_mask = __ballot(key >= 0 && first == lane);
+            nseg = __popcll(first_mask);
+            const int my_seg = key >= 0 ? __popcll(first_mask & ((1ull << first) - 1ull)) : 0;
+            // lane s < nseg describes segment s (segments in order of their first token): the first
+            // lanes write their segment's adapter, rank and token count to the table, lane s reads
+            int32_t *segtab = gtab->key;   // the claimed slots are no longer needed
+            __builtin_amdgcn_wave_barrier();
+            if (key >= 0 && first == lane) {
+                segtab[my_seg] = key;
+                segtab[64 + my_seg] = r;
+                reinterpret_cast<int32_t *>(gtab->mask)[my_seg] = cnt;
+            }
+            __builtin_amdgcn_wave_barrier();
+            const bool segl = lane < nseg;
+            seg_a = segl ? segtab[lane] : 0;
+            seg_r = segl ? segtab[64 + lane] : 0;
+            seg_n = segl ? reinterpret_cast<int32_t *>(gtab->mask)[lane] : 0;
+            poff = wave_incl_scan(seg_r, lane);
+            toff = wave_incl_scan(seg_n, lane);
+            npages = __builtin_amdgcn_readlane(poff, 63);
+            const int32_t nvalid = __builtin_amdgcn_readlane(toff, 63);
+            poff -= seg_r;   // exclusive
+            toff -= seg_n;
+            const int idrank = __popcll(__ballot(lane < T && key < 0) & ((1ull << lane) - 1ull));
+            const int32_t seg_first_pos = __shfl(toff, my_seg, 64);
+            my_pos = key >= 0 ? seg_first_pos + rank_in : nvalid + idrank;
+            // page of this lane's column (lane % 16) in the workgroup's first block, and its segment:
+            // one ballot per column counts the segments that start at or before the page
+            const int p = tile * 16 + lrow;
+            plive = p < npages;
+            int sg = 0;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const uint64_t mk = __ballot(segl && poff <= tile * 16 + c);
+                if (lrow == c) sg = max(__popcll(mk) - 1, 0);
+            }
+            pa = __shfl(seg_a, sg, 64);
+            pj = p - __shfl(poff, sg, 64);
+            pidx = plive ? (int64_t)pa * stride + pj : 0;
+            ptc = pt + pidx;
+            // the page-table row of the segment this workgroup publishes first
+            const int ps = (int)blockIdx.x < nseg ? (int)blockIdx.x : 0;
+            int32_t a_pub = __shfl(seg_a, ps, 64), r_pub = __shfl(seg_r, ps, 64);
+            if ((int)blockIdx.x >= nseg) a_pub = r_pub = 0;   // nothing to publish: read entry 0
+            const int lim = min(2 * r_pub + 1, stride);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) ent[u] = pt[(int64_t)a_pub * stride + min(lane + 64 * u, lim - 1)];
+            pid = *ptc;
+            sc = scale[plive ? pa : 0];
         }
-        // accumulator layout: lane holds rows 4*(lane/16)+i of column lane%16
-        if (wlive) {
+        if (st == S2) {
+            // this block's pages: lane loads page (lane % 16), K rows kq + 32 s + 8 (lane / 16) + [0, 8)
+            int32_t pg = pid;
+            const bool pok = plive && pg >= 0 && (int64_t)pg < num_pages;   // bad rows are reported by the publisher
+            const uint16_t *pr = pok ? pages + (int64_t)pg * H + kq + lq * 8 : x + lq * 8;
+#pragma unroll
+            for (int s2 = 0; s2 < KQ; ++s2) pv[s2] = load16(pr + 32 * min(s2, slast));
+            plive = pok;
+        }
+        // steps past the wave's K range multiply by zero (branch-free: a branch here would let the
+        // compiler sink the W loads into it, after the point they are meant to be issued)
+        const bool sl = st < nst;
+        u32x4_t xa[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) xa[m] = xop(st, m);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const u32x4_t wb = sl ? wv[st][nb] : zero;
 #pragma unroll
             for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = m * 16 + (lane >> 4) * 4 + i;
-                    if (t < T) ypart[((int64_t)split * T + t) * H + wn] = acc[m][i];
-                }
+                acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[m]),
+                                                                     __builtin_bit_cast(bf16x8_t, wb), acc[m][nb], 0, 0, 0);
         }
-        return;
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---------------------------------------------------------------------- meta-wave (lane = token)
-    int err = 0;
-    int32_t key = -1, r = 0;
-    {
-        const int32_t a = lane < T ? ids[lane] : -1;
-        const int32_t rr = ranks[a >= 0 && a < max_adapters ? a : 0];
-        if (a != -1) {
-            if (a < -1 || a >= max_adapters) err |= DEV_ERR_ID;
-            else if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
-            else if (rr > 0) { key = a; r = rr; }
-        }
-    }
-    // group by key with ballots: rank within key, count, first lane; segments in first-lane order
-    int rank_in = 0, cnt = 0, first = lane;
-    {
-        uint64_t remaining = __ballot(key >= 0);
-        while (remaining) {
-            const int leader = __ffsll((unsigned long long)remaining) - 1;
-            const int32_t lkey = __shfl(key, leader, 64);
-            const uint64_t m = __ballot(key == lkey);
-            if (key == lkey) {
-                rank_in = __popcll(m & ((1ull << lane) - 1ull));
-                cnt = __popcll(m);
-                first = leader;
-            }
-            remaining &= ~m;
-        }
-    }
-    const uint64_t first_mask = __ballot(key >= 0 && rank_in == 0);
-    const int nseg = __popcll(first_mask);
-    const int my_seg = key >= 0 ? __popcll(first_mask & ((1ull << first) - 1ull)) : -1;
-    // lane s < nseg describes segment s: the s-th first lane
-    int32_t seg_lane = 0;
-    {
-        uint64_t fm = first_mask;
-        for (int s = 0; s < nseg; ++s) {
-            const int l = __ffsll((unsigned long long)fm) - 1;
-            if (lane == s) seg_lane = l;
-            fm &= fm - 1;
-        }
-    }
-    const int32_t seg_a = __shfl(key, seg_lane, 64), seg_r = __shfl(r, seg_lane, 64), seg_n = __shfl(cnt, seg_lane, 64);
-    const bool segl = lane < nseg;
-    // prefix sums over segments: pages (r) and tokens (n)
-    int32_t poff = segl ? seg_r : 0, toff = segl ? seg_n : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t y1 = __shfl_up(poff, off, 64), y2 = __shfl_up(toff, off, 64);
-        if (lane >= off) { poff += y1; toff += y2; }
-    }
-    const int32_t npages = __shfl(poff, 63, 64), nvalid = __shfl(toff, 63, 64);
-    poff -= segl ? seg_r : 0;   // exclusive
-    toff -= segl ? seg_n : 0;
-    // sorted position of this lane's token: grouped tokens first (segments in order), then the rest
-    const int idrank = __popcll(__ballot(lane < T && key < 0) & ((1ull << lane) - 1ull));
-    const int32_t seg_first_pos = __shfl(toff, max(my_seg, 0), 64);   // every lane shuffles
-    const int my_pos = key >= 0 ? seg_first_pos + rank_in : nvalid + idrank;
-
-    // this tile's page blocks: pages [16 b, 16 b + 16) of the list, b = tile + k * n_tiles
-    f32x4_t pacc[MB];
-    for (int b = tile; b * 16 < npages; b += n_tiles) {
-        const int p = min(b * 16 + lrow, npages - 1);
-        const bool plive = b * 16 + lrow < npages;
-        int sg = 0;   // segment of page p: last s with poff[s] <= p
-        for (int s = 1; s < nseg; ++s) sg += __shfl(poff, s, 64) <= p ? 1 : 0;
-        const int32_t pa = __shfl(seg_a, sg, 64), pj = p - __shfl(poff, sg, 64);
-        int32_t pid = pt[(int64_t)pa * stride + pj];
-        if (pid < 0 || (int64_t)pid >= num_pages) pid = 0;   // the row is reported below; token dropped
-        const uint16_t *ap = pages + (int64_t)pid * H + kb + lk;
-        u32x4_t preg[KS];
-#pragma unroll
-        for (int st = 0; st < KS; ++st) preg[st] = load16(ap + 32 * min(st, max(nst - 1, 0)));
-        if (b == tile) workgroup_barrier();   // x staged (the workgroup's only barrier)
+    // ---- page blocks: MFMA over the K quarter, scaled by s; the four quarters are summed in wave order
+    auto page_mfma = [&](const u32x4_t *pvb, float sc_col, f32x4_t *pacc) {
 #pragma unroll
         for (int m = 0; m < MB; ++m) pacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-            const u32x4_t bb = plive && st < nst ? preg[st] : zero;
+        for (int s2 = 0; s2 < KQ; ++s2) {   // columns of dead pages hold stand-in data and are never stored
+            const u32x4_t bb = s2 < nst ? pvb[s2] : zero;
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const int row = m * 16 + lrow;
-                const u32x4_t xa = load16(xs + row * XS + (((st * 4 + (lk >> 3)) ^ (row & 15)) << 3));
-                pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+            for (int m = 0; m < MB; ++m)
+                pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xop(s2, m)),
                                                                   __builtin_bit_cast(bf16x8_t, bb), pacc[m], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        const float sc = scale[pa];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) pacc[m] *= sc_col;
+    };
+    // thread -> column lrow (its own lane's page), rows lane/16 + 4 (wave + 4 u); the partial of wave
+    // w, row t sits at part(w) + t * pstride
+    auto page_store = [&](const float *part0, size_t wstride, int pstride, bool live_col, int32_t a_col,
+                          int32_t j_col) {
+        float v[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+            const int t = lq + 4 * (wave + 4 * u);
+            const float *q = part0 + t * pstride + lrow;
+            v[u] = ((q[0] + q[wstride]) + q[2 * wstride]) + q[3 * wstride];
+        }
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+            const int t = lq + 4 * (wave + 4 * u);
+            const int32_t key_t = __shfl(key, t & 63, 64);
+            if (live_col && t < T && key_t == a_col) vpart[((int64_t)t * RP + j_col) * S + split] = v[u];
+        }
+    };
+    f32x4_t pacc0[MB];
+    page_mfma(pv, sc, pacc0);
+    // further blocks (more pages than 16 n_tiles: rare) while x is still in LDS, through their own buffer
+    for (int b = tile + n_tiles; b * 16 < npages; b += n_tiles) {
+        const int p = b * 16 + lrow;
+        bool live = p < npages;
+        int sg = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const uint64_t mk = __ballot(lane < nseg && poff <= b * 16 + c);
+            if (lrow == c) sg = max(__popcll(mk) - 1, 0);
+        }
+        const int32_t a2 = __shfl(seg_a, sg, 64), j2 = p - __shfl(poff, sg, 64);
+        const int32_t pg = pt[live ? (int64_t)a2 * stride + j2 : 0];
+        const float sc2 = scale[live ? a2 : 0];
+        live = live && pg >= 0 && (int64_t)pg < num_pages;
+        const uint16_t *pr = live ? pages + (int64_t)pg * H + kq + lq * 8 : x + lq * 8;
+        u32x4_t pv2[KQ];
+#pragma unroll
+        for (int s2 = 0; s2 < KQ; ++s2) pv2[s2] = load16(pr + 32 * min(s2, slast));
+        f32x4_t pacc[MB];
+        page_mfma(pv2, sc2, pacc);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = m * 16 + (lane >> 4) * 4 + i;
-                const int32_t key_t = __shfl(key, t & 63, 64);   // outside any condition: all lanes active
-                if (plive && t < T && key_t == pa) vpart[((int64_t)t * RP + pj) * S + split] = sc * pacc[m][i];
-            }
+            for (int i = 0; i < 4; ++i) pred[((size_t)wave * TP + m * 16 + lq * 4 + i) * PS + lrow] = pacc[m][i];
+        __syncthreads();
+        page_store(pred, (size_t)TP * PS, PS, live, a2, j2);
+        __syncthreads();
     }
-    if (tile * 16 >= npages) workgroup_barrier();   // no page block: still meet the barrier once
 
-    // publish: segments s = blockIdx.x + k * gridDim.x -- check the page-table row, then write the
-    // segment's sorted-token records and B page ids; workgroup 0 also writes the ungrouped tokens
+    // ---- the wave's x slice is no longer read: its region takes the wave's x W partial [TP][RS] and
+    // block-0 page partial [TP][PS]; one barrier, then every wave sums its share in wave order
+    {
+        float *mine = reinterpret_cast<float *>(region);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mine[(m * 16 + lq * 4 + i) * RS + nb * 16 + lrow] = acc[m][nb][i];
+        float *pm = mine + TP * RS;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pm[(m * 16 + lq * 4 + i) * PS + lrow] = pacc0[m][i];
+    }
+    __syncthreads();
+    {
+        const float *red = reinterpret_cast<const float *>(lds_raw);
+        constexpr size_t WS = SH::REGION / 4;   // floats between the waves' regions
+        float v[MB * 4];
+#pragma unroll
+        for (int u = 0; u < MB * 4; ++u) {      // rows t = wave + 4 u, column = lane
+            const float *q = red + (size_t)(wave + 4 * u) * RS + lane;
+            v[u] = ((q[0] + q[WS]) + q[2 * WS]) + q[3 * WS];
+        }
+#pragma unroll
+        for (int u = 0; u < MB * 4; ++u) {
+            const int t = wave + 4 * u;
+            if (t < T) ypart[((int64_t)split * T + t) * H + n0 + lane] = v[u];
+        }
+        page_store(red + TP * RS, WS, PS, plive, pa, pj);
+    }
+
+    // ---- publish (wave 0): segments s = blockIdx.x + k gridDim.x -- check the page-table row, then
+    // write the segment's sorted-token records and B page ids; workgroup 0 also writes the
+    // ungrouped tokens
+    if (wave != 0) return;
     for (int s = blockIdx.x; s < nseg; s += gridDim.x) {
         const int32_t a = __shfl(seg_a, s, 64), rs = __shfl(seg_r, s, 64);
         const int32_t q0 = __shfl(toff, s, 64), qn = __shfl(seg_n, s, 64);
         const int lim = min(2 * rs + 1, stride);
-        int32_t ent[3];
+        if (s != (int)blockIdx.x) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) ent[u] = pt[(int64_t)a * stride + min(lane + 64 * u, lim - 1)];
+        }
         int bad = 0;
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int j = lane + 64 * u;
-            ent[u] = pt[(int64_t)a * stride + min(j, lim - 1)];
-        }
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const int j = lane + 64 * u;
             if (j >= lim) continue;
             if (j < 2 * rs) {
@@ -507,9 +677,8 @@ __global__ __launch_bounds__((NW + 1) * 64, 1) void k_decode_stream(
         }
         for (int off = 32; off > 0; off >>= 1) bad |= __shfl_xor(bad, off, 64);
         err |= bad;
-        // B page ids to every sorted position of the segment
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const int j = lane + 64 * u;
             if (j >= rs && j < 2 * rs)
                 for (int q = q0; q < q0 + qn; ++q) spages[(int64_t)q * RP + (j - rs)] = ent[u];
@@ -654,24 +823,27 @@ __global__ __launch_bounds__(256, 2) void k_decode_main(
 }
 
 // ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
-// Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Round trip 1 reads, by
-// sorted position only, the token record and its B page ids; round trip 2 reads the B rows' column
-// slices, the v partials (summed in split order into LDS) and the x W partials.  Thread -> (token,
-// 8 columns, quarter of j: j in [16 q, 16 q + 16)); quarters meet by lane shuffles.
+// Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Thread -> (token i of the
+// group, 8 columns c, quarter q of j: j in [16 q, 16 q + 16)).  Two dependent round trips:
+//  1. by sorted position only: the token record and this quarter's B page ids;
+//  2. all at once: the quarter's 16 B-row slices, the x W partials of splits q, q + 4 and the v
+//     partials of two j's (summed in split order into LDS).
+// The four quarter threads of a token then add their x W partials and expand terms by two lane
+// shuffles (a fixed order), and one of them rounds and stores.
 template <int SY, int SV>
 __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ sorted_tok,
                                                        const int32_t *__restrict__ spages,
                                                        const float *__restrict__ ypart, const float *__restrict__ vpart,
                                                        int32_t RP, const uint16_t *__restrict__ pages, int32_t H,
                                                        int32_t T, uint16_t *__restrict__ y) {
+    constexpr int SQ = (SY + 3) / 4;   // x W splits per quarter thread
     __shared__ float s_v[8][64];
     const int n0 = blockIdx.x * 64;
     const int i = threadIdx.x >> 5, c = ((threadIdx.x >> 2) & 7) * 8, q = threadIdx.x & 3;
     const int sp = min((int)blockIdx.y * 8 + i, T - 1);
     const bool live_tok = (int)blockIdx.y * 8 + i < T;
+    // ---- round trip 1
     const int4 st = sorted_tok[sp];
-    const int t = st.x, a = live_tok ? st.y : -1, r = st.z;
-    const bool has = a >= 0;
     int32_t pid[16];
     {
         const int4 *pr = reinterpret_cast<const int4 *>(spages + (int64_t)sp * RP + 16 * min(q, RP / 16 - 1));
@@ -684,50 +856,67 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
             pid[4 * u + 3] = v4.w;
         }
     }
-    // v[t][j] for j = 2 * (thread within token) + {0, 1}, summed over the SV partials in order
-    {
-        const int jj = (threadIdx.x & 31) * 2;
-        float v0 = 0.f, v1 = 0.f;
-        if (has && jj < RP) {
-            const float *src = vpart + ((int64_t)t * RP + jj) * SV;
-            float pv[2 * SV];
-#pragma unroll
-            for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
-#pragma unroll
-            for (int u = 0; u < SV; ++u) {
-                v0 += pv[u];
-                v1 += pv[SV + u];
-            }
-        }
-        s_v[i][jj] = jj < r ? v0 : 0.f;
-        s_v[i][jj + 1] = jj + 1 < r ? v1 : 0.f;
-    }
-    f32x4_t part[SY][2];
-    if (q == 0) {   // one lane of each quad needs the x W partials
-#pragma unroll
-        for (int s = 0; s < SY; ++s) {
-            const float *src = ypart + ((int64_t)s * T + t) * H + n0 + c;
-            part[s][0] = *reinterpret_cast<const f32x4_t *>(src);
-            part[s][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
-        }
-    }
+    const int t = st.x, a = live_tok ? st.y : -1;
+    const bool has = a >= 0;
+    const int r = has ? st.z : 0;
     const int j0 = 16 * q;
     const bool qlive = has && j0 < r;
+    // ---- round trip 2 (every load unconditional, stand-in addresses for dead entries)
     u32x4_t bv[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int32_t pg = qlive && j0 + u < r ? pid[u] : pid[0];
         bv[u] = load16(pages + (int64_t)(qlive ? pg : 0) * H + n0 + c);
     }
+    f32x4_t part[SQ][2];
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const float *src = ypart + ((int64_t)min(q + 4 * k, SY - 1) * T + t) * H + n0 + c;
+        part[k][0] = *reinterpret_cast<const f32x4_t *>(src);
+        part[k][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
+    }
+    const int jj = (threadIdx.x & 31) * 2;   // this thread's two j's of v
+    float pv[2 * SV];
+    {
+        const float *src = vpart + ((int64_t)t * RP + min(jj, RP - 2)) * SV;
+#pragma unroll
+        for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
+    }
+    // ---- v[t][j] summed over the splits in order; entries past the rank (never written) are dropped
+    {
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < SV; ++u) {
+            v0 += pv[u];
+            v1 += pv[SV + u];
+        }
+        s_v[i][jj] = jj < r ? v0 : 0.f;
+        s_v[i][jj + 1] = jj + 1 < r ? v1 : 0.f;
+    }
     __syncthreads();
+    // ---- this thread's x W splits + its quarter of the expand.  Rows past the token's rank load a
+    // stand-in row and are zeroed before use: the page they read (page 0, or the token's first B page)
+    // may hold any bits, NaN included, and 0 * NaN is NaN.
+    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        if (q + 4 * k < SY) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[e] += part[k][0][e];
+                o[e + 4] += part[k][1][e];
+            }
+        }
+    }
+#pragma unroll
     for (int u = 0; u < 16; ++u) {
+        const bool lu = qlive && j0 + u < r;
         float bf[8];
-        unpack_bf16x8(bv[u], bf);
-        const float w = (qlive && j0 + u < r) ? s_v[i][j0 + u] : 0.f;
+        unpack_bf16x8(lu ? bv[u] : zero, bf);
+        const float w = lu ? s_v[i][j0 + u] : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = fmaf(w, bf[e], o[e]);
     }
@@ -736,21 +925,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
         o[e] += __shfl_xor(o[e], 1, 64);
         o[e] += __shfl_xor(o[e], 2, 64);
     }
-    if (q == 0 && live_tok) {
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int s = 0; s < SY; ++s)   // base partials in split order, then the low-rank sum
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[e] += part[s][0][e];
-                acc[e + 4] += part[s][1][e];
-            }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += o[e];
-        store16(y + (int64_t)t * H + n0 + c, pack_bf16x8(acc));
-    }
+    if (q == 0 && live_tok) store16(y + (int64_t)t * H + n0 + c, pack_bf16x8(o));
 }
 
 // ---- float32 pools: grouping kernel + gathered shrink + plain VALU kernel ---------------------------
@@ -812,19 +987,20 @@ __global__ __launch_bounds__(256) void k_project_f32(const float *__restrict__ x
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------
-template <int MB, int KS, int NW>
+template <int MB, int KQ>
 static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
                                 const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
                                 hipStream_t s) {
-    const size_t lds = (size_t)MB * 16 * KS * 32 * 2;
+    constexpr size_t lds = StreamShape<MB, KQ>::LDS;
+    static_assert(lds <= 160 * 1024, "stream kernel LDS");
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_decode_stream<MB, KS, NW>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_decode_stream<MB, KQ>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_decode_stream<MB, KS, NW>), dim3(plan.n_tiles * plan.ysplit), dim3((NW + 1) * 64), lds, s,
+    hipLaunchKernelGGL((k_decode_stream<MB, KQ>), dim3(plan.n_tiles * plan.ysplit), dim3(256), lds, s,
                        (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)p->pages, p->num_pages, pt,
                        2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden,
                        plan.ysplit, plan.n_tiles, plan.rp, ws.ypart, ws.v, (int4 *)ws.sorted_tok, ws.spages, p->dev_err);
@@ -870,12 +1046,12 @@ hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, con
                          hipStream_t s, hipEvent_t mid) {
     hipError_t e;
     if (plan.stream) {
-        switch (plan.nw * 4096 + plan.mb * 64 + plan.ks) {
-#define LP_CASE(M, K, N) case N * 4096 + M * 64 + K: e = launch_stream<M, K, N>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            LP_CASE(1, 8, 4) LP_CASE(1, 16, 4) LP_CASE(1, 32, 4) LP_CASE(1, 8, 8) LP_CASE(1, 16, 8) LP_CASE(1, 32, 8)
-            LP_CASE(2, 8, 4) LP_CASE(2, 16, 4) LP_CASE(2, 32, 4) LP_CASE(2, 8, 8) LP_CASE(2, 16, 8) LP_CASE(2, 32, 8)
-            LP_CASE(3, 8, 4) LP_CASE(3, 16, 4) LP_CASE(3, 32, 4) LP_CASE(3, 8, 8) LP_CASE(3, 16, 8) LP_CASE(3, 32, 8)
-            LP_CASE(4, 8, 4) LP_CASE(4, 16, 4) LP_CASE(4, 32, 4) LP_CASE(4, 8, 8) LP_CASE(4, 16, 8) LP_CASE(4, 32, 8)
+        switch (plan.mb * 64 + plan.ks) {
+#define LP_CASE(M, K) case M * 64 + K: e = launch_stream<M, K>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+            LP_CASE(1, 1) LP_CASE(1, 2) LP_CASE(1, 4) LP_CASE(1, 8)
+            LP_CASE(2, 1) LP_CASE(2, 2) LP_CASE(2, 4) LP_CASE(2, 8)
+            LP_CASE(3, 1) LP_CASE(3, 2) LP_CASE(3, 4) LP_CASE(3, 8)
+            LP_CASE(4, 1) LP_CASE(4, 2) LP_CASE(4, 4) LP_CASE(4, 8)
 #undef LP_CASE
             default: return hipErrorInvalidValue;
         }

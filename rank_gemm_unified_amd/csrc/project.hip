@@ -40,19 +40,16 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     if (pl->path == PATH_DECODE) {
         const int64_t ksteps = H / 32;
         if (T <= 64 && H <= 8192) {
-            // streaming kernel: tiles of 16 NW columns x S splits of K, about 200-256 workgroups
-            // (one per CU: x's K chunk fills most of the LDS); fewest splits that reach that count
+            // streaming kernel: 64-column tiles x S splits of K, each split cut into four K quarters
+            // (one per wave) of at most 8 steps of 32; S grows towards 256 workgroups when H is small
             pl->stream = 1;
             pl->mb = (int32_t)std::max<int64_t>(1, (T + 15) / 16);
-            for (int nw = 4; nw <= 8; nw *= 2) {
-                pl->nw = nw;
-                pl->n_tiles = (int32_t)((H + 16 * nw - 1) / (16 * nw));
-                const int64_t S = std::max<int64_t>(1, std::min<int64_t>(8, (200 + pl->n_tiles - 1) / pl->n_tiles));
-                pl->ysplit = (int32_t)S;
-                if ((ksteps + S - 1) / S <= 32) break;
-            }
-            const int64_t need = (ksteps + pl->ysplit - 1) / pl->ysplit;
-            pl->ks = need <= 8 ? 8 : need <= 16 ? 16 : 32;
+            pl->n_tiles = (int32_t)(H / 64);
+            int64_t S = std::max<int64_t>(1, (ksteps + 31) / 32);
+            while (S < 8 && pl->n_tiles * S < 256 && 4 * (S + 1) <= ksteps) ++S;
+            pl->ysplit = (int32_t)S;
+            const int64_t q = (ksteps + 4 * S - 1) / (4 * S);
+            pl->ks = q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : 8;
         } else {
             pl->stream = 0;
             if (T <= 64) {

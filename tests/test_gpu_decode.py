@@ -99,13 +99,17 @@ def test_decode_shapes_integer_exact(T):
     assert torch.equal(y.cpu().view(torch.int16), bf16_round_f64(ref).view(torch.int16))
 
 
-@pytest.mark.parametrize("H", [64, 192, 512, 5120])
-def test_decode_hidden_sizes(H):
+# (H, T): every K-steps-per-wave variant of the T <= 64 kernel (1, 2, 4, 8), 16-row blocks 1..4,
+# waves with no K steps (H = 64), ragged quarters (192), a split count that is not a divisor of 8
+# (5120: plain workgroup order) and the largest hidden size the kernel takes (8192, 1024 workgroups)
+@pytest.mark.parametrize("H,T", [(64, 48), (192, 48), (512, 48), (5120, 48), (3072, 30), (2048, 64),
+                                 (8192, 64), (1024, 7)])
+def test_decode_hidden_sizes(H, T):
     rng = np.random.default_rng(H)
     ranks = [8, 16, 64, 0, 32]
-    ids = rng.integers(-1, len(ranks), 48)
+    ids = rng.integers(-1, len(ranks), T)
     w = custom(H, ranks, ids, device="cuda", seed=H)
-    say("case hidden", H)
+    say("case hidden", H, "T", T)
     pool = device_pool(w)
     y = run(pool, w, 0)
     torch.cuda.synchronize()
