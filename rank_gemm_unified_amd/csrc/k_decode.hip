@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     constexpr int SWZ = P < 16 ? P - 1 : 15;          // piece c of row r sits in slot c ^ (r & SWZ)
     constexpr int DS = KQ < 2 ? KQ : 2;               // W steps in flight ahead of the MFMA step
     constexpr int S1 = KQ > 1 ? 1 : 0;                // step that consumes the ranks (grouping)
-    constexpr int S2 = KQ > 3 ? 3 : KQ - 1;           // step that consumes the page-table entries
+    constexpr int S2 = KQ > 5 ? 5 : KQ - 1;           // step that consumes the page-table entries
     constexpr int XI = TP * P / 64;                   // row-contiguous x loads per wave (= MB * KQ)
     extern __shared__ __align__(16) char lds_raw[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -408,6 +408,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     // instead of queueing on one.  Rows >= T and pieces past the wave's K steps load valid stand-in
     // data: the MFMA rows and K steps they feed are never stored or never run.
     const int32_t a_raw = ids[min(lane, T - 1)];
+    // one W load (step 0, first 16 columns) goes out with x: the first touch of the wave's W rows
+    // (address translation, a cold HBM row) then overlaps x's instead of following it
+    const uint16_t *wr = W + (int64_t)(n0 + lrow) * H + kq + lq * 8;
+    const u32x4_t wfirst = load16(wr);
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t xv[XI];
 #pragma unroll
@@ -428,13 +432,13 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     // for x: issued together, the W misses delay x, and nothing can use W before x is in LDS.
 #pragma unroll
     for (int i = 0; i < XI; ++i) store16(xs + (size_t)(((i + tile) % XI) * 64 + lane) * 8, xv[i]);
-    const uint16_t *wr = W + (int64_t)(n0 + lrow) * H + kq + lq * 8;
     const int slast = max(nst - 1, 0);
     u32x4_t wv[KQ][4];
 #pragma unroll
     for (int st = 0; st < DS; ++st)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) wv[st][nb] = load16(wr + (int64_t)(16 * nb) * H + 32 * min(st, slast));
+        for (int nb = 0; nb < 4; ++nb)
+            wv[st][nb] = st == 0 && nb == 0 ? wfirst : load16(wr + (int64_t)(16 * nb) * H + 32 * min(st, slast));
     __builtin_amdgcn_sched_barrier(0);
 
     // metadata produced at steps S1 / S2
@@ -451,6 +455,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    u32x4_t xk[KQ][MB];   // the A operands of every step, kept for block 0's page MFMAs
     auto xop = [&](int st, int m) {   // MFMA A operand: rows m*16 + lrow, K step st
         const int row = m * 16 + lrow;
         return load16(xs + (size_t)(row * P + ((st * 4 + lq) ^ (row & SWZ))) * 8);
@@ -517,17 +522,17 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
             pj = p - __shfl(poff, sg, 64);
             pidx = plive ? (int64_t)pa * stride + pj : 0;
             ptc = pt + pidx;
-            // the page-table row of the segment this workgroup publishes first
+            pid = *ptc;
+            sc = scale[plive ? pa : 0];
+        }
+        if (st == S2) {
+            // the page-table row of the segment this workgroup publishes first (used at the end)
             const int ps = (int)blockIdx.x < nseg ? (int)blockIdx.x : 0;
             int32_t a_pub = __shfl(seg_a, ps, 64), r_pub = __shfl(seg_r, ps, 64);
             if ((int)blockIdx.x >= nseg) a_pub = r_pub = 0;   // nothing to publish: read entry 0
             const int lim = min(2 * r_pub + 1, stride);
 #pragma unroll
             for (int u = 0; u < 2; ++u) ent[u] = pt[(int64_t)a_pub * stride + min(lane + 64 * u, lim - 1)];
-            pid = *ptc;
-            sc = scale[plive ? pa : 0];
-        }
-        if (st == S2) {
             // this block's pages: lane loads page (lane % 16), K rows kq + 32 s + 8 (lane / 16) + [0, 8)
             int32_t pg = pid;
             const bool pok = plive && pg >= 0 && (int64_t)pg < num_pages;   // bad rows are reported by the publisher
@@ -539,22 +544,22 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
         // steps past the wave's K range multiply by zero (branch-free: a branch here would let the
         // compiler sink the W loads into it, after the point they are meant to be issued)
         const bool sl = st < nst;
-        u32x4_t xa[MB];
 #pragma unroll
-        for (int m = 0; m < MB; ++m) xa[m] = xop(st, m);
+        for (int m = 0; m < MB; ++m) xk[st][m] = xop(st, m);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const u32x4_t wb = sl ? wv[st][nb] : zero;
 #pragma unroll
             for (int m = 0; m < MB; ++m)
-                acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[m]),
+                acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xk[st][m]),
                                                                      __builtin_bit_cast(bf16x8_t, wb), acc[m][nb], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- page blocks: MFMA over the K quarter, scaled by s; the four quarters are summed in wave order
-    auto page_mfma = [&](const u32x4_t *pvb, float sc_col, f32x4_t *pacc) {
+    // (block 0 takes its A operands from registers, further blocks re-read them from LDS)
+    auto page_mfma = [&](const u32x4_t *pvb, float sc_col, f32x4_t *pacc, bool from_regs) {
 #pragma unroll
         for (int m = 0; m < MB; ++m) pacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -562,7 +567,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
             const u32x4_t bb = s2 < nst ? pvb[s2] : zero;
 #pragma unroll
             for (int m = 0; m < MB; ++m)
-                pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xop(s2, m)),
+                pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, from_regs ? xk[s2][m] : xop(s2, m)),
                                                                   __builtin_bit_cast(bf16x8_t, bb), pacc[m], 0, 0, 0);
         }
 #pragma unroll
@@ -587,7 +592,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
         }
     };
     f32x4_t pacc0[MB];
-    page_mfma(pv, sc, pacc0);
+    asm volatile("" ::"v"(ent[0]), "v"(ent[1]));   // the publisher's row has landed: keep its loads at S2
+    page_mfma(pv, sc, pacc0, true);
     // further blocks (more pages than 16 n_tiles: rare) while x is still in LDS, through their own buffer
     for (int b = tile + n_tiles; b * 16 < npages; b += n_tiles) {
         const int p = b * 16 + lrow;
@@ -607,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
 #pragma unroll
         for (int s2 = 0; s2 < KQ; ++s2) pv2[s2] = load16(pr + 32 * min(s2, slast));
         f32x4_t pacc[MB];
-        page_mfma(pv2, sc2, pacc);
+        page_mfma(pv2, sc2, pacc, false);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -637,16 +643,18 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     {
         const float *red = reinterpret_cast<const float *>(lds_raw);
         constexpr size_t WS = SH::REGION / 4;   // floats between the waves' regions
-        float v[MB * 4];
+        f32x4_t v[MB];
 #pragma unroll
-        for (int u = 0; u < MB * 4; ++u) {      // rows t = wave + 4 u, column = lane
-            const float *q = red + (size_t)(wave + 4 * u) * RS + lane;
-            v[u] = ((q[0] + q[WS]) + q[2 * WS]) + q[3 * WS];
+        for (int u = 0; u < MB; ++u) {          // thread -> row e / 16, columns 4 (e % 16) + [0, 4)
+            const int e = threadIdx.x + 256 * u;
+            const float *q = red + (size_t)(e >> 4) * RS + 4 * (e & 15);
+            v[u] = ((*reinterpret_cast<const f32x4_t *>(q) + *reinterpret_cast<const f32x4_t *>(q + WS)) +
+                    *reinterpret_cast<const f32x4_t *>(q + 2 * WS)) + *reinterpret_cast<const f32x4_t *>(q + 3 * WS);
         }
 #pragma unroll
-        for (int u = 0; u < MB * 4; ++u) {
-            const int t = wave + 4 * u;
-            if (t < T) ypart[((int64_t)split * T + t) * H + n0 + lane] = v[u];
+        for (int u = 0; u < MB; ++u) {
+            const int e = threadIdx.x + 256 * u, t = e >> 4;
+            if (t < T) *reinterpret_cast<f32x4_t *>(ypart + ((int64_t)split * T + t) * H + n0 + 4 * (e & 15)) = v[u];
         }
         page_store(red + TP * RS, WS, PS, plive, pa, pj);
     }
