@@ -147,9 +147,13 @@ __global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vp
 
 // ---- base GEMM + fused expand --------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDK = BK + 8;                         // padded LDS row (elements): conflict-free 16-B reads
-constexpr int STAGE = (BM + BN) * LDK;              // elements per pipeline stage
+constexpr int LDK = BK + 8;                         // padded LDS row (elements) of the low-rank operands
+constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline stage (unpadded, swizzled)
+// 16-byte piece p of row r of a stage sits in slot p ^ (r & 7): the 8 rows a group of lanes reads or
+// writes at one piece land on 8 different slots, so fragment reads and tile writes are conflict-free
+__device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ (r & 7)) << 3); }
 constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
+static_assert((size_t)BM * BN * 2 <= MAIN_LDS && (size_t)(BM + BN) * LDK * 2 <= MAIN_LDS, "LDS reuse after the K loop");
 
 __global__ __launch_bounds__(256, 1) void k_prefill_main(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
@@ -163,29 +167,43 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
     const int mt = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
     const int m0 = mt * BM, n0 = nt * BN;
 
-    // global -> LDS mapping: thread covers 8 rows (tid/8 + 32 i), 8 elements at column (tid%8)*8
+    // global -> LDS mapping: thread covers 8 rows (tid/8 + 32 i), 8 elements at column (tid%8)*8 of
+    // the BK slice.  Loads go through buffer resources based at the tile's first row, with 32-bit
+    // row offsets (no 64-bit address per load).  Rows past T (x) or H (W) read the last valid row:
+    // they only feed output rows or columns that are never stored.
     const int gr = tid >> 3, gc = (tid & 7) * 8;
-    const uint16_t *ga[8], *gb[8];
-    bool va[8], vb[8];
+    const int rvx = min(T - m0, BM), rvw = min(H - n0, BN);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(x + (int64_t)m0 * H), (short)0, rvx * H * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (int64_t)n0 * H), (short)0, rvw * H * 2, 0x00020000);
+    uint32_t offa[8], offb[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int row = gr + 32 * i;
-        va[i] = m0 + row < T;
-        vb[i] = n0 + row < H;
-        ga[i] = x + (int64_t)(va[i] ? m0 + row : 0) * H + gc;
-        gb[i] = W + (int64_t)(vb[i] ? n0 + row : 0) * H + gc;
+        offa[i] = (uint32_t)(min(gr + 32 * i, rvx - 1) * H + gc) * 2u;
+        offb[i] = (uint32_t)(min(gr + 32 * i, rvw - 1) * H + gc) * 2u;
     }
+    // the tile for K step kt + 1 is loaded while step kt computes and written to the other LDS stage
+    // (free since the last barrier) between the MFMAs of step kt's last two k-substeps
     u32x4_t ra[8], rb[8];
+    auto gload = [&](int kt) {
+        const int soff = kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        ra[i] = va[i] ? load16(ga[i]) : u32x4_t{0, 0, 0, 0};
-        rb[i] = vb[i] ? load16(gb[i]) : u32x4_t{0, 0, 0, 0};
-    }
+        for (int i = 0; i < 8; ++i) {
+            ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, offa[i], soff, 0));
+            rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, offb[i], soff, 0));
+        }
+    };
+    auto lstore = [&](uint16_t *stage, int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        store16(sm + (gr + 32 * i) * LDK + gc, ra[i]);
-        store16(sm + BM * LDK + (gr + 32 * i) * LDK + gc, rb[i]);
-    }
+        for (int i = i0; i < i1; ++i) {
+            store16(stage + swz(gr + 32 * i, gc >> 3), ra[i]);
+            store16(stage + BM * BK + swz(gr + 32 * i, gc >> 3), rb[i]);
+        }
+    };
+    const int nk = H / BK;
+    gload(0);
+    lstore(sm, 0, 8);
     __syncthreads();
 
     f32x16_t acc[4][4];
@@ -197,43 +215,50 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
             for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
 
     const int frow = lane & 31, fk = (lane >> 5) * 8;   // 32x32x16 operand: row lane%32, k 8*(lane/32)
-    const int nk = H / BK;
     for (int kt = 0; kt < nk; ++kt) {
         const uint16_t *As = sm + (kt & 1) * STAGE;
-        const uint16_t *Bs = As + BM * LDK;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int k = (kt + 1) * BK;
+        const uint16_t *Bs = As + BM * BK;
+        // the last step loads and stores a stand-in tile (step 0 again) into the unused stage: keeps
+        // the loop free of branches around the loads and stores
+        gload(kt + 1 < nk ? kt + 1 : 0);
+        uint16_t *nxt = sm + ((kt + 1) & 1) * STAGE;
+        // fragments of k-substep ks + 1 are read while the MFMAs of ks run
+        u32x4_t af[2][4], bf[2][4];
+        auto frag = [&](int ks, u32x4_t *fa, u32x4_t *fb) {   // in the order the MFMAs consume them
+            const int pc = ks * 2 + (fk >> 3);   // 16-byte piece of the row
+            fa[0] = load16(As + swz(wm * 128 + frow, pc));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                ra[i] = va[i] ? load16(ga[i] + k) : u32x4_t{0, 0, 0, 0};
-                rb[i] = vb[i] ? load16(gb[i] + k) : u32x4_t{0, 0, 0, 0};
-            }
-        }
+            for (int ni = 0; ni < 4; ++ni) fb[ni] = load16(Bs + swz(wn * 128 + ni * 32 + frow, pc));
+#pragma unroll
+            for (int mi = 1; mi < 4; ++mi) fa[mi] = load16(As + swz(wm * 128 + mi * 32 + frow, pc));
+        };
+        frag(0, af[0], bf[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            u32x4_t af[4], bf[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = load16(As + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                bf[ni] = load16(Bs + (wn * 128 + ni * 32 + frow) * LDK + ks * 16 + fk);
+            constexpr int NKS = BK / 16;
+            if (ks + 1 < NKS) frag(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            if (ks >= NKS - 2) lstore(nxt, (ks - (NKS - 2)) * 4, (ks - (NKS - 2)) * 4 + 4);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[mi]),
-                                                                          __builtin_bit_cast(bf16x8_t, bf[ni]),
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mi]),
+                                                                          __builtin_bit_cast(bf16x8_t, bf[ks & 1][ni]),
                                                                           acc[mi][ni], 0, 0, 0);
-        }
-        if (more) {
-            uint16_t *An = sm + ((kt + 1) & 1) * STAGE;
+            // the next k-substep's 8 fragment reads go out between the first 8 MFMAs, the tile writes
+            // between the last 8
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                store16(An + (gr + 32 * i) * LDK + gc, ra[i]);
-                store16(An + BM * LDK + (gr + 32 * i) * LDK + gc, rb[i]);
+            for (int g = 0; g < 8; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (ks + 1 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (ks >= NKS - 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
@@ -315,20 +340,27 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
         __syncthreads();
     }
 
-    // ---- one rounding, store.  32x32 block layout: lane holds column lane%32 and, in register e,
-    //      row 8*(e/4) + 4*(lane/32) + e%4.
+    // ---- one rounding, then the tile goes out through LDS as row-contiguous 16-byte stores.  32x32
+    //      block layout: lane holds column lane%32 and, in register e, row 8*(e/4) + 4*(lane/32) + e%4.
+    //      (The low-rank loop above ends with a barrier, so the LDS is free.)
+    constexpr int OS = BN;       // row of the staged tile (elements)
+    uint16_t *ot = sm;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int col = n0 + wn * 128 + ni * 32 + (lane & 31);
-            if (col >= H) continue;
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * 128 + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
-                if (row < T) y[(int64_t)row * H + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][e]);
+                const int row = wm * 128 + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+                const int col = wn * 128 + ni * 32 + (lane & 31);
+                ot[row * OS + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][e]);
             }
-        }
+    __syncthreads();
+#pragma unroll 4
+    for (int u = 0; u < BM * BN / 8 / 256; ++u) {
+        const int idx = tid + 256 * u, row = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+        if (m0 + row < T && n0 + c < H) store16(y + (int64_t)(m0 + row) * H + n0 + c, load16(ot + row * OS + c));
+    }
 }
 
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
