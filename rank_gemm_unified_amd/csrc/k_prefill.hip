@@ -1,9 +1,9 @@
 // Prefill-shaped projection (many tokens per request, T > 256): MFMA-bound.
 //
-//   k_shrink_mfma    v = s_a X_seg A_a for every 64-row chunk of every adapter segment (tokens
-//                    grouped by the grouping kernel), as a bf16 MFMA GEMM against the r gathered A
-//                    pages, split over K; the last split to arrive for a chunk sums the float32
-//                    partials in split order, scales, and stores v in bfloat16.
+//   k_shrink_mfma    partials of X_seg A_a for every 64-row chunk of every adapter segment (tokens
+//                    grouped by the grouping kernel), a small tiled bf16 MFMA GEMM against the r
+//                    gathered A pages, split over K;
+//   k_v_finalize     v = bf16(s_a * the split partials summed in split order);
 //   k_prefill_main   y = x W for a 256x256 output tile (bf16 MFMA 32x32x16, LDS double buffer),
 //                    then the low-rank term as extra K: for each adapter that owns rows of the
 //                    tile, [x | v_a] [W ; B_a] with v_a zero outside its rows and B_a's rows
@@ -19,78 +19,20 @@ namespace lorapool {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---- shrink ------------------------------------------------------------------------------------
-constexpr int SH_ROWS = 64;   // rows per work item (4 waves x 16)
+constexpr int SH_ROWS = 64;   // rows per work item
 constexpr int VSPLIT = 8;     // K-splits of the shrink
 
-// One wave: 16 rows x (NBR*16 pages) over K range [kb, ke); partial sums to vpart[split].
-// NBR is a template parameter so the MFMA loop carries no per-block conditions; pages j >= r are
-// read from a clamped valid page and zeroed by select.
-template <int NBR>
-__device__ __forceinline__ void shrink_rows(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages,
-                                            int32_t H, const int32_t *__restrict__ prow, int32_t r,
-                                            const int32_t *__restrict__ prm, int n, int kb, int ke, int lane,
-                                            int wave, float *__restrict__ vout, int32_t T, int32_t R) {
-    const int lrow = lane & 15, lk = (lane >> 4) * 8;
-    const int my = wave * 16 + lrow;
-    const bool xv = my < n;
-    const uint16_t *xr = x + (int64_t)prm[xv ? my : 0] * H + lk;
-    const uint16_t *ap[NBR];
-    bool av[NBR];
-#pragma unroll
-    for (int nb = 0; nb < NBR; ++nb) {
-        const int j = nb * 16 + lrow;
-        av[nb] = j < r;
-        ap[nb] = pages + (int64_t)prow[min(j, r - 1)] * H + lk;
-    }
-    f32x4_t acc[NBR];
-#pragma unroll
-    for (int nb = 0; nb < NBR; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int U = 4;
-    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
-    int k = kb;
-    for (; k + 32 * U <= ke; k += 32 * U) {
-        u32x4_t xa[U], bb[U][NBR];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            xa[u] = load16(xr + k + 32 * u);
-#pragma unroll
-            for (int nb = 0; nb < NBR; ++nb) bb[u][nb] = load16(ap[nb] + k + 32 * u);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const u32x4_t xs = xv ? xa[u] : zero;
-#pragma unroll
-            for (int nb = 0; nb < NBR; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs),
-                                                                  __builtin_bit_cast(bf16x8_t, av[nb] ? bb[u][nb] : zero),
-                                                                  acc[nb], 0, 0, 0);
-        }
-    }
-    for (; k < ke; k += 32) {
-        const u32x4_t xs = xv ? load16(xr + k) : zero;
-#pragma unroll
-        for (int nb = 0; nb < NBR; ++nb) {
-            const u32x4_t bb = load16(ap[nb] + k);
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs),
-                                                              __builtin_bit_cast(bf16x8_t, av[nb] ? bb : zero), acc[nb],
-                                                              0, 0, 0);
-        }
-    }
-    // lane holds rows 4*(lane/16)+i of column lane%16 of each 16x16 block
-#pragma unroll
-    for (int nb = 0; nb < NBR; ++nb) {
-        const int j = nb * 16 + lrow;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = wave * 16 + (lane >> 4) * 4 + i;
-            if (rr < n && j < r) vout[(int64_t)prm[rr] * R + j] = acc[nb][i];
-        }
-    }
-}
-
-// Grid (work items, VSPLIT).  Writes float32 partials vpart[split][t][0..r); k_v_finalize adds
-// them.  (No in-kernel cross-workgroup reduction: on this chip a device-scope fence writes back
+// Grid (work items, VSPLIT).  Work item = up to 64 tokens of one adapter segment; split = a K range
+// of H / VSPLIT.  A small tiled GEMM: per K tile of 64, the item's x rows (gathered through perm) and
+// the adapter's A pages (<= 64, one per column of v) go through a double-buffered LDS stage with
+// row-contiguous 16-byte loads; four waves compute 32x32 blocks (rows 32 wm.., pages 32 wn..) with
+// 32x32x16 MFMAs.  Writes float32 partials vpart[split][t][0..r); k_v_finalize adds them in split
+// order.  (No in-kernel cross-workgroup reduction: on this chip a device-scope fence writes back
 // and invalidates the whole L2.)
+constexpr int SK = 64;                                  // K tile
+constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements
+__device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ (r & 7)) << 3); }
+
 __global__ __launch_bounds__(256) void k_shrink_mfma(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H, const int32_t *__restrict__ pt,
     int32_t stride, const int32_t *__restrict__ perm, const int32_t *__restrict__ seg_a,
@@ -99,24 +41,68 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(
     int32_t R) {
     const int item = blockIdx.x;
     if (item >= ctrl[CTRL_NITEMS]) return;
+    __shared__ __align__(16) uint16_t st[2][SH_STAGE];
     __shared__ int32_t s_perm[SH_ROWS];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int split = blockIdx.y;
-    const int32_t s = item_seg[item], row0 = item_row[item];
-    const int32_t n = min(seg_start[s + 1] - row0, SH_ROWS);
-    if (threadIdx.x < SH_ROWS) s_perm[threadIdx.x] = perm[row0 + min((int)threadIdx.x, n - 1)];
-    const int32_t a = seg_a[s];
+    const int32_t sg = item_seg[item], row0 = item_row[item];
+    const int32_t n = min(seg_start[sg + 1] - row0, SH_ROWS);
+    if (tid < SH_ROWS) s_perm[tid] = perm[row0 + min(tid, n - 1)];
+    const int32_t a = seg_a[sg];
+    const int32_t *prow = pt + (int64_t)a * stride;
     __syncthreads();
     const int32_t r = tok_r[s_perm[0]];
-    const int32_t *prow = pt + (int64_t)a * stride;
-    const int ksteps = H / 32;
-    const int kb = (int)((int64_t)ksteps * split / VSPLIT) * 32, ke = (int)((int64_t)ksteps * (split + 1) / VSPLIT) * 32;
+    const int ktiles = H / SK;
+    const int kt0 = (int)((int64_t)ktiles * split / VSPLIT), kt1 = (int)((int64_t)ktiles * (split + 1) / VSPLIT);
+    // loads: thread -> row tid/8 (+32), 16-byte piece tid%8: x rows 0..63 (gathered), page rows 0..63
+    // (pages j >= r read page j = r - 1: their columns are never stored)
+    const int lr = tid >> 3, lp = tid & 7;
+    const uint16_t *src[4];
+    src[0] = x + (int64_t)s_perm[lr] * H + lp * 8;
+    src[1] = x + (int64_t)s_perm[lr + 32] * H + lp * 8;
+    src[2] = pages + (int64_t)prow[min(lr, r - 1)] * H + lp * 8;
+    src[3] = pages + (int64_t)prow[min(lr + 32, r - 1)] * H + lp * 8;
+    u32x4_t rv[4];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv[i] = load16(src[i] + kt * SK);
+    };
+    auto lstore = [&](uint16_t *stg) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store16(stg + sswz(lr + 32 * i, lp), rv[i]);
+    };
+    const int wm = wave >> 1, wn = wave & 1;
+    const int frow = lane & 31, fk = lane >> 5;
+    f32x16_t acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (kt0 < kt1) {
+        gload(kt0);
+        lstore(st[0]);
+        __syncthreads();
+        for (int kt = kt0; kt < kt1; ++kt) {
+            const int sidx = (kt - kt0) & 1;
+            const bool more = kt + 1 < kt1;
+            if (more) gload(kt + 1);
+            const uint16_t *S = st[sidx];
+#pragma unroll
+            for (int ks = 0; ks < SK / 16; ++ks) {
+                const u32x4_t fa = load16(S + sswz(wm * 32 + frow, ks * 2 + fk));
+                const u32x4_t fb = load16(S + sswz(SH_ROWS + wn * 32 + frow, ks * 2 + fk));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa),
+                                                              __builtin_bit_cast(bf16x8_t, fb), acc, 0, 0, 0);
+            }
+            if (more) lstore(st[sidx ^ 1]);
+            __syncthreads();
+        }
+    }
+    // 32x32 block layout: lane holds column (page) lane%32 and, in register e, row 8 (e/4) + 4 (lane/32) + e%4
     float *vout = vpart + (int64_t)split * T * R;
-    switch ((r + 15) / 16) {
-        case 1: shrink_rows<1>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
-        case 2: shrink_rows<2>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
-        case 3: shrink_rows<3>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
-        default: shrink_rows<4>(x, pages, H, prow, r, s_perm, n, kb, ke, lane, wave, vout, T, R); break;
+    const int j = wn * 32 + (lane & 31);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int rr = wm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+        if (rr < n && j < r) vout[(int64_t)s_perm[rr] * R + j] = acc[e];
     }
 }
 

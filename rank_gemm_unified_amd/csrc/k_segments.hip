@@ -49,12 +49,81 @@ __device__ int32_t block_exclusive_scan(int32_t *a, int32_t n, int32_t *scratch)
     return total;
 }
 
-// One workgroup of 1024 threads.  LDS: hist[max_adapters] | segf[max_adapters] | seglen[max_adapters]
-// | scratch[32].  Each thread keeps up to KPT of its tokens (t = tid + 1024 u) in registers, so a
-// batch of up to 8192 tokens costs one read of the ids; longer batches re-read them from tok_a.
-// Tokens of one adapter land in perm in an unspecified order (LDS atomics): no result depends on
-// the order of tokens within a segment.
+// Wave-aggregated LDS counter update: every lane with key >= 0 adds 1 to cnt[key]; the lanes sharing
+// a key are served by one atomic (issued by the lowest of them), and each gets old + its rank among
+// them.  Returns -1 for lanes with key < 0.  (Tokens of one adapter are mostly neighbours, so a wave
+// holds few distinct keys; per-lane atomics on a handful of counters would serialize.)
+__device__ __forceinline__ int32_t wave_add_rank(int32_t *cnt, int32_t key) {
+    const int lane = threadIdx.x & 63;
+    int32_t pos = -1;
+    uint64_t remaining = __ballot(key >= 0);
+    while (remaining) {
+        const int leader = __ffsll((unsigned long long)remaining) - 1;
+        const int32_t lkey = __shfl(key, leader, 64);
+        const uint64_t m = __ballot(key == lkey);
+        int32_t old = 0;
+        if (lane == leader) old = atomicAdd(&cnt[lkey], __popcll(m));
+        old = __shfl(old, leader, 64);
+        if (key == lkey) pos = old + __popcll(m & ((1ull << lane) - 1ull));
+        remaining &= ~m;
+    }
+    return pos;
+}
+
+// Exclusive scan of three arrays at once (same layout as block_exclusive_scan); returns the totals.
+__device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int32_t n, int32_t *scratch) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = SEG_THREADS / 64;
+    const int per = (n + SEG_THREADS - 1) / SEG_THREADS;
+    const int b = tid * per, e = min(n, b + per);
+    int32_t l0 = 0, l1 = 0, l2 = 0;
+    for (int i = b; i < e; ++i) { l0 += a0[i]; l1 += a1[i]; l2 += a2[i]; }
+    int32_t i0 = l0, i1 = l1, i2 = l2;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y0 = __shfl_up(i0, off, 64), y1 = __shfl_up(i1, off, 64), y2 = __shfl_up(i2, off, 64);
+        if (lane >= off) { i0 += y0; i1 += y1; i2 += y2; }
+    }
+    if (lane == 63) { scratch[wave] = i0; scratch[NW + 1 + wave] = i1; scratch[2 * (NW + 1) + wave] = i2; }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            int32_t *sc = scratch + q * (NW + 1);
+            const int32_t w = lane < NW ? sc[lane] : 0;
+            int32_t wi = w;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int32_t y = __shfl_up(wi, off, 64);
+                if (lane >= off) wi += y;
+            }
+            if (lane < NW) sc[lane] = wi - w;
+            if (lane == NW - 1) sc[NW] = wi;
+        }
+    }
+    __syncthreads();
+    int32_t r0 = scratch[wave] + i0 - l0, r1 = scratch[NW + 1 + wave] + i1 - l1,
+            r2 = scratch[2 * (NW + 1) + wave] + i2 - l2;
+    for (int i = b; i < e; ++i) {
+        const int32_t v0 = a0[i], v1 = a1[i], v2 = a2[i];
+        a0[i] = r0; a1[i] = r1; a2[i] = r2;
+        r0 += v0; r1 += v1; r2 += v2;
+    }
+    const int3 tot = make_int3(scratch[NW], scratch[2 * (NW + 1) - 1], scratch[3 * (NW + 1) - 1]);
+    __syncthreads();
+    return tot;
+}
+
+// One workgroup of 1024 threads, two dependent rounds of global reads:
+//  1. the ids (range-checked; tokens counted per adapter id);
+//  2. for every adapter in use, its rank and its whole page-table row, all loaded together and
+//     checked after they arrive (entries [0, 2r) hold pages in range, entry 2r is -1 when 2r < stride).
+// Tokens of an adapter with rank 0, a bad rank or a bad row get no low-rank term.  Segments are in
+// adapter order; tokens of one adapter land in perm in an unspecified order (LDS atomics): no result
+// depends on the order of tokens within a segment.
+// LDS: cnt | uidx | ulist | rk (max_adapters each) | scratch[3 * 17].
 constexpr int KPT = 8;
+constexpr int32_t F_OFF = 1 << 30;   // cnt flag: the adapter's tokens get no low-rank term
 
 __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const int32_t *__restrict__ pt,
@@ -64,162 +133,142 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     int32_t *__restrict__ item_row, int32_t *__restrict__ ctrl, int32_t *__restrict__ counters,
     int32_t n_counters, int *__restrict__ err) {
     extern __shared__ int32_t lds[];
-    int32_t *hist = lds, *segf = lds + max_adapters, *seglen = lds + 2 * max_adapters;
-    int32_t *scratch = lds + 3 * max_adapters;
+    int32_t *cnt = lds, *uidx = lds + max_adapters, *ulist = lds + 2 * max_adapters, *rk = lds + 3 * max_adapters;
+    int32_t *scratch = lds + 4 * max_adapters;
     __shared__ int s_err;
     const int tid = threadIdx.x;
     const bool cached = T <= KPT * SEG_THREADS;
     int my_err = 0;
     if (tid == 0) s_err = 0;
     for (int i = tid; i < n_counters; i += SEG_THREADS) counters[i] = 0;
-    for (int a = tid; a < max_adapters; a += SEG_THREADS) hist[a] = 0;
+    for (int a = tid; a < max_adapters; a += SEG_THREADS) cnt[a] = 0;
     __syncthreads();
 
-    // 1. id and rank range checks; count tokens per adapter with rank > 0
+    // ---- round 1: ids
     int32_t key[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) key[u] = -1;
     for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
-        int32_t a[KPT], rr[KPT];
+        int32_t a[KPT];
 #pragma unroll
         for (int u = 0; u < KPT; ++u) a[u] = ids[min(t0 + u * SEG_THREADS + tid, T - 1)];
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) rr[u] = ranks[a[u] >= 0 && a[u] < max_adapters ? a[u] : 0];
-#pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int t = t0 + u * SEG_THREADS + tid;
-            int32_t k = -1, r = 0;
+            int32_t k = -1;
             if (t < T && a[u] != -1) {
-                if (a[u] < -1 || a[u] >= max_adapters) {
-                    my_err |= DEV_ERR_ID;
-                } else if (rr[u] < 0 || rr[u] > max_rank) {
-                    my_err |= DEV_ERR_RANK;
-                } else if (rr[u] > 0) {
-                    k = a[u];
-                    r = rr[u];
-                    atomicAdd(&hist[k], 1);
-                }
+                if (a[u] < -1 || a[u] >= max_adapters) my_err |= DEV_ERR_ID;
+                else k = a[u];
             }
-            if (t < T) {
-                tok_a[t] = k;
-                tok_r[t] = r;
-            }
+            wave_add_rank(cnt, k);
+            if (t < T && !cached) tok_a[t] = k;
             if (cached) key[u] = k;
         }
     }
     __syncthreads();
-
-    // 2. each adapter in use: its page-table row must hold exactly 2r in-range pages.  The entries
-    //    of all used adapters are checked by all threads together (flattened list, 4 loads in flight).
-    for (int a = tid; a < max_adapters; a += SEG_THREADS) segf[a] = hist[a] > 0;
+    for (int a = tid; a < max_adapters; a += SEG_THREADS) uidx[a] = cnt[a] > 0;
     __syncthreads();
-    const int32_t nused = block_exclusive_scan(segf, max_adapters, scratch);   // segf := used index
+    const int32_t nused = block_exclusive_scan(uidx, max_adapters, scratch);
     for (int a = tid; a < max_adapters; a += SEG_THREADS)
-        if (hist[a] > 0) seglen[segf[a]] = a;                                   // seglen := used list
+        if (cnt[a] > 0) ulist[uidx[a]] = a;
     __syncthreads();
-    for (int u = tid; u < max_adapters; u += SEG_THREADS)
-        segf[u] = u < nused ? min(2 * ranks[seglen[u]] + 1, stride) : 0;
-    __syncthreads();
-    const int32_t nchk = block_exclusive_scan(segf, max_adapters, scratch);    // segf := entry offsets
-    for (int e0 = tid; e0 < nchk; e0 += 4 * SEG_THREADS) {
-        int ua[4], j[4];
-        int32_t ent[4];
+
+    // ---- round 2: rank and page-table row of every adapter in use (stride entries each)
+    const int32_t nent = nused * stride;
+    for (int e0 = tid; e0 < nent; e0 += 8 * SEG_THREADS) {
+        int32_t av[8], jv[8], rv[8], ev[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = min(e0 + u * SEG_THREADS, nchk - 1);
-            int lo = 0, hi = nused - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (segf[mid] <= e) lo = mid; else hi = mid - 1;
-            }
-            ua[u] = seglen[lo];
-            j[u] = e - segf[lo];
-            ent[u] = pt[(int64_t)ua[u] * stride + j[u]];
+        for (int u = 0; u < 8; ++u) {
+            const int e = min(e0 + u * SEG_THREADS, nent - 1);
+            av[u] = ulist[e / stride];
+            jv[u] = e % stride;
+            rv[u] = ranks[av[u]];
+            ev[u] = pt[(int64_t)av[u] * stride + jv[u]];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (e0 + u * SEG_THREADS >= nchk) continue;
-            const int32_t r = ranks[ua[u]];
+        for (int u = 0; u < 8; ++u) {
+            if (e0 + u * SEG_THREADS >= nent) continue;
+            const int32_t r = rv[u], j = jv[u], ent = ev[u];
             int bad = 0;
-            if (j[u] < 2 * r) {
-                if (ent[u] == -1) bad = DEV_ERR_TABLE;
-                else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad = DEV_ERR_PAGE;
-            } else if (ent[u] != -1) {
+            if (r < 0 || r > max_rank) {
+                if (j == 0) { bad = DEV_ERR_RANK; atomicOr(&cnt[av[u]], F_OFF); }
+            } else if (r == 0) {
+                if (j == 0) atomicOr(&cnt[av[u]], F_OFF);
+            } else if (j < 2 * r) {
+                if (ent == -1) bad = DEV_ERR_TABLE;
+                else if (ent < 0 || (int64_t)ent >= num_pages) bad = DEV_ERR_PAGE;
+            } else if (j == 2 * r && ent != -1) {
                 bad = DEV_ERR_TABLE;
             }
+            if (j == 0) rk[av[u]] = r;
             if (bad) {
                 my_err |= bad;
-                atomicOr(&hist[ua[u]], 0x40000000);
+                atomicOr(&cnt[av[u]], F_OFF);
             }
         }
     }
     __syncthreads();
 
-    // 3. tokens of a faulty adapter get the base product only
-    for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int t = t0 + u * SEG_THREADS + tid;
-            if (t >= T) continue;
-            const int32_t k = cached ? key[u] : tok_a[t];
-            if (k >= 0 && (hist[k] & 0x40000000)) {
-                tok_a[t] = -1;
-                tok_r[t] = 0;
-                if (cached) key[u] = -1;
+    // ---- segments: adapters in use with a good row, in adapter order; work items of `chunk` tokens
+    for (int a = tid; a < max_adapters; a += SEG_THREADS) {
+        const int32_t c = cnt[a];
+        const int32_t n = (c & F_OFF) ? 0 : c;
+        cnt[a] = n;                       // -> first sorted position
+        uidx[a] = n > 0;                  // -> segment index
+        ulist[a] = (n + chunk - 1) / chunk;   // -> first work item
+    }
+    __syncthreads();
+    // (a segment's length is re-derived from the scanned offsets of consecutive adapters)
+    const int3 tot = block_exclusive_scan3(cnt, uidx, ulist, max_adapters, scratch);
+    const int32_t nvalid = tot.x, nseg = tot.y, nitems = tot.z;
+    for (int a = tid; a < max_adapters; a += SEG_THREADS) {
+        const int32_t next = a + 1 < max_adapters ? cnt[a + 1] : nvalid;
+        const int32_t n = next - cnt[a];
+        if (n > 0) {
+            const int32_t sg = uidx[a];
+            seg_a[sg] = a;
+            seg_start[sg] = cnt[a];
+            int32_t it = ulist[a];
+            for (int32_t r0 = cnt[a]; r0 < next; r0 += chunk, ++it) {
+                item_seg[it] = sg;
+                item_row[it] = r0;
             }
-        }
-    }
-    __syncthreads();
-    for (int a = tid; a < max_adapters; a += SEG_THREADS) {
-        const int32_t c = (hist[a] & 0x40000000) ? 0 : hist[a];
-        hist[a] = c;
-        segf[a] = c > 0;
-        seglen[a] = c;
-    }
-    __syncthreads();
-    const int32_t nvalid = block_exclusive_scan(hist, max_adapters, scratch);   // hist := offsets
-    const int32_t nseg = block_exclusive_scan(segf, max_adapters, scratch);     // segf := segment index
-
-    // 4. segments in adapter order
-    for (int a = tid; a < max_adapters; a += SEG_THREADS) {
-        if (seglen[a] > 0) {
-            seg_a[segf[a]] = a;
-            seg_start[segf[a]] = hist[a];
         }
     }
     if (tid == 0) {
         seg_start[nseg] = nvalid;
         ctrl[CTRL_NSEG] = nseg;
         ctrl[CTRL_NVALID] = nvalid;
+        ctrl[CTRL_NITEMS] = nitems;
     }
     __syncthreads();
 
-    // 5. scatter token ids into their segments
+    // ---- tokens: record, scatter into their segments (cnt[a] runs through the segment's positions)
     for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int t = t0 + u * SEG_THREADS + tid;
             if (t >= T) continue;
-            const int32_t k = cached ? key[u] : tok_a[t];
-            if (k >= 0) perm[atomicAdd(&hist[k], 1)] = t;
+            int32_t k = cached ? key[u] : tok_a[t];
+            // the adapter has a segment iff its offset range is non-empty
+            const bool live = k >= 0 && (k + 1 < max_adapters ? cnt[k + 1] : nvalid) > cnt[k];
+            if (!live) k = -1;
+            tok_a[t] = k;
+            tok_r[t] = k >= 0 ? rk[k] : 0;
         }
     }
     __syncthreads();
-
-    // 6. shrink work items: each segment split into runs of `chunk` tokens
-    for (int s = tid; s < max_adapters; s += SEG_THREADS)
-        segf[s] = s < nseg ? (seglen[seg_a[s]] + chunk - 1) / chunk : 0;
-    __syncthreads();
-    const int32_t nitems = block_exclusive_scan(segf, max_adapters, scratch);
-    for (int s = tid; s < nseg; s += SEG_THREADS) {
-        const int32_t b = seg_start[s], e = b + seglen[seg_a[s]];
-        int32_t it = segf[s];
-        for (int32_t r0 = b; r0 < e; r0 += chunk, ++it) {
-            item_seg[it] = s;
-            item_row[it] = r0;
+    // positions: a second pass so that every live range check above read the unmodified offsets
+    // (every lane takes part in each step: the counter update is wave-wide)
+    for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int t = t0 + u * SEG_THREADS + tid;
+            const int32_t k = t < T ? tok_a[t] : -1;
+            const int32_t pos = wave_add_rank(cnt, k);
+            if (k >= 0) perm[pos] = t;
         }
     }
-    if (tid == 0) ctrl[CTRL_NITEMS] = nitems;
     if (my_err) atomicOr(&s_err, my_err);
     __syncthreads();
     if (tid == 0 && s_err) atomicOr(err, s_err);
@@ -262,7 +311,7 @@ __global__ __launch_bounds__(128) void k_debug_gather(const int32_t *__restrict_
     if (j == 0 && any) atomicOr(err, any);
 }
 
-static size_t segments_lds(int32_t max_adapters) { return (size_t)(3 * max_adapters + 32) * sizeof(int32_t); }
+static size_t segments_lds(int32_t max_adapters) { return (size_t)(4 * max_adapters + 3 * 17) * sizeof(int32_t); }
 
 hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws, const int32_t *ids,
                            const int32_t *ranks, const int32_t *pt, hipStream_t s) {

@@ -133,3 +133,32 @@ def test_prefill_matches_decode_path_within_tolerance():
     torch.cuda.synchronize()
     rel, mx = errors(y_small, storage_to_f64(y_big[:64]))
     assert rel <= BF16_REL and mx <= BF16_ABS
+
+
+def test_prefill_device_checks_flag_bad_tokens(prefill):
+    """The grouping kernel's checks on the prefill path: an out-of-range id, an adapter whose rank
+    does not match its page-table row and an adapter whose rank exceeds the pool's are reported in
+    the error word; their tokens get the base product bit for bit, every other token is unchanged."""
+    w, pool, y_ok = prefill
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0
+    ids, ranks = w.ids.copy(), w.ranks.copy()
+    ids[5] = 5000                                   # out of range
+    a_tab, a_rk = int(ids[600]), int(ids[1200])     # adapters of requests 1 and 2
+    assert a_tab != a_rk and min(a_tab, a_rk) >= 0
+    ranks[a_tab] = max(int(ranks[a_tab]) // 2, 1)   # not the loaded rank
+    ranks[a_rk] = w.max_rank + 5                    # beyond the pool's largest rank
+    y = torch.empty_like(w.x())
+    rg.lora_project(pool.handle, w.x(), w.W(0), pool.table[0], torch.as_tensor(ids, device="cuda"),
+                    torch.as_tensor(ranks, device="cuda"), torch.as_tensor(w.scales, device="cuda"), w.T, y,
+                    pool.workspace(w.T))
+    assert rg.lora_check_device_errors(pool.handle, check=False) == rg.LORA_EDEVICE
+    msg = rg.lora_last_error()
+    for part in ("adapter-id-out-of-range", "rank-out-of-range", "adapter-not-loaded-at-this-rank"):
+        assert part in msg, msg
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0     # cleared
+    bad = (ids == 5000) | (ids == a_tab) | (ids == a_rk)
+    y0 = run(pool, w, 0, ids=np.full(w.T, -1, np.int32))
+    torch.cuda.synchronize()
+    b = torch.as_tensor(bad, device="cuda")
+    assert torch.equal(y[b].view(torch.int16), y0[b].view(torch.int16))
+    assert torch.equal(y[~b].view(torch.int16), y_ok[~b].view(torch.int16))
