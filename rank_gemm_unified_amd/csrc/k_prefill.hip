@@ -31,7 +31,7 @@ constexpr int VSPLIT = 8;     // K-splits of the shrink
 // and invalidates the whole L2.)
 constexpr int SK = 64;                                  // K tile
 constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements
-__device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ (r & 7)) << 3); }
+__device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ ((r >> 1) & 7)) << 3); }   // as swz
 
 __global__ __launch_bounds__(256) void k_shrink_mfma(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H, const int32_t *__restrict__ pt,
@@ -135,26 +135,45 @@ __global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vp
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LDK = BK + 8;                         // padded LDS row (elements) of the low-rank operands
 constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline stage (unpadded, swizzled)
-// 16-byte piece p of row r of a stage sits in slot p ^ (r & 7): the 8 rows a group of lanes reads or
-// writes at one piece land on 8 different slots, so fragment reads and tile writes are conflict-free
-__device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ (r & 7)) << 3); }
+// 16-byte piece p of row r of a stage sits in slot p ^ ((r >> 1) & 7).  The LDS serves a 16-byte read
+// 16 lanes at a time over 64 banks (256 bytes): two 128-byte rows fill the banks once, so the 16 rows
+// of one piece that a fragment read touches must use 8 different slots in each of the two halves --
+// rows 2i and 2i + 1 share slot p ^ i.  Tile writes (8 lanes per row) are conflict-free either way.
+__device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 7)) << 3); }
 constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
 static_assert((size_t)BM * BN * 2 <= MAIN_LDS && (size_t)(BM + BN) * LDK * 2 <= MAIN_LDS, "LDS reuse after the K loop");
 
-__global__ __launch_bounds__(256, 1) void k_prefill_main(
+// 512 threads, two waves per SIMD: while one waits on LDS, a load or the barrier, the other keeps the
+// SIMD's MFMA pipe busy.  Wave w computes rows 128 (w / 4) + [0, 128) x columns 64 (w % 4) + [0, 64)
+// of the 256 x 256 tile as 4 x 2 blocks of 32 x 32.
+constexpr int PF_THREADS = 512;
+constexpr int WMI = 4, WNI = 2;
+
+__global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
     int32_t n_tiles_n, uint16_t *__restrict__ y) {
     extern __shared__ __align__(16) uint16_t sm[];
-    __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[4], s_nlist;
+    __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int mt = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
+    const int wm = wave >> 2, wn = wave & 3;
+    // tile order: consecutive workgroups go to the 8 XCDs in turn, so (when the tile count allows)
+    // each XCD takes a contiguous run of the order below; the order walks groups of 4 row tiles
+    // across all column tiles, so an XCD's tiles share x rows and W columns in its L2
+    int mt, nt;
+    {
+        const int n_tiles = gridDim.x, tm = n_tiles / n_tiles_n;
+        const int t = (n_tiles & 7) == 0 ? (blockIdx.x & 7) * (n_tiles >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+        constexpr int GM = 4;
+        const int grp = GM * n_tiles_n, g = t / grp, fm = g * GM, gsz = min(tm - fm, GM);
+        mt = fm + (t % grp) % gsz;
+        nt = (t % grp) / gsz;
+    }
     const int m0 = mt * BM, n0 = nt * BN;
 
-    // global -> LDS mapping: thread covers 8 rows (tid/8 + 32 i), 8 elements at column (tid%8)*8 of
-    // the BK slice.  Loads go through buffer resources based at the tile's first row, with 32-bit
+    // global -> LDS mapping: thread covers rows tid/8 + 64 i (i < 4), 8 elements at column (tid%8)*8
+    // of the BK slice.  Loads go through buffer resources based at the tile's first row, with 32-bit
     // row offsets (no 64-bit address per load).  Rows past T (x) or H (W) read the last valid row:
     // they only feed output rows or columns that are never stored.
     const int gr = tid >> 3, gc = (tid & 7) * 8;
@@ -163,19 +182,19 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
         __builtin_amdgcn_make_buffer_rsrc((void *)(x + (int64_t)m0 * H), (short)0, rvx * H * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc((void *)(W + (int64_t)n0 * H), (short)0, rvw * H * 2, 0x00020000);
-    uint32_t offa[8], offb[8];
+    uint32_t offa[4], offb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        offa[i] = (uint32_t)(min(gr + 32 * i, rvx - 1) * H + gc) * 2u;
-        offb[i] = (uint32_t)(min(gr + 32 * i, rvw - 1) * H + gc) * 2u;
+    for (int i = 0; i < 4; ++i) {
+        offa[i] = (uint32_t)(min(gr + 64 * i, rvx - 1) * H + gc) * 2u;
+        offb[i] = (uint32_t)(min(gr + 64 * i, rvw - 1) * H + gc) * 2u;
     }
     // the tile for K step kt + 1 is loaded while step kt computes and written to the other LDS stage
     // (free since the last barrier) between the MFMAs of step kt's last two k-substeps
-    u32x4_t ra[8], rb[8];
+    u32x4_t ra[4], rb[4];
     auto gload = [&](int kt) {
         const int soff = kt * BK * 2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, offa[i], soff, 0));
             rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, offb[i], soff, 0));
         }
@@ -183,20 +202,20 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
     auto lstore = [&](uint16_t *stage, int i0, int i1) {
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
-            store16(stage + swz(gr + 32 * i, gc >> 3), ra[i]);
-            store16(stage + BM * BK + swz(gr + 32 * i, gc >> 3), rb[i]);
+            store16(stage + swz(gr + 64 * i, gc >> 3), ra[i]);
+            store16(stage + BM * BK + swz(gr + 64 * i, gc >> 3), rb[i]);
         }
     };
     const int nk = H / BK;
     gload(0);
-    lstore(sm, 0, 8);
+    lstore(sm, 0, 4);
     __syncthreads();
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[WMI][WNI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < WNI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
 
@@ -206,58 +225,57 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
         const uint16_t *Bs = As + BM * BK;
         // the last step loads and stores a stand-in tile (step 0 again) into the unused stage: keeps
         // the loop free of branches around the loads and stores
-        gload(kt + 1 < nk ? kt + 1 : 0);
+        const int ktn = kt + 1 < nk ? kt + 1 : 0;
         uint16_t *nxt = sm + ((kt + 1) & 1) * STAGE;
         // fragments of k-substep ks + 1 are read while the MFMAs of ks run
-        u32x4_t af[2][4], bf[2][4];
+        u32x4_t af[2][WMI], bf[2][WNI];
         auto frag = [&](int ks, u32x4_t *fa, u32x4_t *fb) {   // in the order the MFMAs consume them
             const int pc = ks * 2 + (fk >> 3);   // 16-byte piece of the row
             fa[0] = load16(As + swz(wm * 128 + frow, pc));
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) fb[ni] = load16(Bs + swz(wn * 128 + ni * 32 + frow, pc));
+            for (int ni = 0; ni < WNI; ++ni) fb[ni] = load16(Bs + swz(wn * 64 + ni * 32 + frow, pc));
 #pragma unroll
-            for (int mi = 1; mi < 4; ++mi) fa[mi] = load16(As + swz(wm * 128 + mi * 32 + frow, pc));
+            for (int mi = 1; mi < WMI; ++mi) fa[mi] = load16(As + swz(wm * 128 + mi * 32 + frow, pc));
         };
         frag(0, af[0], bf[0]);
         __builtin_amdgcn_sched_barrier(0);
+        // per k-substep (8 MFMAs): the next substep's 6 fragment reads, then in substep 0 the next
+        // tile's 8 global loads, in substeps 2 and 3 four of its LDS writes, one after each MFMA
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             constexpr int NKS = BK / 16;
             if (ks + 1 < NKS) frag(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-            if (ks >= NKS - 2) lstore(nxt, (ks - (NKS - 2)) * 4, (ks - (NKS - 2)) * 4 + 4);
+            if (ks == 0) gload(ktn);
+            if (ks >= NKS - 2) lstore(nxt, (ks - (NKS - 2)) * 2, (ks - (NKS - 2)) * 2 + 2);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < WNI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mi]),
                                                                           __builtin_bit_cast(bf16x8_t, bf[ks & 1][ni]),
                                                                           acc[mi][ni], 0, 0, 0);
-            // the next k-substep's 8 fragment reads go out between the first 8 MFMAs, the tile writes
-            // between the last 8
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
+            for (int g = 0; g < WMI * WNI; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (ks + 1 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (ks >= NKS - 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (ks + 1 < NKS && g < WMI + WNI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (ks >= NKS - 2 && g >= 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
 
-    // ---- low-rank term: one K-extension per adapter owning rows of this tile
+    // ---- low-rank term: one K-extension per adapter owning rows of this tile (threads < BM own a row)
+    const bool rowt = tid < BM;
     {
         const int row = tid;
-        const int32_t key = m0 + row < T ? tok_a[m0 + row] : -1;
-        s_key[row] = key;
+        const int32_t key = rowt && m0 + row < T ? tok_a[m0 + row] : -1;
+        if (rowt) s_key[row] = key;
         __syncthreads();
         int first = key >= 0;
         for (int u = 0; u < row && first; ++u) first = s_key[u] != key;
-        // exclusive scan of `first` over the 256 threads
+        // exclusive scan of `first` over the 256 row threads
         int incl = first;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -272,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
             s_list[before + incl - 1] = key;
             s_lr[before + incl - 1] = tok_r[m0 + row];
         }
-        if (tid == 255) s_nlist = before + incl;
+        if (tid == BM - 1) s_nlist = before + incl;
         __syncthreads();
     }
     const int nlist = s_nlist;
@@ -282,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
         const int32_t a = s_list[li], r = s_lr[li];
         const int rp = (r + 15) & ~15;
         const int32_t *prow = pt + (int64_t)a * stride + r;
-        for (int idx = tid; idx < rp * (BN / 8); idx += 256) {
+        for (int idx = tid; idx < rp * (BN / 8); idx += PF_THREADS) {
             const int j = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
             u32x4_t b = u32x4_t{0, 0, 0, 0};
             if (j < r && n0 + c < H) b = load16(pages + (int64_t)prow[j] * H + n0 + c);
@@ -292,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
                 Bt[(c + 2 * e + 1) * LDK + j] = (uint16_t)(b[e] >> 16);
             }
         }
-        {
+        if (rowt) {
             const int row = tid;
             const bool mine = s_key[row] == a;
             const uint16_t *vr = v16 + (int64_t)(mine ? m0 + row : 0) * R;
@@ -310,15 +328,15 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
         }
         __syncthreads();
         for (int ks = 0; ks < rp / 16; ++ks) {
-            u32x4_t af[4], bf[4];
+            u32x4_t af[WMI], bf[WNI];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) af[mi] = load16(Vs + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
+            for (int mi = 0; mi < WMI; ++mi) af[mi] = load16(Vs + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) bf[ni] = load16(Bt + (wn * 128 + ni * 32 + frow) * LDK + ks * 16 + fk);
+            for (int ni = 0; ni < WNI; ++ni) bf[ni] = load16(Bt + (wn * 64 + ni * 32 + frow) * LDK + ks * 16 + fk);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < WNI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[mi]),
                                                                           __builtin_bit_cast(bf16x8_t, bf[ni]),
                                                                           acc[mi][ni], 0, 0, 0);
@@ -332,19 +350,19 @@ __global__ __launch_bounds__(256, 1) void k_prefill_main(
     constexpr int OS = BN;       // row of the staged tile (elements)
     uint16_t *ot = sm;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < WNI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = wm * 128 + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
-                const int col = wn * 128 + ni * 32 + (lane & 31);
+                const int col = wn * 64 + ni * 32 + (lane & 31);
                 ot[row * OS + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][e]);
             }
     __syncthreads();
 #pragma unroll 4
-    for (int u = 0; u < BM * BN / 8 / 256; ++u) {
-        const int idx = tid + 256 * u, row = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+    for (int u = 0; u < BM * BN / 8 / PF_THREADS; ++u) {
+        const int idx = tid + PF_THREADS * u, row = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
         if (m0 + row < T && n0 + c < H) store16(y + (int64_t)(m0 + row) * H + n0 + c, load16(ot + row * OS + c));
     }
 }
@@ -371,7 +389,7 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
     const int tn = (p->hidden + BN - 1) / BN, tm = (int)((plan.T + BM - 1) / BM);
-    hipLaunchKernelGGL(k_prefill_main, dim3(tm * tn), dim3(256), MAIN_LDS, s, (const uint16_t *)x, (const uint16_t *)W,
+    hipLaunchKernelGGL(k_prefill_main, dim3(tm * tn), dim3(PF_THREADS), MAIN_LDS, s, (const uint16_t *)x, (const uint16_t *)W,
                        (const uint16_t *)p->pages, pt, 2 * p->max_rank, ws.tok_a, ws.tok_r, ws.v16,
                        plan.rp, (int32_t)plan.T, p->hidden, tn, (uint16_t *)y);
     return hipGetLastError();
