@@ -141,7 +141,8 @@ constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline sta
 // rows 2i and 2i + 1 share slot p ^ i.  Tile writes (8 lanes per row) are conflict-free either way.
 __device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 7)) << 3); }
 constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
-static_assert((size_t)BM * BN * 2 <= MAIN_LDS && (size_t)(BM + BN) * LDK * 2 <= MAIN_LDS, "LDS reuse after the K loop");
+static_assert((size_t)BM * BN * 2 <= MAIN_LDS && ((size_t)64 * (BN + 8) + (size_t)BM * LDK) * 2 <= MAIN_LDS,
+              "LDS reuse after the K loop");
 
 // 512 threads, two waves per SIMD: while one waits on LDS, a load or the barrier, the other keeps the
 // SIMD's MFMA pipe busy.  Wave w computes rows 128 (w / 4) + [0, 128) x columns 64 (w % 4) + [0, 64)
@@ -294,8 +295,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
         __syncthreads();
     }
     const int nlist = s_nlist;
-    uint16_t *Bt = sm;                 // [BN][LDK]: B_a transposed, columns x j
-    uint16_t *Vs = sm + BN * LDK;      // [BM][LDK]: v rows of this adapter, zero elsewhere
+    // B_a's rows sit in LDS as they are in the pages, [j][n] (16-byte writes, one row per 32 lanes);
+    // the MFMA B operand (8 consecutive j of one column) is gathered with 2-byte reads, lane -> column,
+    // so neither the writes nor the reads conflict
+    constexpr int BNP = BN + 8;
+    uint16_t *Bn = sm;                 // [64][BNP]: B_a rows x the tile's columns
+    uint16_t *Vs = sm + 64 * BNP;      // [BM][LDK]: v rows of this adapter, zero elsewhere
     for (int li = 0; li < nlist; ++li) {
         const int32_t a = s_list[li], r = s_lr[li];
         const int rp = (r + 15) & ~15;
@@ -304,11 +309,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
             const int j = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
             u32x4_t b = u32x4_t{0, 0, 0, 0};
             if (j < r && n0 + c < H) b = load16(pages + (int64_t)prow[j] * H + n0 + c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Bt[(c + 2 * e) * LDK + j] = (uint16_t)(b[e] & 0xffffu);
-                Bt[(c + 2 * e + 1) * LDK + j] = (uint16_t)(b[e] >> 16);
-            }
+            store16(Bn + j * BNP + c, b);
         }
         if (rowt) {
             const int row = tid;
@@ -332,7 +333,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi) af[mi] = load16(Vs + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
 #pragma unroll
-            for (int ni = 0; ni < WNI; ++ni) bf[ni] = load16(Bt + (wn * 64 + ni * 32 + frow) * LDK + ks * 16 + fk);
+            for (int ni = 0; ni < WNI; ++ni) {
+                const uint16_t *col = Bn + (ks * 16 + fk) * BNP + wn * 64 + ni * 32 + frow;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) bf[ni][w] = (uint32_t)col[2 * w * BNP] | ((uint32_t)col[(2 * w + 1) * BNP] << 16);
+            }
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
