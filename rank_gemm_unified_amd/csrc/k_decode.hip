@@ -295,19 +295,6 @@ __device__ void dec_publish(DecGroup &g, int err, const int32_t *__restrict__ pt
 }
 
 // ---- wave-level grouping helpers for the T <= 64 kernel (lane = token) --------------------------------
-// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 inside each row of 16 lanes (DPP;
-// lanes shifted in from outside the row read 0), then the row totals carried across rows.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
-    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-              r2 = __builtin_amdgcn_readlane(v, 47);
-    const int row = lane >> 4;
-    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
-
 // Lanes holding the same key >= 0 (itself included), through a wave-private open-addressing table of
 // 128 slots in LDS: each lane claims its key's slot by compare-and-swap, then sets its bit in the
 // slot's mask.  At most 64 keys, so a free slot always exists.  Lanes with key < 0 get 0.

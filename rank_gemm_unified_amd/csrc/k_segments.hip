@@ -18,22 +18,12 @@ __device__ int32_t block_exclusive_scan(int32_t *a, int32_t n, int32_t *scratch)
     const int b = tid * per, e = min(n, b + per);
     int32_t local = 0;
     for (int i = b; i < e; ++i) local += a[i];
-    int32_t incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-    }
+    const int32_t incl = wave_incl_scan(local, lane);
     if (lane == 63) scratch[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        int32_t w = lane < SEG_THREADS / 64 ? scratch[lane] : 0;
-        int32_t wi = w;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t y = __shfl_up(wi, off, 64);
-            if (lane >= off) wi += y;
-        }
+        const int32_t w = lane < SEG_THREADS / 64 ? scratch[lane] : 0;
+        const int32_t wi = wave_incl_scan(w, lane);
         if (lane < SEG_THREADS / 64) scratch[lane] = wi - w;        // exclusive wave offsets
         if (lane == SEG_THREADS / 64 - 1) scratch[SEG_THREADS / 64] = wi;
     }
@@ -78,12 +68,7 @@ __device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int
     const int b = tid * per, e = min(n, b + per);
     int32_t l0 = 0, l1 = 0, l2 = 0;
     for (int i = b; i < e; ++i) { l0 += a0[i]; l1 += a1[i]; l2 += a2[i]; }
-    int32_t i0 = l0, i1 = l1, i2 = l2;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t y0 = __shfl_up(i0, off, 64), y1 = __shfl_up(i1, off, 64), y2 = __shfl_up(i2, off, 64);
-        if (lane >= off) { i0 += y0; i1 += y1; i2 += y2; }
-    }
+    const int32_t i0 = wave_incl_scan(l0, lane), i1 = wave_incl_scan(l1, lane), i2 = wave_incl_scan(l2, lane);
     if (lane == 63) { scratch[wave] = i0; scratch[NW + 1 + wave] = i1; scratch[2 * (NW + 1) + wave] = i2; }
     __syncthreads();
     if (wave == 0) {
@@ -91,12 +76,7 @@ __device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int
         for (int q = 0; q < 3; ++q) {
             int32_t *sc = scratch + q * (NW + 1);
             const int32_t w = lane < NW ? sc[lane] : 0;
-            int32_t wi = w;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int32_t y = __shfl_up(wi, off, 64);
-                if (lane >= off) wi += y;
-            }
+            const int32_t wi = wave_incl_scan(w, lane);
             if (lane < NW) sc[lane] = wi - w;
             if (lane == NW - 1) sc[NW] = wi;
         }
@@ -243,28 +223,19 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     }
     __syncthreads();
 
-    // ---- tokens: record, scatter into their segments (cnt[a] runs through the segment's positions)
+    // ---- tokens: record, scatter into their segments.  An adapter is live iff its segment index steps
+    // up after it (uidx, unlike cnt, is not changed by the scatter).  Every lane takes part in each
+    // step: the counter update is wave-wide.
     for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int t = t0 + u * SEG_THREADS + tid;
-            if (t >= T) continue;
-            int32_t k = cached ? key[u] : tok_a[t];
-            // the adapter has a segment iff its offset range is non-empty
-            const bool live = k >= 0 && (k + 1 < max_adapters ? cnt[k + 1] : nvalid) > cnt[k];
-            if (!live) k = -1;
-            tok_a[t] = k;
-            tok_r[t] = k >= 0 ? rk[k] : 0;
-        }
-    }
-    __syncthreads();
-    // positions: a second pass so that every live range check above read the unmodified offsets
-    // (every lane takes part in each step: the counter update is wave-wide)
-    for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int t = t0 + u * SEG_THREADS + tid;
-            const int32_t k = t < T ? tok_a[t] : -1;
+            int32_t k = t < T ? (cached ? key[u] : tok_a[t]) : -1;
+            if (k >= 0 && (k + 1 < max_adapters ? uidx[k + 1] : nseg) == uidx[k]) k = -1;
+            if (t < T) {
+                tok_a[t] = k;
+                tok_r[t] = k >= 0 ? rk[k] : 0;
+            }
             const int32_t pos = wave_add_rank(cnt, k);
             if (k >= 0) perm[pos] = t;
         }
