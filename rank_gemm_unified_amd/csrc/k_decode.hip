@@ -27,9 +27,6 @@ constexpr int DEC_T = 256;     // most tokens on the decode path
 constexpr int NT = 64;         // columns per base tile (64 < T <= 256 kernel)
 constexpr int NB = NT / 16;    // 16-column MFMA blocks per tile
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glob_void;
-
 // s_barrier with no memory fence; the asm statements keep the compiler from moving memory
 // accesses across it.  Callers make their own LDS writes complete first.
 __device__ __forceinline__ void workgroup_barrier() {

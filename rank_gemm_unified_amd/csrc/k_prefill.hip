@@ -144,11 +144,16 @@ constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
 static_assert((size_t)BM * BN * 2 <= MAIN_LDS && ((size_t)64 * (BN + 8) + (size_t)BM * LDK) * 2 <= MAIN_LDS,
               "LDS reuse after the K loop");
 
-// 512 threads, two waves per SIMD: while one waits on LDS, a load or the barrier, the other keeps the
-// SIMD's MFMA pipe busy.  Wave w computes rows 128 (w / 4) + [0, 128) x columns 64 (w % 4) + [0, 64)
-// of the 256 x 256 tile as 4 x 2 blocks of 32 x 32.
-constexpr int PF_THREADS = 512;
-constexpr int WMI = 4, WNI = 2;
+// PF_WAVES waves in a 2 x (PF_WAVES / 2) grid over the 256 x 256 tile; wave (wm, wn) computes rows
+// WTM wm + [0, WTM) x columns WTN wn + [0, WTN) as WMI x WNI blocks of 32 x 32.
+#ifndef PF_WAVES
+#define PF_WAVES 8
+#endif
+constexpr int PF_THREADS = PF_WAVES * 64;
+constexpr int WGN = PF_WAVES / 2;
+constexpr int WTM = BM / 2, WTN = BN / WGN;
+constexpr int WMI = WTM / 32, WNI = WTN / 32;
+constexpr int DPW = (BM * BK * 2 / 1024) / PF_WAVES;   // 1 KiB tile chunks per wave per operand per K step
 
 __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     extern __shared__ __align__(16) uint16_t sm[];
     __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WGN, wn = wave % WGN;
     // tile order: consecutive workgroups go to the 8 XCDs in turn, so (when the tile count allows)
     // each XCD takes a contiguous run of the order below; the order walks groups of 4 row tiles
     // across all column tiles, so an XCD's tiles share x rows and W columns in its L2
@@ -173,44 +178,46 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     }
     const int m0 = mt * BM, n0 = nt * BN;
 
-    // global -> LDS mapping: thread covers rows tid/8 + 64 i (i < 4), 8 elements at column (tid%8)*8
-    // of the BK slice.  Loads go through buffer resources based at the tile's first row, with 32-bit
-    // row offsets (no 64-bit address per load).  Rows past T (x) or H (W) read the last valid row:
-    // they only feed output rows or columns that are never stored.
-    const int gr = tid >> 3, gc = (tid & 7) * 8;
+    // Tiles go from global memory straight into LDS (16 bytes per lane, no register staging, no LDS
+    // write instructions).  One such load fills 1 KiB of a stage, rows 8c .. 8c + 7: lane l lands in
+    // row 8c + l / 8, slot l % 8, the slot of piece (l % 8) ^ ((row >> 1) & 7) -- so that is the piece
+    // the lane fetches.  Wave w issues chunks c = PF_WAVES i + w (i < DPW) of the x tile and of the W
+    // tile.
+    // Loads go through buffer resources based at the tile's first row, with 32-bit row offsets.  Rows
+    // past T (x) or H (W) read the last valid row: they only feed output rows or columns that are never
+    // stored.
     const int rvx = min(T - m0, BM), rvw = min(H - n0, BN);
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void *)(x + (int64_t)m0 * H), (short)0, rvx * H * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc((void *)(W + (int64_t)n0 * H), (short)0, rvw * H * 2, 0x00020000);
-    uint32_t offa[4], offb[4];
+    uint32_t offa[DPW], offb[DPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        offa[i] = (uint32_t)(min(gr + 64 * i, rvx - 1) * H + gc) * 2u;
-        offb[i] = (uint32_t)(min(gr + 64 * i, rvw - 1) * H + gc) * 2u;
+    for (int i = 0; i < DPW; ++i) {
+        const int r = 8 * (PF_WAVES * i + wave) + (lane >> 3), p = (lane & 7) ^ ((r >> 1) & 7);
+        offa[i] = (uint32_t)(min(r, rvx - 1) * H + p * 8) * 2u;
+        offb[i] = (uint32_t)(min(r, rvw - 1) * H + p * 8) * 2u;
     }
-    // the tile for K step kt + 1 is loaded while step kt computes and written to the other LDS stage
-    // (free since the last barrier) between the MFMAs of step kt's last two k-substeps
-    u32x4_t ra[4], rb[4];
-    auto gload = [&](int kt) {
+    auto dma = [&](int kt, uint16_t *stage) {
         const int soff = kt * BK * 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, offa[i], soff, 0));
-            rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, offb[i], soff, 0));
+        for (int i = 0; i < DPW; ++i) {
+            uint16_t *dst = stage + 8 * (PF_WAVES * i + wave) * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)dst, 16, offa[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(dst + BM * BK), 16, offb[i], soff, 0, 0);
         }
     };
-    auto lstore = [&](uint16_t *stage, int i0, int i1) {
+    const int frow = lane & 31, fk = (lane >> 5) * 8;   // 32x32x16 operand: row lane%32, k 8*(lane/32)
+    // the fragments of k-substep ks of a stage, in the order the MFMAs consume them
+    auto frag = [&](const uint16_t *stage, int ks, u32x4_t *fa, u32x4_t *fb) {
+        const uint16_t *As = stage, *Bs = stage + BM * BK;
+        const int pc = ks * 2 + (fk >> 3);   // 16-byte piece of the row
+        fa[0] = load16(As + swz(wm * WTM + frow, pc));
 #pragma unroll
-        for (int i = i0; i < i1; ++i) {
-            store16(stage + swz(gr + 64 * i, gc >> 3), ra[i]);
-            store16(stage + BM * BK + swz(gr + 64 * i, gc >> 3), rb[i]);
-        }
+        for (int ni = 0; ni < WNI; ++ni) fb[ni] = load16(Bs + swz(wn * WTN + ni * 32 + frow, pc));
+#pragma unroll
+        for (int mi = 1; mi < WMI; ++mi) fa[mi] = load16(As + swz(wm * WTM + mi * 32 + frow, pc));
     };
-    const int nk = H / BK;
-    gload(0);
-    lstore(sm, 0, 4);
-    __syncthreads();
 
     f32x16_t acc[WMI][WNI];
 #pragma unroll
@@ -220,34 +227,30 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
 
-    const int frow = lane & 31, fk = (lane >> 5) * 8;   // 32x32x16 operand: row lane%32, k 8*(lane/32)
+    // Pipeline over K steps of BK (two LDS stages; step kt computes from stage kt & 1 in four
+    // k-substeps).  The one barrier of a step sits between substeps 2 and 3: each wave first waits for
+    // its own loads of tile kt + 1 and for its last reads of stage kt & 1.  After it, substep 3 reads
+    // the fragments of step kt + 1's first substep (so no MFMA waits for LDS at a step boundary) and
+    // starts the loads of tile kt + 2 into stage kt & 1, which no wave reads any more.  Steps past the
+    // end load a stand-in tile (step 0 again): it keeps the loop free of branches and is never read.
+    const int nk = H / BK;
+    u32x4_t af[2][WMI], bf[2][WNI];
+    dma(0, sm);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma(nk > 1 ? 1 : 0, sm + STAGE);
+    frag(sm, 0, af[0], bf[0]);
     for (int kt = 0; kt < nk; ++kt) {
-        const uint16_t *As = sm + (kt & 1) * STAGE;
-        const uint16_t *Bs = As + BM * BK;
-        // the last step loads and stores a stand-in tile (step 0 again) into the unused stage: keeps
-        // the loop free of branches around the loads and stores
-        const int ktn = kt + 1 < nk ? kt + 1 : 0;
-        uint16_t *nxt = sm + ((kt + 1) & 1) * STAGE;
-        // fragments of k-substep ks + 1 are read while the MFMAs of ks run
-        u32x4_t af[2][WMI], bf[2][WNI];
-        auto frag = [&](int ks, u32x4_t *fa, u32x4_t *fb) {   // in the order the MFMAs consume them
-            const int pc = ks * 2 + (fk >> 3);   // 16-byte piece of the row
-            fa[0] = load16(As + swz(wm * 128 + frow, pc));
-#pragma unroll
-            for (int ni = 0; ni < WNI; ++ni) fb[ni] = load16(Bs + swz(wn * 64 + ni * 32 + frow, pc));
-#pragma unroll
-            for (int mi = 1; mi < WMI; ++mi) fa[mi] = load16(As + swz(wm * 128 + mi * 32 + frow, pc));
-        };
-        frag(0, af[0], bf[0]);
+        uint16_t *cur = sm + (kt & 1) * STAGE, *oth = sm + ((kt + 1) & 1) * STAGE;
+        const int kt2 = kt + 2 < nk ? kt + 2 : 0;
         __builtin_amdgcn_sched_barrier(0);
-        // per k-substep (8 MFMAs): the next substep's 6 fragment reads, then in substep 0 the next
-        // tile's 8 global loads, in substeps 2 and 3 four of its LDS writes, one after each MFMA
+        // per k-substep (WMI x WNI MFMAs, operands in buffer ks & 1): the next WMI + WNI fragment reads
+        // into the other buffer and, in substep 3, the 2 DPW loads of tile kt + 2, one after each MFMA
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            constexpr int NKS = BK / 16;
-            if (ks + 1 < NKS) frag(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-            if (ks == 0) gload(ktn);
-            if (ks >= NKS - 2) lstore(nxt, (ks - (NKS - 2)) * 2, (ks - (NKS - 2)) * 2 + 2);
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) frag(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            else frag(oth, 0, af[0], bf[0]);
+            if (ks == 3) dma(kt2, cur);
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
@@ -258,14 +261,20 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll
             for (int g = 0; g < WMI * WNI; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (ks + 1 < NKS && g < WMI + WNI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                if (ks >= NKS - 2 && g >= 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (g < WMI + WNI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (ks == 3 && g < 2 * DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (ks == 2) {
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        __syncthreads();
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads have landed: the LDS is reused below
+    __syncthreads();
 
     // ---- low-rank term: one K-extension per adapter owning rows of this tile (threads < BM own a row)
     const bool rowt = tid < BM;
@@ -331,10 +340,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
         for (int ks = 0; ks < rp / 16; ++ks) {
             u32x4_t af[WMI], bf[WNI];
 #pragma unroll
-            for (int mi = 0; mi < WMI; ++mi) af[mi] = load16(Vs + (wm * 128 + mi * 32 + frow) * LDK + ks * 16 + fk);
+            for (int mi = 0; mi < WMI; ++mi) af[mi] = load16(Vs + (wm * WTM + mi * 32 + frow) * LDK + ks * 16 + fk);
 #pragma unroll
             for (int ni = 0; ni < WNI; ++ni) {
-                const uint16_t *col = Bn + (ks * 16 + fk) * BNP + wn * 64 + ni * 32 + frow;
+                const uint16_t *col = Bn + (ks * 16 + fk) * BNP + wn * WTN + ni * 32 + frow;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) bf[ni][w] = (uint32_t)col[2 * w * BNP] | ((uint32_t)col[(2 * w + 1) * BNP] << 16);
             }
@@ -360,8 +369,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
         for (int ni = 0; ni < WNI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = wm * 128 + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
-                const int col = wn * 64 + ni * 32 + (lane & 31);
+                const int row = wm * WTM + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+                const int col = wn * WTN + ni * 32 + (lane & 31);
                 ot[row * OS + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][e]);
             }
     __syncthreads();
