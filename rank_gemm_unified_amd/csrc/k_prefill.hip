@@ -154,6 +154,8 @@ constexpr int WGN = PF_WAVES / 2;
 constexpr int WTM = BM / 2, WTN = BN / WGN;
 constexpr int WMI = WTM / 32, WNI = WTN / 32;
 constexpr int DPW = (BM * BK * 2 / 1024) / PF_WAVES;   // 1 KiB tile chunks per wave per operand per K step
+constexpr int LR_K = 64 * (BN / 8) / PF_THREADS;         // B-row pieces per thread of the low-rank term
+constexpr int LR_V = BM * (64 / 8) / PF_THREADS;         // v-row pieces per thread of the low-rank term
 
 __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
@@ -177,6 +179,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
         nt = (t % grp) / gsz;
     }
     const int m0 = mt * BM, n0 = nt * BN;
+
+    // ---- the adapters owning rows of this tile, in order of their first row (s_list, ranks s_lr), and
+    // the B page ids of the first one (pg0): worked out here, before the first tile load is waited
+    // for, so that after the K loop the low-rank term needs one round trip.  Thread t < BM owns row t.
+    // The two token loads go out before the tile loads, so waiting for them does not wait for those.
+    const bool rowt = tid < BM;
+    const int32_t key = rowt && m0 + tid < T ? tok_a[m0 + tid] : -1;
+    const int32_t key_r = rowt && m0 + tid < T ? tok_r[m0 + tid] : 0;
+    __builtin_amdgcn_sched_barrier(0);
 
     // Tiles go from global memory straight into LDS (16 bytes per lane, no register staging, no LDS
     // write instructions).  One such load fills 1 KiB of a stage, rows 8c .. 8c + 7: lane l lands in
@@ -236,6 +247,39 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     const int nk = H / BK;
     u32x4_t af[2][WMI], bf[2][WNI];
     dma(0, sm);
+    {
+        // LDS-only barriers here: a full __syncthreads would also wait for the tile loads
+        auto lds_sync = [] {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        if (rowt) s_key[tid] = key;
+        lds_sync();
+        int first = key >= 0;
+        for (int u = 0; u < tid && first; ++u) first = s_key[u] != key;
+        const int incl = wave_incl_scan(first, lane);   // exclusive scan of `first` over the row threads
+        if (lane == 63) s_wsum[wave] = incl;
+        lds_sync();
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += s_wsum[w];
+        if (first) {
+            s_list[before + incl - 1] = key;
+            s_lr[before + incl - 1] = key_r;
+        }
+        if (tid == BM - 1) s_nlist = before + incl;
+        lds_sync();
+    }
+    const int nlist = s_nlist;
+    // page ids of B rows j = (tid + PF_THREADS k) / 32 of adapter li (row r - 1 stands in past r)
+    auto lr_pages = [&](int li, int32_t *pg) {
+        const int32_t a = s_list[li], r = max(s_lr[li], 1);
+        const int32_t *prow = pt + (int64_t)a * stride + r;
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k) pg[k] = prow[min((tid + PF_THREADS * k) >> 5, r - 1)];
+    };
+    int32_t pg0[LR_K];
+    if (nlist > 0) lr_pages(0, pg0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     dma(nk > 1 ? 1 : 0, sm + STAGE);
@@ -276,66 +320,46 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads have landed: the LDS is reused below
     __syncthreads();
 
-    // ---- low-rank term: one K-extension per adapter owning rows of this tile (threads < BM own a row)
-    const bool rowt = tid < BM;
-    {
-        const int row = tid;
-        const int32_t key = rowt && m0 + row < T ? tok_a[m0 + row] : -1;
-        if (rowt) s_key[row] = key;
-        __syncthreads();
-        int first = key >= 0;
-        for (int u = 0; u < row && first; ++u) first = s_key[u] != key;
-        // exclusive scan of `first` over the 256 row threads
-        int incl = first;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int yv = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += yv;
-        }
-        if (lane == 63) s_wsum[wave] = incl;
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; ++w) before += s_wsum[w];
-        if (first) {
-            s_list[before + incl - 1] = key;
-            s_lr[before + incl - 1] = tok_r[m0 + row];
-        }
-        if (tid == BM - 1) s_nlist = before + incl;
-        __syncthreads();
-    }
-    const int nlist = s_nlist;
-    // B_a's rows sit in LDS as they are in the pages, [j][n] (16-byte writes, one row per 32 lanes);
-    // the MFMA B operand (8 consecutive j of one column) is gathered with 2-byte reads, lane -> column,
-    // so neither the writes nor the reads conflict
+    // ---- low-rank term: one K-extension per adapter owning rows of this tile.  B_a's rows sit in LDS
+    // as they are in the pages, [j][n] (16-byte writes, one row per 32 lanes); the MFMA B operand (8
+    // consecutive j of one column) is gathered with 2-byte reads, lane -> column, so neither the
+    // writes nor the reads conflict.  Thread -> B row j = idx / 32, columns 8 (idx % 32) + [0, 8) for
+    // idx = tid + PF_THREADS k (k < LR_K); v row tid % BM, entries 8 (LR_V (tid / BM) + k) + [0, 8)
+    // (k < LR_V).
     constexpr int BNP = BN + 8;
     uint16_t *Bn = sm;                 // [64][BNP]: B_a rows x the tile's columns
     uint16_t *Vs = sm + 64 * BNP;      // [BM][LDK]: v rows of this adapter, zero elsewhere
-    for (int li = 0; li < nlist; ++li) {
+    auto lowrank = [&](int li, const int32_t *pg) {
         const int32_t a = s_list[li], r = s_lr[li];
         const int rp = (r + 15) & ~15;
-        const int32_t *prow = pt + (int64_t)a * stride + r;
-        for (int idx = tid; idx < rp * (BN / 8); idx += PF_THREADS) {
-            const int j = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
-            u32x4_t b = u32x4_t{0, 0, 0, 0};
-            if (j < r && n0 + c < H) b = load16(pages + (int64_t)prow[j] * H + n0 + c);
-            store16(Bn + j * BNP + c, b);
-        }
-        if (rowt) {
-            const int row = tid;
-            const bool mine = s_key[row] == a;
-            const uint16_t *vr = v16 + (int64_t)(mine ? m0 + row : 0) * R;
-            for (int j = 0; j < rp; j += 8) {
-                u32x4_t vv = mine ? load16(vr + j) : u32x4_t{0, 0, 0, 0};
-                if (j + 8 > r) {   // clear entries j >= r of a partial group
+        u32x4_t bv[LR_K], vv[LR_V];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = j + 2 * e < r ? 0xffffu : 0u, hi = j + 2 * e + 1 < r ? 0xffff0000u : 0u;
-                        vv[e] &= lo | hi;
-                    }
-                }
-                store16(Vs + row * LDK + j, vv);
+        for (int k = 0; k < LR_K; ++k) {   // stand-in row (the adapter's first) past r, zeroed below
+            const int idx = tid + PF_THREADS * k, j = idx >> 5, c = (idx & 31) * 8;
+            bv[k] = load16(pages + (int64_t)pg[k] * H + min(n0 + c, H - 8));
+            if (!(j < r && n0 + c < H)) bv[k] = u32x4_t{0, 0, 0, 0};
+        }
+        const int vrow = tid % BM, vj = (tid / BM) * LR_V * 8;
+        const bool mine = s_key[vrow] == a;
+#pragma unroll
+        for (int k = 0; k < LR_V; ++k) {
+            const int j = vj + 8 * k;
+            vv[k] = load16(v16 + (int64_t)(mine ? m0 + vrow : m0) * R + min(j, R - 8));
+            if (!mine) vv[k] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {   // entries j >= r (never written for this token) are cleared
+                const uint32_t lo = j + 2 * e < r ? 0xffffu : 0u, hi = j + 2 * e + 1 < r ? 0xffff0000u : 0u;
+                vv[k][e] &= lo | hi;
             }
         }
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k) {
+            const int idx = tid + PF_THREADS * k, j = idx >> 5, c = (idx & 31) * 8;
+            if (j < rp) store16(Bn + j * BNP + c, bv[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < LR_V; ++k)
+            if (vj + 8 * k < rp) store16(Vs + vrow * LDK + vj + 8 * k, vv[k]);
         __syncthreads();
         for (int ks = 0; ks < rp / 16; ++ks) {
             u32x4_t af[WMI], bf[WNI];
@@ -356,6 +380,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
                                                                           acc[mi][ni], 0, 0, 0);
         }
         __syncthreads();
+    };
+    if (nlist > 0) lowrank(0, pg0);
+    for (int li = 1; li < nlist; ++li) {
+        int32_t pg[LR_K];
+        lr_pages(li, pg);
+        lowrank(li, pg);
     }
 
     // ---- one rounding, then the tile goes out through LDS as row-contiguous 16-byte stores.  32x32
