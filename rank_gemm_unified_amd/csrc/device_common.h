@@ -13,6 +13,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;   // an LDS address, as the LDS-load builtins take it
 
+// 16 bytes per lane from a buffer resource straight into LDS: lane l's bytes land at dst + 16 l.
+// (A non-template device function: a kernel template that names this builtin directly is dropped
+// from the host compilation pass.)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void *dst, uint32_t voff, int32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Round-to-nearest-even float32 -> bfloat16 bits; NaN stays NaN (quiet bit set).

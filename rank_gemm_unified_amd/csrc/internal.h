@@ -87,13 +87,11 @@ struct Plan {
     int32_t n_items_max;    // bound on shrink work items
     int32_t vsplit;         // K-splits of the shrink (partial v buffers)
     int32_t ysplit;         // K-splits of the decode base GEMM
-    int32_t n_tiles;        // decode: column tiles (one arrival counter each)
+    int32_t n_tiles;        // decode: 64-column tiles
     int32_t mb;             // decode: 16-row blocks per wave
-    int32_t wm;             // decode: waves along M (4 / wm along K)
-    int32_t n_shrink;       // decode: shrink workgroups beside the base workgroups
     int32_t n_counters;     // arrival counters the grouping kernel zeroes
     int32_t rp;             // row stride of v and per-token page lists (max_rank rounded up to 16)
-    int32_t stream;         // decode: 1 = streaming kernel (T <= 64), 0 = shrink/base workgroups
+    int32_t stream;         // decode: 1 = k_decode_stream (T <= 64), 0 = k_decode_wide
     int32_t ks;             // decode streaming kernel: max K steps of 32 per wave (a quarter of a split)
     // byte offsets into the workspace
     size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row,
@@ -129,6 +127,9 @@ hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws,
                            hipStream_t s);
 hipError_t launch_debug_gather(const lora_pool *p, const int32_t *pt, const int32_t *ids,
                                const int32_t *ranks, int64_t T, int32_t *out, hipStream_t s);
+hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
+                              const void *W, const int32_t *ids, const int32_t *ranks, const int32_t *pt,
+                              const float *scale, hipStream_t s);
 hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
                          const void *W, const int32_t *ids, const int32_t *ranks, const int32_t *pt,
                          const float *scale, void *y, hipStream_t s, hipEvent_t mid);

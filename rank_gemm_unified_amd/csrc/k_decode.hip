@@ -6,8 +6,8 @@
 // Two launches per call:
 //   T <= 64:       k_decode_stream   W, x and the batch's A pages in one streaming MFMA pass
 //                                    (the shrink x A is extra MFMA columns of the same contraction)
-//   64 < T <= 256: k_decode_main     shrink workgroups (one wave per gathered A page) beside split-K
-//                                    base workgroups
+//   64 < T <= 256: k_decode_wide     (k_decode_wide.hip) x streamed through LDS, W and the A pages
+//                                    of per-adapter work units in registers, one MFMA pass
 //   then           k_decode_finish   partial sums in split order + the expand sum_j v_j B_a[j, :]
 //                                    from B rows gathered from their pages + one rounding
 // ("S-LoRA, in depth", section "Merge or keep adapters separate": xW batched over all tokens
@@ -22,18 +22,7 @@
 
 namespace lorapool {
 
-constexpr int CHUNK = 16;      // tokens per shrink work item
-constexpr int DEC_T = 256;     // most tokens on the decode path
-constexpr int NT = 64;         // columns per base tile (64 < T <= 256 kernel)
-constexpr int NB = NT / 16;    // 16-column MFMA blocks per tile
-
-// s_barrier with no memory fence; the asm statements keep the compiler from moving memory
-// accesses across it.  Callers make their own LDS writes complete first.
-__device__ __forceinline__ void workgroup_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+constexpr int CHUNK = 16;      // tokens per shrink work item of the float32 path
 
 // One wave: v[tok[i]][j] = sc * <x[tok[i]], page> for i < n (1 <= n <= CHUNK).
 // Tokens go in groups of G; for each group the page is read in blocks of BLK 16-byte vectors per
@@ -102,193 +91,6 @@ __device__ __forceinline__ void shrink_page_wave(const char *__restrict__ x, con
             if (lane == 0 && g0 + i < n) v[(int64_t)tok[g0 + i] * R + j] = sc * tot;
         }
     }
-}
-
-// ---- in-LDS grouping of <= 256 tokens by adapter (thread t handles token t) ---------------------
-struct DecGroup {
-    int32_t key[DEC_T];        // adapter id, or -1 (none, rank 0, id or rank out of range)
-    int32_t r[DEC_T];
-    int32_t seg[DEC_T];        // segment of a token with key >= 0
-    int32_t seg_a[DEC_T], seg_r[DEC_T], seg_n[DEC_T], seg_bad[DEC_T];
-    int32_t seg_off[DEC_T + 1];    // first sorted position of each segment
-    int32_t item_off[DEC_T + 1];   // first 16-token shrink item of each segment
-    int32_t page_off[DEC_T + 1];   // first page of each segment in the batch's page list
-    int32_t chk_off[DEC_T + 1];    // first page-table entry to check of each segment
-    int32_t sorted[DEC_T];     // sorted position -> token
-    int32_t wsum[8];
-    int32_t n_seg, n_valid, n_items, n_pages, n_chk;
-};
-
-// exclusive prefix of v over the NTH threads; *total gets the sum (all threads)
-template <int NTH>
-__device__ int32_t scan_block(int32_t v, int32_t *wsum, int32_t *total) {
-    constexpr int NW = NTH / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-    }
-    __syncthreads();
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        before += w < wave ? wsum[w] : 0;
-        tot += wsum[w];
-    }
-    *total = tot;
-    return before + incl - v;
-}
-
-// last index s in [0, n) with off[s] <= i (off ascending, off[0] = 0)
-__device__ __forceinline__ int find_seg(const int32_t *off, int n, int32_t i) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Every workgroup that needs the grouping derives it from the ids; all derive the same one.
-// Returns the id/rank error bits this thread saw.
-template <int NTH>
-__device__ int dec_group(DecGroup &g, const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks,
-                         int32_t T, int32_t max_adapters, int32_t max_rank, int32_t stride) {
-    const int t = threadIdx.x;
-    const bool tok_thread = t < DEC_T;
-    int err = 0;
-    int32_t key = -1, r = 0;
-    if (t < T) {
-        const int32_t a = ids[t];
-        const int32_t rr = ranks[a >= 0 && a < max_adapters ? a : 0];
-        if (a != -1) {
-            if (a < -1 || a >= max_adapters) err |= DEV_ERR_ID;
-            else if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
-            else if (rr > 0) { key = a; r = rr; }
-        }
-    }
-    if (tok_thread) {
-        g.key[t] = key;
-        g.r[t] = r;
-        g.seg_n[t] = 0;
-        g.seg_bad[t] = 0;
-    }
-    __syncthreads();
-    int32_t first = t, rank_in = 0;
-    if (key >= 0) {
-        for (int u = 0; u < t; ++u) {
-            if (g.key[u] == key) {
-                if (rank_in == 0) first = u;
-                ++rank_in;
-            }
-        }
-    }
-    const int is_first = key >= 0 && rank_in == 0;
-    int32_t nseg;
-    const int32_t sid = scan_block<NTH>(is_first, g.wsum, &nseg);
-    if (is_first) {
-        g.seg[t] = sid;
-        g.seg_a[sid] = key;
-        g.seg_r[sid] = r;
-    }
-    __syncthreads();
-    int32_t my_seg = -1;
-    if (key >= 0) {
-        my_seg = g.seg[first];
-        atomicAdd(&g.seg_n[my_seg], 1);
-    }
-    __syncthreads();
-    // per segment (thread s): token offsets, shrink items, pages, entries to check
-    const bool seg_thread = t < nseg;
-    const int32_t n_s = seg_thread ? g.seg_n[t] : 0;
-    const int32_t r_s = seg_thread ? g.seg_r[t] : 0;
-    int32_t nvalid, nitems, npages, nchk, nid;
-    const int32_t off = scan_block<NTH>(n_s, g.wsum, &nvalid);
-    const int32_t ioff = scan_block<NTH>(r_s * ((n_s + CHUNK - 1) / CHUNK), g.wsum, &nitems);
-    const int32_t poff = scan_block<NTH>(r_s, g.wsum, &npages);
-    const int32_t coff = scan_block<NTH>(seg_thread ? min(2 * r_s + 1, stride) : 0, g.wsum, &nchk);
-    // identity / invalid tokens go after the grouped ones, in token order
-    const int32_t idpos = scan_block<NTH>(t < T && key < 0, g.wsum, &nid);
-    if (seg_thread) {
-        g.seg_off[t] = off;
-        g.item_off[t] = ioff;
-        g.page_off[t] = poff;
-        g.chk_off[t] = coff;
-    }
-    if (t == 0) {
-        g.n_seg = nseg;
-        g.n_valid = nvalid;
-        g.n_items = nitems;
-        g.n_pages = npages;
-        g.n_chk = nchk;
-        g.seg_off[nseg] = nvalid;
-        g.item_off[nseg] = nitems;
-        g.page_off[nseg] = npages;
-        g.chk_off[nseg] = nchk;
-    }
-    __syncthreads();
-    if (t < T) g.sorted[key >= 0 ? g.seg_off[my_seg] + rank_in : nvalid + idpos] = t;
-    __syncthreads();
-    return err;
-}
-
-// Workgroup 0's extra duty: check every page-table row in use (exactly 2r in-range pages, -1 after),
-// publish the sorted token list {token, adapter or -1, rank, 0} and, per sorted position, the token's
-// B page ids (row entries r..2r-1) for the finishing kernel; report errors.
-template <int NTH>
-__device__ void dec_publish(DecGroup &g, int err, const int32_t *__restrict__ pt, int32_t stride,
-                            int64_t num_pages, int32_t T, int32_t RP, int4 *__restrict__ sorted_tok,
-                            int32_t *__restrict__ spages, int *__restrict__ err_word) {
-    const int nseg = g.n_seg;
-    for (int e0 = threadIdx.x; e0 < g.n_chk; e0 += NTH * 4) {
-        int32_t ent[4];
-        int sg[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = min(e0 + u * NTH, g.n_chk - 1);
-            sg[u] = find_seg(g.chk_off, nseg, e);
-            ent[u] = pt[(int64_t)g.seg_a[sg[u]] * stride + (e - g.chk_off[sg[u]])];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * NTH;
-            if (e >= g.n_chk) continue;
-            const int s = sg[u], j = e - g.chk_off[s], r = g.seg_r[s];
-            int bad = 0;
-            if (j < 2 * r) {
-                if (ent[u] == -1) bad = DEV_ERR_TABLE;
-                else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad = DEV_ERR_PAGE;
-            } else if (ent[u] != -1) {
-                bad = DEV_ERR_TABLE;
-            }
-            if (bad) {
-                atomicOr(&g.seg_bad[s], bad);
-                err |= bad;
-            }
-            if (j >= r && j < 2 * r) {   // a B page: give it to every sorted position of the segment
-                for (int q = g.seg_off[s]; q < g.seg_off[s + 1]; ++q) spages[(int64_t)q * RP + (j - r)] = ent[u];
-            }
-        }
-    }
-    __syncthreads();
-    const int p = threadIdx.x;
-    if (p < T) {
-        const int32_t tt = g.sorted[p];
-        int32_t a = -1, r = 0;
-        if (p < g.n_valid) {
-            const int s = find_seg(g.seg_off, nseg, p);
-            if (!g.seg_bad[s]) {
-                a = g.seg_a[s];
-                r = g.seg_r[s];
-            }
-        }
-        sorted_tok[p] = int4{tt, a, r, 0};
-    }
-    if (err) atomicOr(err_word, err);
 }
 
 // ---- wave-level grouping helpers for the T <= 64 kernel (lane = token) --------------------------------
@@ -687,133 +489,6 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     }
 }
 
-// ---- decode, 64 < T <= 256: shrink workgroups + base workgroups side by side ---------------------------
-template <int MB, int WM>
-__global__ __launch_bounds__(256, 2) void k_decode_main(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
-    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
-    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
-    int32_t T, int32_t H, int32_t n_shrink, int32_t RP, float *__restrict__ vpart, int4 *__restrict__ sorted_tok,
-    int32_t *__restrict__ spages, float *__restrict__ ypart, int *__restrict__ err_word) {
-    extern __shared__ __align__(16) char lds_raw[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-
-    if ((int)blockIdx.x < n_shrink) {
-        // ------------------------------------------------------------ shrink role
-        DecGroup &g = *reinterpret_cast<DecGroup *>(lds_raw);
-        const int err = dec_group<256>(g, ids, ranks, T, max_adapters, max_rank, stride);
-        if (blockIdx.x == 0) dec_publish<256>(g, err, pt, stride, num_pages, T, RP, sorted_tok, spages, err_word);
-        const int nseg = g.n_seg;
-        const int nw = n_shrink * 4;
-        for (int i = blockIdx.x * 4 + wave; i < g.n_items; i += nw) {
-            const int s = find_seg(g.item_off, nseg, i);
-            const int32_t r = g.seg_r[s], a = g.seg_a[s];
-            const int local = i - g.item_off[s];
-            const int chunk = local / r, j = local % r;
-            const int32_t page = pt[(int64_t)a * stride + j];
-            if (page < 0 || (int64_t)page >= num_pages) continue;   // reported by workgroup 0
-            const int n = min(CHUNK, g.seg_n[s] - chunk * CHUNK);
-            int32_t tok[CHUNK];
-#pragma unroll
-            for (int u = 0; u < CHUNK; ++u) tok[u] = u < n ? g.sorted[g.seg_off[s] + chunk * CHUNK + u] : 0;
-            shrink_page_wave<2>((const char *)x, (const char *)(pages + (int64_t)page * H), (int64_t)H * 2, tok, n,
-                                scale[a], j, vpart, RP, lane);
-        }
-        return;
-    }
-
-    // ---------------------------------------------------------------- base role
-    constexpr int WK = 4 / WM;
-    constexpr int TP = WM * MB * 16;   // padded rows
-    float *red = reinterpret_cast<float *>(lds_raw);   // [WK][TP][NT]
-    const int b = blockIdx.x - n_shrink;
-    const int n_tiles = H / NT;
-    const int tile = b % n_tiles, split = b / n_tiles;
-    const int S = (gridDim.x - n_shrink) / n_tiles;
-    const int wm = wave % WM, wk = wave / WM;
-    const int n0 = tile * NT;
-    const int G = S * WK, gi = split * WK + wk;
-    const int ksteps = H / 32;
-    const int kb = (int)((int64_t)ksteps * gi / G) * 32, ke = (int)((int64_t)ksteps * (gi + 1) / G) * 32;
-
-    f32x4_t acc[MB][NB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int lrow = lane & 15, lk = (lane >> 4) * 8;
-    const uint16_t *xrow[MB];
-    bool xval[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        const int row = (wm * MB + m) * 16 + lrow;
-        xval[m] = row < T;
-        xrow[m] = x + (int64_t)(xval[m] ? row : 0) * H + lk;
-    }
-    const uint16_t *wrow[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) wrow[nb] = W + (int64_t)(n0 + nb * 16 + lrow) * H + lk;
-
-    constexpr int U = 2;   // K-steps of 32 in flight per wave
-    int k = kb;
-    for (; k + 32 * U <= ke; k += 32 * U) {
-        u32x4_t xa[U][MB], wb[U][NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) wb[u][nb] = load16(wrow[nb] + k + 32 * u);
-#pragma unroll
-            for (int m = 0; m < MB; ++m) xa[u][m] = xval[m] ? load16(xrow[m] + k + 32 * u) : u32x4_t{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[u][m]),
-                                                                         __builtin_bit_cast(bf16x8_t, wb[u][nb]),
-                                                                         acc[m][nb], 0, 0, 0);
-    }
-    for (; k < ke; k += 32) {
-        u32x4_t xa[MB], wb[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wb[nb] = load16(wrow[nb] + k);
-#pragma unroll
-        for (int m = 0; m < MB; ++m) xa[m] = xval[m] ? load16(xrow[m] + k) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[m]),
-                                                                     __builtin_bit_cast(bf16x8_t, wb[nb]),
-                                                                     acc[m][nb], 0, 0, 0);
-    }
-    float *mine = red + (size_t)wk * TP * NT;
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                mine[((wm * MB + m) * 16 + (lane >> 4) * 4 + i) * NT + nb * 16 + (lane & 15)] = acc[m][nb][i];
-    __syncthreads();
-    for (int p = threadIdx.x; p < T * (NT / 8); p += 256) {
-        const int t = p / (NT / 8), c = (p % (NT / 8)) * 8;
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
-        for (int q = 0; q < WK; ++q) {
-            const float *src = red + ((size_t)q * TP + t) * NT + c;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += src[e];
-        }
-        float *dst = ypart + ((int64_t)split * T + t) * H + n0 + c;
-        *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
-    }
-}
-
 // ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
 // Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Thread -> (token i of the
 // group, 8 columns c, quarter q of j: j in [16 q, 16 q + 16)).  Two dependent round trips:
@@ -999,21 +674,6 @@ static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const Ws &
     return hipGetLastError();
 }
 
-template <int MB, int WM>
-static hipError_t launch_main(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                              const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
-                              hipStream_t s) {
-    constexpr int WK = 4 / WM;
-    const size_t red = (size_t)WK * WM * MB * 16 * NT * sizeof(float);
-    const size_t lds = red > sizeof(DecGroup) ? red : sizeof(DecGroup);
-    dim3 grid(plan.n_shrink + plan.n_tiles * plan.ysplit);
-    hipLaunchKernelGGL((k_decode_main<MB, WM>), grid, dim3(256), lds, s, (const uint16_t *)x, (const uint16_t *)W,
-                       (const uint16_t *)p->pages, p->num_pages, pt, 2 * p->max_rank, ids, ranks, scale,
-                       p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.n_shrink, plan.rp, ws.v,
-                       (int4 *)ws.sorted_tok, ws.spages, ws.ypart, p->dev_err);
-    return hipGetLastError();
-}
-
 template <int SY, int SV>
 static void launch_finish_t(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
     dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8));
@@ -1022,7 +682,7 @@ static void launch_finish_t(const lora_pool *p, const Plan &plan, const Ws &ws, 
 }
 
 static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
-    const int sy = plan.ysplit, sv = plan.stream ? plan.ysplit : 1;
+    const int sy = plan.ysplit, sv = plan.ysplit;   // both decode kernels write S v partials
     switch (sy * 16 + sv) {
 #define LP_CASE(A, B) case A * 16 + B: launch_finish_t<A, B>(p, plan, ws, y, s); break;
         LP_CASE(1, 1) LP_CASE(2, 1) LP_CASE(4, 1) LP_CASE(8, 1)
@@ -1048,15 +708,7 @@ hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, con
             default: return hipErrorInvalidValue;
         }
     } else {
-        switch (plan.wm * 8 + plan.mb) {
-            case 2 * 8 + 4: e = launch_main<4, 2>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            case 4 * 8 + 4: e = launch_main<4, 4>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            case 1 * 8 + 1: e = launch_main<1, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            case 1 * 8 + 2: e = launch_main<2, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            case 1 * 8 + 3: e = launch_main<3, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            case 1 * 8 + 4: e = launch_main<4, 1>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
-            default: return hipErrorInvalidValue;
-        }
+        e = launch_decode_wide(p, plan, ws, x, W, ids, ranks, pt, scale, s);
     }
     if (e != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;

@@ -1,0 +1,444 @@
+// Decode-shaped projection for 64 < T <= 256 tokens: one streaming pass over W, x and the batch's A
+// pages, then k_decode_finish (split partials + expand + rounding).
+//
+// ("S-LoRA, in depth", section "Merge or keep adapters separate": x W batched over all tokens whatever
+// their adapter, plus two thin low-rank products per adapter; section "Kernels for a batch of mixed
+// ranks": low-rank work follows tokens and ranks, adapter traffic follows distinct adapters.)
+//
+// Grid: n_tiles column tiles of 64 x S splits of K (chunks of 64), 256 threads.  Wave w owns columns
+// 16 w + [0, 16) of its tile for every token:
+//  * x: the split's K range streams through LDS in chunks of [TP rows][64], loaded straight from
+//    global memory into LDS (three stages); every wave reads every row of a chunk;
+//  * W: the wave's 16 columns as MFMA operands straight into registers, DW K steps in flight;
+//  * the shrink: work units (adapter segment, 16 of its A pages, 16 of its tokens) dealt round robin
+//    over the waves of all tiles; a unit's operands are its page rows (registers, like W) and its
+//    tokens' x rows, gathered from the LDS chunk by row index.  So the A pages of the batch are read
+//    once per call and x A costs one MFMA per unit and K step.
+// The grouping of tokens by adapter (segments in order of first token, tokens in order within a
+// segment) is worked out by every workgroup from the ids, deterministically, so all agree.
+// Outputs as the T <= 64 kernel: float32 partials of x W (ypart[split]) and of s x A
+// (vpart[t][j][split]); the workgroups that own a segment check its page-table row and publish its
+// sorted-token records and B page ids for the finishing kernel.
+#include "device_common.h"
+#include "internal.h"
+
+namespace lorapool {
+namespace wide {
+
+constexpr int WT = 256;       // most tokens (thread t holds token t during the grouping)
+constexpr int KC = 64;        // K chunk staged in LDS: two MFMA steps of 32
+constexpr int NSTAGE = 3;     // x chunk stages
+constexpr int DW = 8;         // K steps of W and page loads in flight per wave
+constexpr int UPW = 4;        // shrink units per wave and pass
+constexpr int HSLOTS = 512;   // grouping hash slots
+
+struct WideGroup {
+    int32_t hkey[HSLOTS];
+    unsigned long long hmask[HSLOTS][4];   // tokens holding the slot's key, one bit each
+    int32_t slot_seg[HSLOTS];
+    int32_t seg_a[WT], seg_r[WT], seg_n[WT], seg_toff[WT + 1], seg_uoff[WT + 1];
+    int32_t sorted[WT];                     // sorted position -> token
+    int32_t pub_ent[2 * 64 + 1];           // page-table row of the segment being published
+    int32_t wsum[3][4];
+    int32_t pub_bad, nseg, nvalid, nunits;
+};
+
+__device__ __forceinline__ int wswz(int r, int p) { return r * KC + ((p ^ ((r >> 1) & 7)) << 3); }
+
+// LDS-only barrier: a full __syncthreads would also wait for every outstanding global load
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// last index s in [0, n) with off[s] <= i (off ascending, off[0] = 0)
+__device__ __forceinline__ int last_leq(const int32_t *off, int n, int32_t i) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace wide
+using namespace wide;
+
+template <int MB16>
+__global__ __launch_bounds__(256, 1) void k_decode_wide(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
+    int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
+    float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
+    int *__restrict__ err_word) {
+    constexpr int TP = MB16 * 16;           // padded token rows
+    constexpr int XSTAGE = TP * KC;         // elements per x stage
+    constexpr int D = TP / 32;              // x chunk loads per wave (1 KiB each)
+    constexpr int LPS = 1 + UPW;            // global loads per K step per wave (W + units)
+    extern __shared__ __align__(16) char lds_raw[];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds_raw);
+    WideGroup &g = *reinterpret_cast<WideGroup *>(lds_raw + (size_t)NSTAGE * XSTAGE * 2);
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lrow = lane & 15, lq = lane >> 4;
+    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+
+    // XCD-aware order (consecutive workgroups go to the 8 XCDs in turn): the splits are spread over
+    // XCDs, so each XCD's L2 holds one or two K ranges of x
+    int tile, split;
+    if ((gridDim.x & 7) == 0 && 8 % S == 0) {
+        const int per = 8 / S;
+        split = (blockIdx.x & 7) / per;
+        tile = (blockIdx.x >> 3) * per + (blockIdx.x & 7) % per;
+    } else {
+        tile = blockIdx.x % n_tiles;
+        split = blockIdx.x / n_tiles;
+    }
+    const int nck = H / KC;
+    const int c0 = (int)((int64_t)nck * split / S), nch = (int)((int64_t)nck * (split + 1) / S) - c0;
+    const int kb = c0 * KC, nst = 2 * nch;   // K steps of 32 of this workgroup
+    const int n0 = tile * 64;
+
+    // ---- x chunks: one load fills 8 rows x 128 bytes of a stage; lane l lands in row 8c + l / 8,
+    // slot l % 8, which holds piece (l % 8) ^ ((row >> 1) & 7) -- the piece the lane fetches.  Rows
+    // past T read row T - 1 (never stored).  Chunks past the split's range reload chunk 0 (never read).
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, T * H * 2, 0x00020000);
+    uint32_t xoff[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        const int r = 8 * (4 * i + wave) + (lane >> 3), p = (lane & 7) ^ ((r >> 1) & 7);
+        xoff[i] = (uint32_t)(min(r, T - 1) * H + kb + p * 8) * 2u;
+    }
+    auto dma_x = [&](int c, int stage) {
+        const int soff = (c < nch ? c : 0) * KC * 2;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+            lds_load16(rx, (lds_void *)(xs + stage * XSTAGE + 8 * (4 * i + wave) * KC), xoff[i], soff);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- ids first (the first wait is for them alone), then x chunks 0 and 1 and the first W steps:
+    // their first touches overlap the grouping's round trips
+    const int32_t a_raw = tid < T ? ids[tid] : -1;
+    __builtin_amdgcn_sched_barrier(0);
+    dma_x(0, 0);
+    dma_x(1, 1);
+    const uint16_t *wr = W + (int64_t)(n0 + 16 * wave + lrow) * H + kb + lq * 8;
+    u32x4_t wv[DW];
+#pragma unroll
+    for (int i = 0; i < DW; ++i) wv[i] = load16(wr + 32 * min(i, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- validate the ids and ranks; key = adapter of a token with a nonzero rank, else -1
+    const int32_t rr = ranks[a_raw >= 0 && a_raw < max_adapters ? a_raw : 0];
+    for (int i = tid; i < HSLOTS; i += 256) {
+        g.hkey[i] = -1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) g.hmask[i][w] = 0ull;
+    }
+    if (tid == 0) g.pub_bad = 0;
+    int err = 0;
+    int32_t key = -1, r_tok = 0;
+    if (tid < T && a_raw != -1) {
+        if (a_raw < -1 || a_raw >= max_adapters) err |= DEV_ERR_ID;
+        else if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
+        else if (rr > 0) { key = a_raw; r_tok = rr; }
+    }
+    lds_sync();
+
+    // ---- grouping: each key claims a hash slot; every token sets its bit in the slot's mask (the
+    // masks do not depend on the order of the atomics, so every workgroup derives the same grouping)
+    int slot = 0;
+    if (key >= 0) {
+        uint32_t h = ((uint32_t)key * 0x9E3779B1u) >> 23;
+        for (int probe = 0; probe < HSLOTS; ++probe) {
+            const int32_t old = atomicCAS(&g.hkey[h], -1, key);
+            if (old == -1 || old == key) break;
+            h = (h + 1) & (HSLOTS - 1);
+        }
+        slot = (int)h;
+        atomicOr(&g.hmask[slot][tid >> 6], 1ull << (tid & 63));
+    }
+    lds_sync();
+    int first = tid, rank_in = 0, cnt = 0;
+    if (key >= 0) {
+        unsigned long long m[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m[w] = g.hmask[slot][w];
+        first = -1;
+#pragma unroll
+        for (int w = 3; w >= 0; --w)
+            if (m[w]) first = 64 * w + __ffsll((unsigned long long)m[w]) - 1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            cnt += __popcll(m[w]);
+            rank_in += w < (tid >> 6) ? __popcll(m[w]) : w == (tid >> 6) ? __popcll(m[w] & ((1ull << (tid & 63)) - 1ull)) : 0;
+        }
+    }
+    const int is_first = key >= 0 && first == tid;
+    // segment ids in order of first token (exclusive scan over the tokens)
+    int nseg;
+    {
+        const int incl = wave_incl_scan(is_first, lane);
+        if (lane == 63) g.wsum[0][wave] = incl;
+        lds_sync();
+        int before = 0;
+        nseg = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int s = g.wsum[0][w];
+            before += w < wave ? s : 0;
+            nseg += s;
+        }
+        if (is_first) {
+            const int sid = before + incl - 1;
+            g.slot_seg[slot] = sid;
+            g.seg_a[sid] = key;
+            g.seg_r[sid] = r_tok;
+            g.seg_n[sid] = cnt;
+        }
+    }
+    lds_sync();
+    const int my_seg = key >= 0 ? g.slot_seg[slot] : -1;
+    // per segment (thread s): first sorted position and first unit; per token: rank among the
+    // ungrouped tokens
+    {
+        const bool sl = tid < nseg;
+        const int n_s = sl ? g.seg_n[tid] : 0, r_s = sl ? g.seg_r[tid] : 0;
+        const int u_s = ((r_s + 15) >> 4) * ((n_s + 15) >> 4);
+        const int ungrouped = tid < T && key < 0;
+        const int i0 = wave_incl_scan(n_s, lane), i1 = wave_incl_scan(u_s, lane), i2 = wave_incl_scan(ungrouped, lane);
+        if (lane == 63) {
+            g.wsum[0][wave] = i0;
+            g.wsum[1][wave] = i1;
+            g.wsum[2][wave] = i2;
+        }
+        lds_sync();
+        int b0 = 0, b1 = 0, b2 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            b0 += w < wave ? g.wsum[0][w] : 0;
+            b1 += w < wave ? g.wsum[1][w] : 0;
+            b2 += w < wave ? g.wsum[2][w] : 0;
+            t0 += g.wsum[0][w];
+            t1 += g.wsum[1][w];
+        }
+        if (sl) {
+            g.seg_toff[tid] = b0 + i0 - n_s;
+            g.seg_uoff[tid] = b1 + i1 - u_s;
+        }
+        if (tid == 0) {
+            g.seg_toff[nseg] = t0;
+            g.seg_uoff[nseg] = t1;
+            g.nvalid = t0;
+            g.nunits = t1;
+        }
+        lds_sync();
+        if (tid < T) g.sorted[key >= 0 ? g.seg_toff[my_seg] + rank_in : t0 + b2 + i2 - ungrouped] = tid;
+        lds_sync();
+    }
+    const int nvalid = g.nvalid, nunits = g.nunits;
+
+    f32x4_t acc[MB16];
+#pragma unroll
+    for (int m = 0; m < MB16; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- passes over the split's K range: pass 0 carries W and the first 4 n_tiles UPW units, further
+    // passes (more units than that: not at H >= 4096) only units, with W's operand zeroed
+    const int cap = 4 * n_tiles * UPW;
+    const int npass = max(1, (nunits + cap - 1) / cap);
+    for (int pass = 0; pass < npass; ++pass) {
+        if (pass > 0) {
+            dma_x(0, 0);
+            dma_x(1, 1);
+#pragma unroll
+            for (int i = 0; i < DW; ++i) wv[i] = load16(wr + 32 * min(i, nst - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const bool with_w = pass == 0;
+        // this wave's units: u = pass cap + 4 tile + wave + 4 n_tiles e (uniform per wave)
+        int32_t u_seg[UPW], u_pb[UPW], u_tc[UPW];
+        bool u_live[UPW];
+        const uint16_t *upr[UPW];
+        int u_row[UPW];
+        float u_sc[UPW];
+#pragma unroll
+        for (int e = 0; e < UPW; ++e) {
+            const int u = pass * cap + 4 * tile + wave + 4 * n_tiles * e;
+            u_live[e] = u < nunits;
+            const int s = u_live[e] ? last_leq(g.seg_uoff, nseg, u) : 0;
+            const int32_t a = g.seg_a[s], rs = g.seg_r[s], ns = g.seg_n[s], to = g.seg_toff[s];
+            const int ntc = (ns + 15) >> 4, local = u - g.seg_uoff[s];
+            u_seg[e] = s;
+            u_pb[e] = u_live[e] ? local / ntc : 0;
+            u_tc[e] = u_live[e] ? local % ntc : 0;
+            const int j = u_pb[e] * 16 + lrow, it = u_tc[e] * 16 + lrow;
+            u_row[e] = g.sorted[u_live[e] ? to + min(it, ns - 1) : 0];
+            const int32_t pid = pt[u_live[e] && j < rs ? (int64_t)a * stride + j : 0];
+            const bool pok = u_live[e] && j < rs && pid >= 0 && (int64_t)pid < num_pages;
+            upr[e] = pok ? pages + (int64_t)pid * H + kb + lq * 8 : x + lq * 8;
+            u_sc[e] = scale[u_live[e] ? a : 0];
+        }
+        u32x4_t pv[UPW][DW];
+#pragma unroll
+        for (int i = 0; i < DW; ++i)
+#pragma unroll
+            for (int e = 0; e < UPW; ++e) pv[e][i] = load16(upr[e] + 32 * min(i, nst - 1));
+        f32x4_t uacc[UPW];
+#pragma unroll
+        for (int e = 0; e < UPW; ++e) uacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // x chunks 0, 1 and the first steps have landed
+        lds_sync();
+
+        // ---- K loop: DW steps per round (the ring of loads in flight is indexed statically)
+        for (int st0 = 0; st0 < nst; st0 += DW) {
+#pragma unroll
+            for (int i = 0; i < DW; ++i) {
+                const int st = st0 + i;
+                const int c = st >> 1;                  // chunk of this step
+                if ((i & 1) == 0) dma_x(c + 2, (c + 2) % NSTAGE);   // into the stage read by chunk c - 1
+                const bool sl = st < nst;
+                const uint16_t *stg = xs + (c % NSTAGE) * XSTAGE;
+                const int pc = (i & 1) * 4 + lq;        // 16-byte piece of the row for this lane
+                const u32x4_t wb = sl && with_w ? wv[i] : zero;
+                u32x4_t pb[UPW];
+#pragma unroll
+                for (int e = 0; e < UPW; ++e) pb[e] = sl && u_live[e] ? pv[e][i] : zero;
+                // the loads of step st + DW refill this slot of the ring
+                const int sn = min(st + DW, nst - 1);
+                wv[i] = load16(wr + 32 * sn);
+#pragma unroll
+                for (int e = 0; e < UPW; ++e) pv[e][i] = load16(upr[e] + 32 * sn);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < MB16; ++m) {
+                    const u32x4_t xa = load16(stg + wswz(m * 16 + lrow, pc));
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                                     __builtin_bit_cast(bf16x8_t, wb), acc[m], 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < UPW; ++e) {
+                    const u32x4_t xa = load16(stg + wswz(u_row[e], pc));
+                    uacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                                      __builtin_bit_cast(bf16x8_t, pb[e]), uacc[e], 0, 0, 0);
+                }
+                if (i & 1) {
+                    // end of chunk c: this wave's loads of chunk c + 1 have landed -- younger than them
+                    // are the two steps of loads of chunk c - 1's half after them, the loads of chunk
+                    // c + 2 and chunk c's two steps of loads
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D + 4 * LPS) : "memory");
+                    lds_sync();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads past the end have landed
+        lds_sync();
+
+        // ---- units: s v partials of this split (tokens and pages past the segment are dropped; a
+        // segment whose page-table row is bad is dropped by the finishing kernel)
+#pragma unroll
+        for (int e = 0; e < UPW; ++e) {
+            if (!u_live[e]) continue;
+            const int s = u_seg[e];
+            const int32_t rs = g.seg_r[s], ns = g.seg_n[s], to = g.seg_toff[s];
+            const int j = u_pb[e] * 16 + lrow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int it = u_tc[e] * 16 + 4 * lq + i;
+                if (j < rs && it < ns) {
+                    const int t = g.sorted[to + it];
+                    vpart[((int64_t)t * RP + j) * S + split] = u_sc[e] * uacc[e][i];
+                }
+            }
+        }
+    }
+
+    // ---- x W partial of this split: lane holds column 16 wave + lrow, rows 16 m + 4 lq + i
+#pragma unroll
+    for (int m = 0; m < MB16; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = m * 16 + 4 * lq + i;
+            if (t < T) ypart[((int64_t)split * T + t) * H + n0 + 16 * wave + lrow] = acc[m][i];
+        }
+
+    // ---- publish: segments s = blockIdx.x + k gridDim.x -- check the page-table row (exactly 2r pages
+    // in range, -1 after), then write the segment's sorted-token records and B page ids; workgroup 0
+    // also writes the ungrouped tokens and reports the id / rank faults every workgroup saw
+    for (int s = blockIdx.x; s < nseg; s += gridDim.x) {
+        const int32_t a = g.seg_a[s], rs = g.seg_r[s], q0 = g.seg_toff[s], qn = g.seg_n[s];
+        const int lim = min(2 * rs + 1, stride);
+        if (tid < lim) {
+            const int32_t ent = pt[(int64_t)a * stride + tid];
+            int bad = 0;
+            if (tid < 2 * rs) {
+                if (ent == -1) bad = DEV_ERR_TABLE;
+                else if (ent < 0 || (int64_t)ent >= num_pages) bad = DEV_ERR_PAGE;
+            } else if (ent != -1) {
+                bad = DEV_ERR_TABLE;
+            }
+            g.pub_ent[tid] = ent;
+            if (bad) atomicOr(&g.pub_bad, bad);
+        }
+        lds_sync();
+        const int bad = g.pub_bad;
+        for (int idx = tid; idx < qn * rs; idx += 256) {
+            const int q = idx / rs, j = idx % rs;
+            spages[(int64_t)(q0 + q) * RP + j] = g.pub_ent[rs + j];
+        }
+        for (int q = tid; q < qn; q += 256)
+            sorted_tok[q0 + q] = int4{g.sorted[q0 + q], bad ? -1 : a, bad ? 0 : rs, 0};
+        if (tid == 0 && bad) atomicOr(err_word, bad);
+        lds_sync();
+        if (tid == 0) g.pub_bad = 0;
+        lds_sync();
+    }
+    if (blockIdx.x == 0) {
+        for (int q = nvalid + tid; q < T; q += 256) sorted_tok[q] = int4{g.sorted[q], -1, 0, 0};
+        const unsigned long long any = __ballot(err != 0);
+        if (any) {
+            for (int off = 32; off > 0; off >>= 1) err |= __shfl_xor(err, off, 64);
+            if (lane == 0) atomicOr(err_word, err);
+        }
+    }
+}
+
+size_t decode_wide_lds(int mb16) { return (size_t)NSTAGE * mb16 * 16 * KC * 2 + sizeof(WideGroup); }
+
+template <int MB16>
+static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
+                                const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
+                                hipStream_t s) {
+    static bool attr_set = false;
+    const size_t lds = decode_wide_lds(MB16);
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_decode_wide<MB16>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    dim3 grid((unsigned)(plan.n_tiles * plan.ysplit));
+    hipLaunchKernelGGL((k_decode_wide<MB16>), grid, dim3(256), lds, s, (const uint16_t *)x, (const uint16_t *)W,
+                       (const uint16_t *)p->pages, p->num_pages, pt, 2 * p->max_rank, ids, ranks, scale,
+                       p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.ysplit, plan.n_tiles, plan.rp,
+                       ws.ypart, ws.v, (int4 *)ws.sorted_tok, ws.spages, p->dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
+                              const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
+                              hipStream_t s) {
+    switch (plan.mb) {
+        case 8: return launch_wide_t<8>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
+        case 12: return launch_wide_t<12>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
+        case 16: return launch_wide_t<16>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lorapool

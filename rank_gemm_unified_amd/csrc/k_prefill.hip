@@ -214,8 +214,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             uint16_t *dst = stage + 8 * (PF_WAVES * i + wave) * BK;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)dst, 16, offa[i], soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(dst + BM * BK), 16, offb[i], soff, 0, 0);
+            lds_load16(rx, (lds_void *)dst, offa[i], soff);
+            lds_load16(rw, (lds_void *)(dst + BM * BK), offb[i], soff);
         }
     };
     const int frow = lane & 31, fk = (lane >> 5) * 8;   // 32x32x16 operand: row lane%32, k 8*(lane/32)

@@ -51,23 +51,13 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
             const int64_t q = (ksteps + 4 * S - 1) / (4 * S);
             pl->ks = q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : 8;
         } else {
+            // k_decode_wide: 64-column tiles x S splits of K (chunks of 64) towards 256 workgroups;
+            // 16-row blocks for every token in each wave
             pl->stream = 0;
-            if (T <= 64) {
-                pl->wm = 1;
-                pl->mb = (int32_t)std::max<int64_t>(1, (T + 15) / 16);
-            } else if (T <= 128) {
-                pl->wm = 2;
-                pl->mb = 4;
-            } else {
-                pl->wm = 4;
-                pl->mb = 4;
-            }
+            pl->mb = T <= 128 ? 8 : T <= 192 ? 12 : 16;
             pl->n_tiles = (int32_t)(H / 64);
-            // splits of K so that the base workgroups cover the 256 CUs: a power of two in [1, 8]
-            int32_t sp = 1;
-            while (sp < 8 && (int64_t)pl->n_tiles * sp < 256) sp *= 2;
-            pl->ysplit = sp;
-            pl->n_shrink = (int32_t)std::min<int64_t>(256, std::max<int64_t>(16, 8 * T));
+            const int64_t nck = H / 64;
+            pl->ysplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({256 / pl->n_tiles, nck, 8}));
         }
     } else if (pl->path == PATH_PREFILL) {
         pl->vsplit = 8;
@@ -85,7 +75,7 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     pl->off_item_row = take((size_t)pl->n_items_max * 4);
     pl->off_ctrl = take(CTRL_WORDS * 4);
     pl->off_counters = take((size_t)std::max(pl->n_counters, 1) * 4);
-    const int64_t sv = pl->path == PATH_DECODE && pl->stream ? pl->ysplit : 1;
+    const int64_t sv = pl->path == PATH_DECODE ? pl->ysplit : 1;
     pl->off_v = take(pl->path == PATH_F32 ? (size_t)T * R * 4 : (size_t)pl->vsplit * T * pl->rp * sv * 4);
     pl->off_ypart = take(pl->path == PATH_DECODE ? (size_t)pl->ysplit * T * H * 4 : 0);
     pl->off_sorted_tok = take(pl->path == PATH_DECODE ? (size_t)T * 16 : 0);
