@@ -5,15 +5,17 @@
 // their adapter, plus two thin low-rank products per adapter; section "Kernels for a batch of mixed
 // ranks": low-rank work follows tokens and ranks, adapter traffic follows distinct adapters.)
 //
-// Grid: n_tiles column tiles of 64 x S splits of K (chunks of 64), 256 threads.  Wave w owns columns
-// 16 w + [0, 16) of its tile for every token:
-//  * x: the split's K range streams through LDS in chunks of [TP rows][64], loaded straight from
-//    global memory into LDS (three stages); every wave reads every row of a chunk;
-//  * W: the wave's 16 columns as MFMA operands straight into registers, DW K steps in flight;
+// Grid: n_tiles column tiles of 64 x S splits of K (chunks of 64), 512 threads (two waves per SIMD,
+// so one feeds the MFMA pipe while the other waits for LDS).  Wave w owns rows 16 MBW w + [0, 16 MBW)
+// (its tokens) x all 64 columns of the tile:
+//  * x and W: the split's K range streams through LDS in chunks of 64 (x: [TP rows][64], three
+//    stages; W: the tile's [64 rows][64], five stages, as it comes from HBM), loaded straight from
+//    global memory into LDS, row-contiguous; each wave reads its own x rows and the chunk's W rows;
 //  * the shrink: work units (adapter segment, 16 of its A pages, 16 of its tokens) dealt round robin
-//    over the waves of all tiles; a unit's operands are its page rows (registers, like W) and its
-//    tokens' x rows, gathered from the LDS chunk by row index.  So the A pages of the batch are read
-//    once per call and x A costs one MFMA per unit and K step.
+//    over the waves of all tiles; a unit's operands are its page rows (MFMA operands straight into
+//    registers, DW K steps in flight) and its tokens' x rows, gathered from the LDS chunk by row
+//    index.  So the A pages of the batch are read once per call and x A costs one MFMA per unit and
+//    K step.
 // The grouping of tokens by adapter (segments in order of first token, tokens in order within a
 // segment) is worked out by every workgroup from the ids, deterministically, so all agree.
 // Outputs as the T <= 64 kernel: float32 partials of x W (ypart[split]) and of s x A
@@ -27,10 +29,17 @@ namespace wide {
 
 constexpr int WT = 256;       // most tokens (thread t holds token t during the grouping)
 constexpr int KC = 64;        // K chunk staged in LDS: two MFMA steps of 32
-constexpr int NSTAGE = 3;     // x chunk stages
-constexpr int DW = 8;         // K steps of W and page loads in flight per wave
-constexpr int UPW = 4;        // shrink units per wave and pass
-constexpr int HSLOTS = 512;   // grouping hash slots
+constexpr int NSTAGE = 3;     // x chunk stages (x chunk c + 2 loads while c computes; x sits in L2)
+constexpr int NWS = 5;        // W chunk stages (W chunk c + 4 loads while c computes; W comes from HBM)
+constexpr int DW = 8;         // K steps of page loads in flight per wave
+#ifndef WIDE_UPW
+#define WIDE_UPW 1
+#endif
+constexpr int UPW = WIDE_UPW;  // shrink units per wave and pass
+constexpr int HSLOTS = 256;   // grouping hash slots (at most 256 keys); the hash keeps 8 bits
+static_assert(HSLOTS == 256, "hash width");
+constexpr int NW = 8;         // waves, one share of the rows each (two per SIMD)
+constexpr int NTH = NW * 64;
 
 struct WideGroup {
     int32_t hkey[HSLOTS];
@@ -39,7 +48,7 @@ struct WideGroup {
     int32_t seg_a[WT], seg_r[WT], seg_n[WT], seg_toff[WT + 1], seg_uoff[WT + 1];
     int32_t sorted[WT];                     // sorted position -> token
     int32_t pub_ent[2 * 64 + 1];           // page-table row of the segment being published
-    int32_t wsum[3][4];
+    int32_t wsum[3][NW];
     int32_t pub_bad, nseg, nvalid, nunits;
 };
 
@@ -66,7 +75,7 @@ __device__ __forceinline__ int last_leq(const int32_t *off, int n, int32_t i) {
 using namespace wide;
 
 template <int MB16>
-__global__ __launch_bounds__(256, 1) void k_decode_wide(
+__global__ __launch_bounds__(NTH, 1) void k_decode_wide(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
@@ -74,14 +83,20 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
     float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
     int *__restrict__ err_word) {
     constexpr int TP = MB16 * 16;           // padded token rows
+    constexpr int MBW = MB16 / NW;          // 16-row blocks per wave
     constexpr int XSTAGE = TP * KC;         // elements per x stage
-    constexpr int D = TP / 32;              // x chunk loads per wave (1 KiB each)
-    constexpr int LPS = 1 + UPW;            // global loads per K step per wave (W + units)
+    constexpr int WSTAGE = 64 * KC;         // elements per W stage
+    constexpr int DX = TP / 64;             // x chunk loads per wave (1 KiB each)
+    constexpr int DWL = 64 / 64;            // W chunk loads per wave
+    constexpr int LPS = UPW;                // page loads per K step per wave
+    static_assert(MB16 % NW == 0, "rows per wave");
     extern __shared__ __align__(16) char lds_raw[];
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds_raw);
-    WideGroup &g = *reinterpret_cast<WideGroup *>(lds_raw + (size_t)NSTAGE * XSTAGE * 2);
+    uint16_t *wst = xs + NSTAGE * XSTAGE;
+    WideGroup &g = *reinterpret_cast<WideGroup *>(lds_raw + (size_t)(NSTAGE * XSTAGE + NWS * WSTAGE) * 2);
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lrow = lane & 15, lq = lane >> 4;
+    const bool tokt = tid < WT;                // threads 0..255 hold one token each in the grouping
     const u32x4_t zero = u32x4_t{0, 0, 0, 0};
 
     // XCD-aware order (consecutive workgroups go to the 8 XCDs in turn): the splits are spread over
@@ -100,41 +115,52 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
     const int kb = c0 * KC, nst = 2 * nch;   // K steps of 32 of this workgroup
     const int n0 = tile * 64;
 
-    // ---- x chunks: one load fills 8 rows x 128 bytes of a stage; lane l lands in row 8c + l / 8,
-    // slot l % 8, which holds piece (l % 8) ^ ((row >> 1) & 7) -- the piece the lane fetches.  Rows
-    // past T read row T - 1 (never stored).  Chunks past the split's range reload chunk 0 (never read).
+    // ---- chunks: one load fills 8 rows x 128 bytes of a stage; lane l lands in row 8c + l / 8, slot
+    // l % 8, which holds piece (l % 8) ^ ((row >> 1) & 7) -- the piece the lane fetches.  x rows past T
+    // read row T - 1 (never stored); W row n is W's row n0 + n.  Chunks past the split's range reload
+    // chunk 0 (never read).
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, T * H * 2, 0x00020000);
-    uint32_t xoff[D];
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (int64_t)n0 * H), (short)0, 64 * H * 2, 0x00020000);
+    uint32_t xoff[DX], woff;
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-        const int r = 8 * (4 * i + wave) + (lane >> 3), p = (lane & 7) ^ ((r >> 1) & 7);
+    for (int i = 0; i < DX; ++i) {
+        const int r = 8 * (NW * i + wave) + (lane >> 3), p = (lane & 7) ^ ((r >> 1) & 7);
         xoff[i] = (uint32_t)(min(r, T - 1) * H + kb + p * 8) * 2u;
     }
-    auto dma_x = [&](int c, int stage) {
+    {
+        const int r = 8 * wave + (lane >> 3), p = (lane & 7) ^ ((r >> 1) & 7);
+        woff = (uint32_t)(r * H + kb + p * 8) * 2u;
+    }
+    auto dma_x = [&](int c) {
         const int soff = (c < nch ? c : 0) * KC * 2;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < D; ++i)
-            lds_load16(rx, (lds_void *)(xs + stage * XSTAGE + 8 * (4 * i + wave) * KC), xoff[i], soff);
+        for (int i = 0; i < DX; ++i)
+            lds_load16(rx, (lds_void *)(xs + (c % NSTAGE) * XSTAGE + 8 * (NW * i + wave) * KC), xoff[i], soff);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto dma_w = [&](int c) {
+        const int soff = (c < nch ? c : 0) * KC * 2;
+        __builtin_amdgcn_sched_barrier(0);
+        lds_load16(rw, (lds_void *)(wst + (c % NWS) * WSTAGE + 8 * wave * KC), woff, soff);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- ids first (the first wait is for them alone), then x chunks 0 and 1 and the first W steps:
-    // their first touches overlap the grouping's round trips
-    const int32_t a_raw = tid < T ? ids[tid] : -1;
+    // ---- ids first (the first wait is for them alone), then the first chunks: their first touches
+    // overlap the grouping's round trips
+    const int32_t a_raw = tid < T && tid < WT ? ids[tid] : -1;
     __builtin_amdgcn_sched_barrier(0);
-    dma_x(0, 0);
-    dma_x(1, 1);
-    const uint16_t *wr = W + (int64_t)(n0 + 16 * wave + lrow) * H + kb + lq * 8;
-    u32x4_t wv[DW];
 #pragma unroll
-    for (int i = 0; i < DW; ++i) wv[i] = load16(wr + 32 * min(i, nst - 1));
+    for (int c = 0; c < NWS; ++c) dma_w(c);
+#pragma unroll
+    for (int c = 0; c < NSTAGE; ++c) dma_x(c);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- validate the ids and ranks; key = adapter of a token with a nonzero rank, else -1
     const int32_t rr = ranks[a_raw >= 0 && a_raw < max_adapters ? a_raw : 0];
-    for (int i = tid; i < HSLOTS; i += 256) {
+    for (int i = tid; i < HSLOTS; i += NTH) {
         g.hkey[i] = -1;
 #pragma unroll
         for (int w = 0; w < 4; ++w) g.hmask[i][w] = 0ull;
@@ -142,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
     if (tid == 0) g.pub_bad = 0;
     int err = 0;
     int32_t key = -1, r_tok = 0;
-    if (tid < T && a_raw != -1) {
+    if (tokt && tid < T && a_raw != -1) {
         if (a_raw < -1 || a_raw >= max_adapters) err |= DEV_ERR_ID;
         else if (rr < 0 || rr > max_rank) err |= DEV_ERR_RANK;
         else if (rr > 0) { key = a_raw; r_tok = rr; }
@@ -153,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
     // masks do not depend on the order of the atomics, so every workgroup derives the same grouping)
     int slot = 0;
     if (key >= 0) {
-        uint32_t h = ((uint32_t)key * 0x9E3779B1u) >> 23;
+        uint32_t h = ((uint32_t)key * 0x9E3779B1u) >> 24;   // 8 bits: HSLOTS = 256
         for (int probe = 0; probe < HSLOTS; ++probe) {
             const int32_t old = atomicCAS(&g.hkey[h], -1, key);
             if (old == -1 || old == key) break;
@@ -188,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         int before = 0;
         nseg = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const int s = g.wsum[0][w];
             before += w < wave ? s : 0;
             nseg += s;
@@ -206,10 +232,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
     // per segment (thread s): first sorted position and first unit; per token: rank among the
     // ungrouped tokens
     {
-        const bool sl = tid < nseg;
+        const bool sl = tokt && tid < nseg;
         const int n_s = sl ? g.seg_n[tid] : 0, r_s = sl ? g.seg_r[tid] : 0;
         const int u_s = ((r_s + 15) >> 4) * ((n_s + 15) >> 4);
-        const int ungrouped = tid < T && key < 0;
+        const int ungrouped = tokt && tid < T && key < 0;
         const int i0 = wave_incl_scan(n_s, lane), i1 = wave_incl_scan(u_s, lane), i2 = wave_incl_scan(ungrouped, lane);
         if (lane == 63) {
             g.wsum[0][wave] = i0;
@@ -219,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         lds_sync();
         int b0 = 0, b1 = 0, b2 = 0, t0 = 0, t1 = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             b0 += w < wave ? g.wsum[0][w] : 0;
             b1 += w < wave ? g.wsum[1][w] : 0;
             b2 += w < wave ? g.wsum[2][w] : 0;
@@ -237,29 +263,31 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
             g.nunits = t1;
         }
         lds_sync();
-        if (tid < T) g.sorted[key >= 0 ? g.seg_toff[my_seg] + rank_in : t0 + b2 + i2 - ungrouped] = tid;
+        if (tokt && tid < T) g.sorted[key >= 0 ? g.seg_toff[my_seg] + rank_in : t0 + b2 + i2 - ungrouped] = tid;
         lds_sync();
     }
     const int nvalid = g.nvalid, nunits = g.nunits;
 
-    f32x4_t acc[MB16];
+    f32x4_t acc[MBW][4];
 #pragma unroll
-    for (int m = 0; m < MB16; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MBW; ++m)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ---- passes over the split's K range: pass 0 carries W and the first 4 n_tiles UPW units, further
+    // ---- passes over the split's K range: pass 0 carries W and the first NW n_tiles UPW units, further
     // passes (more units than that: not at H >= 4096) only units, with W's operand zeroed
-    const int cap = 4 * n_tiles * UPW;
+    const int cap = NW * n_tiles * UPW;
     const int npass = max(1, (nunits + cap - 1) / cap);
     for (int pass = 0; pass < npass; ++pass) {
         if (pass > 0) {
-            dma_x(0, 0);
-            dma_x(1, 1);
 #pragma unroll
-            for (int i = 0; i < DW; ++i) wv[i] = load16(wr + 32 * min(i, nst - 1));
+            for (int c = 0; c < NWS; ++c) dma_w(c);
+#pragma unroll
+            for (int c = 0; c < NSTAGE; ++c) dma_x(c);
             __builtin_amdgcn_sched_barrier(0);
         }
         const bool with_w = pass == 0;
-        // this wave's units: u = pass cap + 4 tile + wave + 4 n_tiles e (uniform per wave)
+        // this wave's units: u = pass cap + NW tile + wave + NW n_tiles e (uniform per wave)
         int32_t u_seg[UPW], u_pb[UPW], u_tc[UPW];
         bool u_live[UPW];
         const uint16_t *upr[UPW];
@@ -267,7 +295,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         float u_sc[UPW];
 #pragma unroll
         for (int e = 0; e < UPW; ++e) {
-            const int u = pass * cap + 4 * tile + wave + 4 * n_tiles * e;
+            const int u = pass * cap + NW * tile + wave + NW * n_tiles * e;
             u_live[e] = u < nunits;
             const int s = u_live[e] ? last_leq(g.seg_uoff, nseg, u) : 0;
             const int32_t a = g.seg_a[s], rs = g.seg_r[s], ns = g.seg_n[s], to = g.seg_toff[s];
@@ -290,47 +318,71 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         f32x4_t uacc[UPW];
 #pragma unroll
         for (int e = 0; e < UPW; ++e) uacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // x chunks 0, 1 and the first steps have landed
+        // the first chunks have landed (the DW UPW page loads just issued are the only younger ones)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DW * UPW) : "memory");
         lds_sync();
 
-        // ---- K loop: DW steps per round (the ring of loads in flight is indexed statically)
+        // ---- K loop, in chunks of two steps of 32.  A chunk's one barrier sits between its steps: before
+        // it each wave has read both halves of its operands from the chunk's stages and waited for its
+        // loads of chunk c + 1; after it the stages of chunk c are free, so they refill with chunks
+        // c + NSTAGE (x) and c + NWS (W) while the second step's MFMAs run and the next chunk's first
+        // operands are read -- no MFMA waits for LDS at a chunk boundary.  DW steps per round (the
+        // ring of page loads in flight is indexed statically).
+        u32x4_t wf[2][4], xf[2][MBW], uf[2][UPW];
+        auto frags = [&](int c, int half, u32x4_t *wfo, u32x4_t *xfo, u32x4_t *ufo) {
+            const uint16_t *stg = xs + (c % NSTAGE) * XSTAGE, *wsg = wst + (c % NWS) * WSTAGE;
+            const int pc = half * 4 + lq;           // 16-byte piece of the row for this lane
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) wfo[nb] = load16(wsg + wswz(16 * nb + lrow, pc));
+#pragma unroll
+            for (int m = 0; m < MBW; ++m) xfo[m] = load16(stg + wswz((wave * MBW + m) * 16 + lrow, pc));
+#pragma unroll
+            for (int e = 0; e < UPW; ++e) ufo[e] = load16(stg + wswz(u_row[e], pc));
+        };
+        frags(0, 0, wf[0], xf[0], uf[0]);
         for (int st0 = 0; st0 < nst; st0 += DW) {
 #pragma unroll
             for (int i = 0; i < DW; ++i) {
-                const int st = st0 + i;
-                const int c = st >> 1;                  // chunk of this step
-                if ((i & 1) == 0) dma_x(c + 2, (c + 2) % NSTAGE);   // into the stage read by chunk c - 1
+                const int st = st0 + i, c = st >> 1, h = i & 1;
                 const bool sl = st < nst;
-                const uint16_t *stg = xs + (c % NSTAGE) * XSTAGE;
-                const int pc = (i & 1) * 4 + lq;        // 16-byte piece of the row for this lane
-                const u32x4_t wb = sl && with_w ? wv[i] : zero;
                 u32x4_t pb[UPW];
 #pragma unroll
                 for (int e = 0; e < UPW; ++e) pb[e] = sl && u_live[e] ? pv[e][i] : zero;
                 // the loads of step st + DW refill this slot of the ring
                 const int sn = min(st + DW, nst - 1);
-                wv[i] = load16(wr + 32 * sn);
 #pragma unroll
                 for (int e = 0; e < UPW; ++e) pv[e][i] = load16(upr[e] + 32 * sn);
+                if (h == 1) {   // chunk c's stages are free: refill them
+                    dma_w(c + NWS);
+                    dma_x(c + NSTAGE);
+                }
                 __builtin_amdgcn_sched_barrier(0);
+                if (h == 0) frags(c, 1, wf[1], xf[1], uf[1]);
+                else frags(c + 1, 0, wf[0], xf[0], uf[0]);
+                const bool wl = sl && with_w;   // steps past the range and unit-only passes add nothing to x W
 #pragma unroll
-                for (int m = 0; m < MB16; ++m) {
-                    const u32x4_t xa = load16(stg + wswz(m * 16 + lrow, pc));
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
-                                                                     __builtin_bit_cast(bf16x8_t, wb), acc[m], 0, 0, 0);
-                }
+                for (int m = 0; m < MBW; ++m)
 #pragma unroll
-                for (int e = 0; e < UPW; ++e) {
-                    const u32x4_t xa = load16(stg + wswz(u_row[e], pc));
-                    uacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xf[h][m]), __builtin_bit_cast(bf16x8_t, wl ? wf[h][nb] : zero),
+                            acc[m][nb], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < UPW; ++e)
+                    uacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, uf[h][e]),
                                                                       __builtin_bit_cast(bf16x8_t, pb[e]), uacc[e], 0, 0, 0);
+#pragma unroll
+                for (int g2 = 0; g2 < MBW * 4 + UPW; ++g2) {   // one operand read after each MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (g2 < 4 + MBW + UPW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-                if (i & 1) {
-                    // end of chunk c: this wave's loads of chunk c + 1 have landed -- younger than them
-                    // are the two steps of loads of chunk c - 1's half after them, the loads of chunk
-                    // c + 2 and chunk c's two steps of loads
+                if (h == 0) {
+                    // mid-chunk: this wave's loads of x chunk c + 1 (and of the older W chunk c + 1) have
+                    // landed.  x chunk c + 1 went out last in chunk c + 1 - NSTAGE; younger are, for
+                    // each chunk between, its two steps of page loads and its W and x loads, and this
+                    // chunk's first step of page loads
                     __builtin_amdgcn_sched_barrier(0);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D + 4 * LPS) : "memory");
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * (2 * LPS + DWL + DX) + LPS) : "memory");
                     lds_sync();
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -358,14 +410,16 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         }
     }
 
-    // ---- x W partial of this split: lane holds column 16 wave + lrow, rows 16 m + 4 lq + i
+    // ---- x W partial of this split: lane holds column 16 nb + lrow, rows 16 (wave MBW + m) + 4 lq + i
 #pragma unroll
-    for (int m = 0; m < MB16; ++m)
+    for (int m = 0; m < MBW; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = m * 16 + 4 * lq + i;
-            if (t < T) ypart[((int64_t)split * T + t) * H + n0 + 16 * wave + lrow] = acc[m][i];
-        }
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = (wave * MBW + m) * 16 + 4 * lq + i;
+                if (t < T) ypart[((int64_t)split * T + t) * H + n0 + 16 * nb + lrow] = acc[m][nb][i];
+            }
 
     // ---- publish: segments s = blockIdx.x + k gridDim.x -- check the page-table row (exactly 2r pages
     // in range, -1 after), then write the segment's sorted-token records and B page ids; workgroup 0
@@ -387,11 +441,11 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         }
         lds_sync();
         const int bad = g.pub_bad;
-        for (int idx = tid; idx < qn * rs; idx += 256) {
+        for (int idx = tid; idx < qn * rs; idx += NTH) {
             const int q = idx / rs, j = idx % rs;
             spages[(int64_t)(q0 + q) * RP + j] = g.pub_ent[rs + j];
         }
-        for (int q = tid; q < qn; q += 256)
+        for (int q = tid; q < qn; q += NTH)
             sorted_tok[q0 + q] = int4{g.sorted[q0 + q], bad ? -1 : a, bad ? 0 : rs, 0};
         if (tid == 0 && bad) atomicOr(err_word, bad);
         lds_sync();
@@ -399,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
         lds_sync();
     }
     if (blockIdx.x == 0) {
-        for (int q = nvalid + tid; q < T; q += 256) sorted_tok[q] = int4{g.sorted[q], -1, 0, 0};
+        for (int q = nvalid + tid; q < T; q += NTH) sorted_tok[q] = int4{g.sorted[q], -1, 0, 0};
         const unsigned long long any = __ballot(err != 0);
         if (any) {
             for (int off = 32; off > 0; off >>= 1) err |= __shfl_xor(err, off, 64);
@@ -408,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_wide(
     }
 }
 
-size_t decode_wide_lds(int mb16) { return (size_t)NSTAGE * mb16 * 16 * KC * 2 + sizeof(WideGroup); }
+size_t decode_wide_lds(int mb16) { return (size_t)(NSTAGE * mb16 * 16 + NWS * 64) * KC * 2 + sizeof(WideGroup); }
 
 template <int MB16>
 static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
@@ -423,7 +477,7 @@ static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const Ws &
         attr_set = true;
     }
     dim3 grid((unsigned)(plan.n_tiles * plan.ysplit));
-    hipLaunchKernelGGL((k_decode_wide<MB16>), grid, dim3(256), lds, s, (const uint16_t *)x, (const uint16_t *)W,
+    hipLaunchKernelGGL((k_decode_wide<MB16>), grid, dim3(NTH), lds, s, (const uint16_t *)x, (const uint16_t *)W,
                        (const uint16_t *)p->pages, p->num_pages, pt, 2 * p->max_rank, ids, ranks, scale,
                        p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.ysplit, plan.n_tiles, plan.rp,
                        ws.ypart, ws.v, (int4 *)ws.sorted_tok, ws.spages, p->dev_err);
@@ -435,7 +489,6 @@ hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const Ws &ws
                               hipStream_t s) {
     switch (plan.mb) {
         case 8: return launch_wide_t<8>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
-        case 12: return launch_wide_t<12>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
         case 16: return launch_wide_t<16>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
         default: return hipErrorInvalidValue;
     }

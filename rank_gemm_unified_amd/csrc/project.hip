@@ -52,9 +52,9 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
             pl->ks = q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : 8;
         } else {
             // k_decode_wide: 64-column tiles x S splits of K (chunks of 64) towards 256 workgroups;
-            // 16-row blocks for every token in each wave
+            // 16-row blocks of tokens (one or two per wave)
             pl->stream = 0;
-            pl->mb = T <= 128 ? 8 : T <= 192 ? 12 : 16;
+            pl->mb = T <= 128 ? 8 : 16;
             pl->n_tiles = (int32_t)(H / 64);
             const int64_t nck = H / 64;
             pl->ysplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({256 / pl->n_tiles, nck, 8}));
