@@ -501,8 +501,8 @@ template <int SY, int SV>
 __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ sorted_tok,
                                                        const int32_t *__restrict__ spages,
                                                        const float *__restrict__ ypart, const float *__restrict__ vpart,
-                                                       int32_t RP, const uint16_t *__restrict__ pages, int32_t H,
-                                                       int32_t T, uint16_t *__restrict__ y) {
+                                                       int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
+                                                       int32_t H, int32_t T, uint16_t *__restrict__ y) {
     constexpr int SQ = (SY + 3) / 4;   // x W splits per quarter thread
     __shared__ float s_v[8][64];
     const int n0 = blockIdx.x * 64;
@@ -523,17 +523,23 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
             pid[4 * u + 3] = v4.w;
         }
     }
-    const int t = st.x, a = live_tok ? st.y : -1;
+    // The records were written (and their page ids checked) by the first kernel; the token index and
+    // the page ids are clamped here all the same, so that a workspace overwritten by another call
+    // can only give wrong values, never an address outside the buffers.
+    const int t = min(max(st.x, 0), T - 1), a = live_tok ? st.y : -1;
     const bool has = a >= 0;
     const int r = has ? st.z : 0;
     const int j0 = 16 * q;
     const bool qlive = has && j0 < r;
     // ---- round trip 2 (every load unconditional, stand-in addresses for dead entries)
     u32x4_t bv[16];
+    uint32_t okm = 0;   // rows whose page id is in range
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int32_t pg = qlive && j0 + u < r ? pid[u] : pid[0];
-        bv[u] = load16(pages + (int64_t)(qlive ? pg : 0) * H + n0 + c);
+        const bool pok = pg >= 0 && (int64_t)pg < num_pages;
+        okm |= pok ? 1u << u : 0u;
+        bv[u] = load16(pages + (int64_t)(qlive && pok ? pg : 0) * H + n0 + c);
     }
     f32x4_t part[SQ][2];
 #pragma unroll
@@ -580,7 +586,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-        const bool lu = qlive && j0 + u < r;
+        const bool lu = qlive && j0 + u < r && ((okm >> u) & 1u);
         float bf[8];
         unpack_bf16x8(lu ? bv[u] : zero, bf);
         const float w = lu ? s_v[i][j0 + u] : 0.f;
@@ -678,7 +684,8 @@ template <int SY, int SV>
 static void launch_finish_t(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
     dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8));
     hipLaunchKernelGGL((k_decode_finish<SY, SV>), grid, dim3(256), 0, s, (const int4 *)ws.sorted_tok, ws.spages,
-                       ws.ypart, ws.v, plan.rp, (const uint16_t *)p->pages, p->hidden, (int32_t)plan.T, (uint16_t *)y);
+                       ws.ypart, ws.v, plan.rp, (const uint16_t *)p->pages, p->num_pages, p->hidden, (int32_t)plan.T,
+                       (uint16_t *)y);
 }
 
 static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {

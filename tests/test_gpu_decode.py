@@ -99,6 +99,25 @@ def test_decode_shapes_integer_exact(T):
     assert torch.equal(y.cpu().view(torch.int16), bf16_round_f64(ref).view(torch.int16))
 
 
+def test_decode_wide_multipass_integer_exact():
+    """The T > 64 kernel deals its shrink work units (adapter segment, 16 pages, 16 tokens) over the
+    waves of all its workgroups; at H = 128 one pass holds 16 units, so 40 adapters of ranks 1..64
+    over 200 tokens take several passes over K.  Integer-valued inputs: the output must equal the
+    oracle's exact result rounded once, bit for bit."""
+    rng = np.random.default_rng(40)
+    ranks = [int(r) for r in rng.integers(1, 65, 40)]
+    ids = rng.integers(-1, 40, 200)
+    w = custom(128, ranks, ids, values="int", scales=[1] * 40, device="cuda", seed=40)
+    say("case wide multipass: 40 adapters, T", w.T)
+    pool = device_pool(w)
+    y = run(pool, w, 0)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0
+    ref = oracle_y(w, 0)
+    assert np.all(ref == np.round(ref)) and np.abs(ref).max() < 2 ** 24
+    assert torch.equal(y.cpu().view(torch.int16), bf16_round_f64(ref).view(torch.int16))
+
+
 # (H, T): every K-steps-per-wave variant of the T <= 64 kernel (1, 2, 4, 8), 16-row blocks 1..4,
 # waves with no K steps (H = 64), ragged quarters (192), a split count that is not a divisor of 8
 # (5120: plain workgroup order) and the largest hidden size the kernel takes (8192, 1024 workgroups)
