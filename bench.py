@@ -245,10 +245,10 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "kernel": ("k_decode_stream (W stream + MFMA partials, gathered-A shrink)" if stream_kernel else
-                           "k_decode_main (W stream + MFMA partials, gathered-A shrink)"),
+                           "k_decode_wide (x and W through LDS + MFMA partials, shrink work units)"),
                 "algorithmic_bytes_per_launch": info["decode_first_bytes"], "avg_launch_us": first_us,
-                "traffic": traffic_from_profiles("decode_stream" if stream_kernel else "decode_main",
-                                                 os.path.join(src, "k_decode.hip")),
+                "traffic": (traffic_from_profiles("decode_stream", os.path.join(src, "k_decode.hip")) if stream_kernel
+                            else traffic_from_profiles("decode_wide", os.path.join(src, "k_decode_wide.hip"))),
                 "timing": "HIP events around each launch on its stream, minus the per-interval event cost "
                           f"({event_gap_us:.2f} us, from the event-free timed loop)",
                 "second_kernel": {"kernel": "k_decode_finish (partials + gathered-B expand + rounding)",
