@@ -48,6 +48,10 @@ __device__ __forceinline__ u32x4_t pack_bf16x8(const float *f) {
 
 __device__ __forceinline__ u32x4_t load16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 __device__ __forceinline__ void store16(void *p, const u32x4_t &v) { *reinterpret_cast<u32x4_t *>(p) = v; }
+// A streaming store: the line is not kept in the caches (for large outputs this kernel never reads)
+__device__ __forceinline__ void store16_nt(void *p, const u32x4_t &v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+}
 
 // Sum over the 64 lanes of a wave; every lane gets the total.  Fixed butterfly order, so the
 // result does not depend on anything but the 64 inputs.

@@ -388,9 +388,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
         lowrank(li, pg);
     }
 
-    // ---- one rounding, then the tile goes out through LDS as row-contiguous 16-byte stores.  32x32
-    //      block layout: lane holds column lane%32 and, in register e, row 8*(e/4) + 4*(lane/32) + e%4.
-    //      (The low-rank loop above ends with a barrier, so the LDS is free.)
+    // ---- one rounding, then the tile goes out through LDS as row-contiguous 16-byte streaming stores
+    //      (every tile ends at about the same time; stores that keep their lines in the caches made the
+    //      burst of y about 4 us longer at 4096 x 4096).  32x32 block layout: lane holds column
+    //      lane%32 and, in register e, row 8*(e/4) + 4*(lane/32) + e%4.  (The low-rank loop above ends
+    //      with a barrier, so the LDS is free.)
     constexpr int OS = BN;       // row of the staged tile (elements)
     uint16_t *ot = sm;
 #pragma unroll
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll 4
     for (int u = 0; u < BM * BN / 8 / PF_THREADS; ++u) {
         const int idx = tid + PF_THREADS * u, row = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
-        if (m0 + row < T && n0 + c < H) store16(y + (int64_t)(m0 + row) * H + n0 + c, load16(ot + row * OS + c));
+        if (m0 + row < T && n0 + c < H) store16_nt(y + (int64_t)(m0 + row) * H + n0 + c, load16(ot + row * OS + c));
     }
 }
 
