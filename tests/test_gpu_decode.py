@@ -137,6 +137,43 @@ def test_decode_hidden_sizes(H, T):
     assert rel <= BF16_REL and mx <= BF16_ABS
 
 
+@pytest.mark.parametrize("T", [48, 200])   # the T <= 64 kernel and the T > 64 kernel
+def test_token_order_and_relabelling_bitwise(T):
+    """A token's result depends only on its own x and its adapter.  Permuting the tokens permutes the
+    rows of y; naming the adapters differently (each one's weights, rank and scale moved to its new
+    id) changes nothing.  Both bit for bit."""
+    rng = np.random.default_rng(1000 + T)
+    ranks = [8, 16, 64, 0, 32, 8, 16]
+    ids = rng.integers(-1, len(ranks), T).astype(np.int32)
+    w = custom(512, ranks, ids, device="cuda", seed=1000 + T)
+    say("case order/relabel T", T)
+    pool = device_pool(w)
+    y = run(pool, w, 0)
+    perm = rng.permutation(T)
+    dperm = torch.as_tensor(perm, device="cuda")
+    yp = run(pool, w, 0, ids=ids[perm], x=w.x()[dperm])
+    # the same adapters under other ids, in a fresh pool
+    sigma = rng.permutation(len(ranks))
+    pool2 = rg.Pool(w.num_pages, w.hidden, rg.LORA_BF16, n_slots=1, max_adapters=len(ranks),
+                    max_rank=w.max_rank, free_order=w.free_order)
+    ranks2 = np.zeros(len(ranks), np.int32)
+    scales2 = np.zeros(len(ranks), np.float32)
+    for a in range(len(ranks)):
+        ranks2[sigma[a]] = ranks[a]
+        scales2[sigma[a]] = w.scales[a]
+        at, b = w.adapter(a) if ranks[a] > 0 else (None, None)
+        rg.lora_pool_load_adapter(pool2.handle, int(sigma[a]), int(ranks[a]), at, b)
+    ids2 = np.where(ids >= 0, sigma[np.maximum(ids, 0)], -1).astype(np.int32)
+    y2 = torch.empty_like(y)
+    pool2.project(0, w.x(), w.W(0), torch.as_tensor(ids2, device="cuda"), torch.as_tensor(ranks2, device="cuda"),
+                  torch.as_tensor(scales2, device="cuda"), y=y2)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool2.handle, check=False) == 0
+    assert torch.equal(yp.view(torch.int16), y[dperm].view(torch.int16))
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+    pool2.close()
+
+
 def test_identity_rows_bitwise():
     w = build("decode", device="cuda")
     pool = device_pool(w)
