@@ -19,6 +19,10 @@ typedef __attribute__((address_space(3))) void lds_void;   // an LDS address, as
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void *dst, uint32_t voff, int32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
+// The same from a per-lane 64-bit global address (a gather): lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void lds_gload16(const void *src, lds_void *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

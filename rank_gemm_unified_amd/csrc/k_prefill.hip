@@ -133,7 +133,6 @@ __global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vp
 
 // ---- base GEMM + fused expand --------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDK = BK + 8;                         // padded LDS row (elements) of the low-rank operands
 constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline stage (unpadded, swizzled)
 // 16-byte piece p of row r of a stage sits in slot p ^ ((r >> 1) & 7).  The LDS serves a 16-byte read
 // 16 lanes at a time over 64 banks (256 bytes): two 128-byte rows fill the banks once, so the 16 rows
@@ -141,8 +140,7 @@ constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline sta
 // rows 2i and 2i + 1 share slot p ^ i.  Tile writes (8 lanes per row) are conflict-free either way.
 __device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 7)) << 3); }
 constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
-static_assert((size_t)BM * BN * 2 <= MAIN_LDS && ((size_t)64 * (BN + 8) + (size_t)BM * LDK) * 2 <= MAIN_LDS,
-              "LDS reuse after the K loop");
+static_assert((size_t)BM * BN * 2 <= MAIN_LDS, "output tile staged in LDS after the K loop");
 
 // PF_WAVES waves in a 2 x (PF_WAVES / 2) grid over the 256 x 256 tile; wave (wm, wn) computes rows
 // WTM wm + [0, WTM) x columns WTN wn + [0, WTN) as WMI x WNI blocks of 32 x 32.
@@ -278,23 +276,137 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll
         for (int k = 0; k < LR_K; ++k) pg[k] = prow[min((tid + PF_THREADS * k) >> 5, r - 1)];
     };
-    int32_t pg0[LR_K];
-    if (nlist > 0) lr_pages(0, pg0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    dma(nk > 1 ? 1 : 0, sm + STAGE);
+    int32_t pg0[LR_K] = {};
+    // tile 0 has landed once at most the page-id loads (younger) are in flight; they are first needed
+    // near the end of the K loop
+    if (nlist > 0) {
+        lr_pages(0, pg0);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LR_K) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // The low-rank operands, [x | v_a] [W ; B_a] as extra K for adapter s_list[li], fill one pipeline
+    // stage (64 KiB):
+    //   Bn [64][BN]  B_a's rows j < 64 over the tile's columns; 16-byte piece p of row j sits in slot
+    //                p ^ 4 ((j >> 3) & 1), since one MFMA operand read takes rows j and j + 8;
+    //   Vs [BM][64]  the tile's v rows (the adapter's tokens; zero elsewhere and past the rank), with
+    //                the tile swizzle.
+    // Thread -> piece idx = tid + PF_THREADS k (k < LR_K = LR_V) of each: B row idx / 32, slot idx % 32;
+    // v row idx / 8, slot idx % 8.  The operands of the first adapter are loaded straight into LDS
+    // during the K loop's second-to-last step (into the stage tile nk would have used), so the low-rank
+    // term waits for no round trip (with a single K step they go out with tile 0); further adapters of
+    // the tile load them through registers after it.
+    static_assert(LR_K == LR_V && (size_t)64 * BN + (size_t)BM * 64 <= (size_t)STAGE, "low-rank operands fill one stage");
+    auto bslot = [](int j, int p) { return j * BN + ((p ^ (((j >> 3) & 1) << 2)) << 3); };
+    auto bsrc = [&](const int32_t *pg, int k) {
+        const int idx = tid + PF_THREADS * k, j = idx >> 5, p = (idx & 31) ^ (((j >> 3) & 1) << 2);
+        return pages + (int64_t)pg[k] * H + min(n0 + 8 * p, H - 8);
+    };
+    auto vsrc = [&](int k) {
+        const int idx = tid + PF_THREADS * k, row = idx >> 3, p = (idx & 7) ^ ((row >> 1) & 7);
+        return v16 + (int64_t)min(m0 + row, T - 1) * R + min(8 * p, R - 8);
+    };
+    auto lr_dma = [&](uint16_t *stg) {
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k)
+            lds_gload16(bsrc(pg0, k), (lds_void *)(stg + (PF_THREADS * k + 64 * wave) * 8));
+#pragma unroll
+        for (int k = 0; k < LR_V; ++k)
+            lds_gload16(vsrc(k), (lds_void *)(stg + 64 * BN + (PF_THREADS * k + 64 * wave) * 8));
+    };
+    // each thread clears, in its own pieces, B rows in [r, roundup(r, 16)) and v entries of other
+    // adapters' rows or past r (the pages may hold any bits, NaN included, and 0 * NaN is NaN)
+    auto lr_mask = [&](uint16_t *stg, int li) {
+        const int32_t a = s_list[li], r = s_lr[li], rp = (r + 15) & ~15;
+        const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k) {
+            const int idx = tid + PF_THREADS * k, j = idx >> 5;
+            if (j >= r && j < rp) store16(stg + idx * 8, zero);
+        }
+#pragma unroll
+        for (int k = 0; k < LR_V; ++k) {
+            const int idx = tid + PF_THREADS * k, row = idx >> 3, j0 = 8 * ((idx & 7) ^ ((row >> 1) & 7));
+            uint16_t *q = stg + 64 * BN + idx * 8;
+            if (j0 >= rp) continue;   // never read
+            if (s_key[row] != a || j0 >= r) {
+                store16(q, zero);
+            } else if (j0 + 8 > r) {
+                u32x4_t v = load16(q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = j0 + 2 * e < r ? 0xffffu : 0u, hi = j0 + 2 * e + 1 < r ? 0xffff0000u : 0u;
+                    v[e] &= lo | hi;
+                }
+                store16(q, v);
+            }
+        }
+    };
+    // the K-extension: rp / 16 substeps of 32x32x16 MFMAs on the accumulators; the B operand (8
+    // consecutive j of one column) is gathered with 2-byte reads, lane -> column
+    auto lr_mfma = [&](const uint16_t *stg, int li) {
+        const int32_t rp = (s_lr[li] + 15) & ~15;
+        const uint16_t *Bn = stg, *Vs = stg + 64 * BN;
+        for (int ks = 0; ks < rp / 16; ++ks) {
+            u32x4_t la[WMI], lb[WNI];
+#pragma unroll
+            for (int mi = 0; mi < WMI; ++mi) la[mi] = load16(Vs + swz(wm * WTM + mi * 32 + frow, ks * 2 + (fk >> 3)));
+#pragma unroll
+            for (int ni = 0; ni < WNI; ++ni) {
+                const int col = wn * WTN + ni * 32 + frow, cp = col >> 3, ce = col & 7;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int j = ks * 16 + fk + 2 * w;
+                    lb[ni][w] = (uint32_t)Bn[bslot(j, cp) + ce] | ((uint32_t)Bn[bslot(j + 1, cp) + ce] << 16);
+                }
+            }
+#pragma unroll
+            for (int mi = 0; mi < WMI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < WNI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, la[mi]),
+                                                                          __builtin_bit_cast(bf16x8_t, lb[ni]),
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+    };
+    // the same operands through registers (the caller has made the stage free with a barrier)
+    auto lr_regs = [&](uint16_t *stg, int li, const int32_t *pg) {
+        u32x4_t bv[LR_K], vv[LR_V];
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k) bv[k] = load16(bsrc(pg, k));
+#pragma unroll
+        for (int k = 0; k < LR_V; ++k) vv[k] = load16(vsrc(k));
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k) store16(stg + (tid + PF_THREADS * k) * 8, bv[k]);
+#pragma unroll
+        for (int k = 0; k < LR_V; ++k) store16(stg + 64 * BN + (tid + PF_THREADS * k) * 8, vv[k]);
+        lr_mask(stg, li);   // this thread's own pieces: its LDS accesses are in order
+        __syncthreads();
+        lr_mfma(stg, li);
+        __syncthreads();
+    };
+
+    if (nk > 1) dma(1, sm + STAGE);
+    else lr_dma(sm + STAGE);   // a single K step: stage 1 is the low-rank stage from the start
     frag(sm, 0, af[0], bf[0]);
-    for (int kt = 0; kt < nk; ++kt) {
+    // One K step.  MODE 0: starts the loads of tile kt + 2 in substep 3; MODE 1 (step nk - 2): the
+    // low-rank operands instead; MODE 2 (the last step): no loads, and its barrier waits for none.
+    auto step = [&](int kt, auto mode) {
+        constexpr int MODE = decltype(mode)::value;
         uint16_t *cur = sm + (kt & 1) * STAGE, *oth = sm + ((kt + 1) & 1) * STAGE;
-        const int kt2 = kt + 2 < nk ? kt + 2 : 0;
         __builtin_amdgcn_sched_barrier(0);
         // per k-substep (WMI x WNI MFMAs, operands in buffer ks & 1): the next WMI + WNI fragment reads
-        // into the other buffer and, in substep 3, the 2 DPW loads of tile kt + 2, one after each MFMA
+        // into the other buffer and, in substep 3, the 2 DPW loads, one after each MFMA
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (ks < 3) frag(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-            else frag(oth, 0, af[0], bf[0]);
-            if (ks == 3) dma(kt2, cur);
+            else if (MODE != 2) frag(oth, 0, af[0], bf[0]);
+            if (ks == 3) {
+                if constexpr (MODE == 0) dma(kt + 2, cur);
+                if constexpr (MODE == 1) lr_dma(cur);
+            }
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
@@ -305,87 +417,38 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
 #pragma unroll
             for (int g = 0; g < WMI * WNI; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (g < WMI + WNI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (ks == 3 && g < 2 * DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (g < WMI + WNI && (ks < 3 || MODE != 2)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (ks == 3 && MODE != 2 && g < 2 * DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (ks == 2) {
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                if constexpr (MODE == 2)
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // only the low-rank loads are in flight
+                else
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads have landed: the LDS is reused below
-    __syncthreads();
-
-    // ---- low-rank term: one K-extension per adapter owning rows of this tile.  B_a's rows sit in LDS
-    // as they are in the pages, [j][n] (16-byte writes, one row per 32 lanes); the MFMA B operand (8
-    // consecutive j of one column) is gathered with 2-byte reads, lane -> column, so neither the
-    // writes nor the reads conflict.  Thread -> B row j = idx / 32, columns 8 (idx % 32) + [0, 8) for
-    // idx = tid + PF_THREADS k (k < LR_K); v row tid % BM, entries 8 (LR_V (tid / BM) + k) + [0, 8)
-    // (k < LR_V).
-    constexpr int BNP = BN + 8;
-    uint16_t *Bn = sm;                 // [64][BNP]: B_a rows x the tile's columns
-    uint16_t *Vs = sm + 64 * BNP;      // [BM][LDK]: v rows of this adapter, zero elsewhere
-    auto lowrank = [&](int li, const int32_t *pg) {
-        const int32_t a = s_list[li], r = s_lr[li];
-        const int rp = (r + 15) & ~15;
-        u32x4_t bv[LR_K], vv[LR_V];
-#pragma unroll
-        for (int k = 0; k < LR_K; ++k) {   // stand-in row (the adapter's first) past r, zeroed below
-            const int idx = tid + PF_THREADS * k, j = idx >> 5, c = (idx & 31) * 8;
-            bv[k] = load16(pages + (int64_t)pg[k] * H + min(n0 + c, H - 8));
-            if (!(j < r && n0 + c < H)) bv[k] = u32x4_t{0, 0, 0, 0};
-        }
-        const int vrow = tid % BM, vj = (tid / BM) * LR_V * 8;
-        const bool mine = s_key[vrow] == a;
-#pragma unroll
-        for (int k = 0; k < LR_V; ++k) {
-            const int j = vj + 8 * k;
-            vv[k] = load16(v16 + (int64_t)(mine ? m0 + vrow : m0) * R + min(j, R - 8));
-            if (!mine) vv[k] = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {   // entries j >= r (never written for this token) are cleared
-                const uint32_t lo = j + 2 * e < r ? 0xffffu : 0u, hi = j + 2 * e + 1 < r ? 0xffff0000u : 0u;
-                vv[k][e] &= lo | hi;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < LR_K; ++k) {
-            const int idx = tid + PF_THREADS * k, j = idx >> 5, c = (idx & 31) * 8;
-            if (j < rp) store16(Bn + j * BNP + c, bv[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < LR_V; ++k)
-            if (vj + 8 * k < rp) store16(Vs + vrow * LDK + vj + 8 * k, vv[k]);
-        __syncthreads();
-        for (int ks = 0; ks < rp / 16; ++ks) {
-            u32x4_t af[WMI], bf[WNI];
-#pragma unroll
-            for (int mi = 0; mi < WMI; ++mi) af[mi] = load16(Vs + (wm * WTM + mi * 32 + frow) * LDK + ks * 16 + fk);
-#pragma unroll
-            for (int ni = 0; ni < WNI; ++ni) {
-                const uint16_t *col = Bn + (ks * 16 + fk) * BNP + wn * WTN + ni * 32 + frow;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) bf[ni][w] = (uint32_t)col[2 * w * BNP] | ((uint32_t)col[(2 * w + 1) * BNP] << 16);
-            }
-#pragma unroll
-            for (int mi = 0; mi < WMI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < WNI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[mi]),
-                                                                          __builtin_bit_cast(bf16x8_t, bf[ni]),
-                                                                          acc[mi][ni], 0, 0, 0);
-        }
-        __syncthreads();
     };
-    if (nlist > 0) lowrank(0, pg0);
+    for (int kt = 0; kt + 2 < nk; ++kt) step(kt, std::integral_constant<int, 0>());
+    if (nk >= 2) step(nk - 2, std::integral_constant<int, 1>());
+    step(nk - 1, std::integral_constant<int, 2>());
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every load, the low-rank operands' included, has landed
+
+    // ---- low-rank term: one K-extension per adapter owning rows of this tile
+    if (nlist > 0) {
+        uint16_t *stg = sm + (nk & 1) * STAGE;   // the stage step nk - 2 (or, for one step, the prologue) filled
+        lr_mask(stg, 0);
+        __syncthreads();
+        lr_mfma(stg, 0);
+    }
+    __syncthreads();
     for (int li = 1; li < nlist; ++li) {
         int32_t pg[LR_K];
         lr_pages(li, pg);
-        lowrank(li, pg);
+        lr_regs(sm, li, pg);
     }
 
     // ---- one rounding, then the tile goes out through LDS as row-contiguous 16-byte streaming stores

@@ -101,6 +101,29 @@ def test_prefill_integer_exact(T, H, pieces):
     assert not bad, (bad[:10], ids[bad[:10]])
 
 
+@pytest.mark.parametrize("T,H", [(700, 192), (300, 64)])
+def test_prefill_small_max_rank_integer_exact(T, H):
+    """A pool whose largest rank is 16: v rows hold 16 entries, so the low-rank operand loads clamp
+    inside the row and everything past each adapter's rank (1, 4, 9, 16) is cleared.  Tiles straddle
+    several adapters; H = 64 is a single K step."""
+    rng = np.random.default_rng(T * 7 + H)
+    ranks = [4, 1, 0, 16, 9]
+    ids = _segments(rng, T, len(ranks), 30)
+    w = custom(H, ranks, ids, values="int", scales=[1] * len(ranks), device="cuda", seed=T + 1)
+    w.max_rank = 16
+    say("case prefill max_rank 16", T, H)
+    pool = device_pool(w)
+    y = run(pool, w, 0)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    ref = oracle_y(w, 0)
+    assert np.all(ref == np.round(ref))
+    got = y.cpu().view(torch.int16)
+    want = bf16_round_f64(ref).view(torch.int16)
+    bad = (got != want).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, (bad[:10], ids[bad[:10]])
+
+
 @pytest.mark.parametrize("H", [320, 448, 5120])
 def test_prefill_odd_hidden(H):
     """Hidden sizes that are not a multiple of the 256-column tile, with a mixed batch: prefill
