@@ -437,10 +437,12 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
             v[u] = ((*reinterpret_cast<const f32x4_t *>(q) + *reinterpret_cast<const f32x4_t *>(q + WS)) +
                     *reinterpret_cast<const f32x4_t *>(q + 2 * WS)) + *reinterpret_cast<const f32x4_t *>(q + 3 * WS);
         }
+        // streaming stores: the finishing kernel reads each partial once (measured: 0.2 us less per call
+        // than stores that keep the lines in this XCD's L2)
 #pragma unroll
         for (int u = 0; u < MB; ++u) {
             const int e = threadIdx.x + 256 * u, t = e >> 4;
-            if (t < T) *reinterpret_cast<f32x4_t *>(ypart + ((int64_t)split * T + t) * H + n0 + 4 * (e & 15)) = v[u];
+            if (t < T) __builtin_nontemporal_store(v[u], reinterpret_cast<f32x4_t *>(ypart + ((int64_t)split * T + t) * H + n0 + 4 * (e & 15)));
         }
         page_store(red + TP * RS, WS, PS, plive, pa, pj);
     }
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
         o[e] += __shfl_xor(o[e], 1, 64);
         o[e] += __shfl_xor(o[e], 2, 64);
     }
-    if (q == 0 && live_tok) store16(y + (int64_t)t * H + n0 + c, pack_bf16x8(o));
+    if (q == 0 && live_tok) store16_nt(y + (int64_t)t * H + n0 + c, pack_bf16x8(o));
 }
 
 // ---- float32 pools: grouping kernel + gathered shrink + plain VALU kernel ---------------------------
