@@ -140,7 +140,6 @@ constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline sta
 // rows 2i and 2i + 1 share slot p ^ i.  Tile writes (8 lanes per row) are conflict-free either way.
 __device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 7)) << 3); }
 constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
-static_assert((size_t)BM * BN * 2 <= MAIN_LDS, "output tile staged in LDS after the K loop");
 
 // PF_WAVES waves in a 2 x (PF_WAVES / 2) grid over the 256 x 256 tile; wave (wm, wn) computes rows
 // WTM wm + [0, WTM) x columns WTN wn + [0, WTN) as WMI x WNI blocks of 32 x 32.
@@ -451,13 +450,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
         lr_regs(sm, li, pg);
     }
 
-    // ---- one rounding, then the tile goes out through LDS as row-contiguous 16-byte streaming stores
-    //      (every tile ends at about the same time; stores that keep their lines in the caches made the
-    //      burst of y about 4 us longer at 4096 x 4096).  32x32 block layout: lane holds column
-    //      lane%32 and, in register e, row 8*(e/4) + 4*(lane/32) + e%4.  (The low-rank loop above ends
-    //      with a barrier, so the LDS is free.)
-    constexpr int OS = BN;       // row of the staged tile (elements)
-    uint16_t *ot = sm;
+    // ---- one rounding, and each lane stores its own elements with 2-byte streaming stores (the 32
+    //      lanes of a half-wave cover 64 contiguous bytes of a row).  Every tile ends at about the same
+    //      time, so y (T x H) leaves in one burst at the write rate; stores that keep their lines in
+    //      the caches made it about 4 us longer at 4096 x 4096, and staging the tile through LDS for
+    //      16-byte stores cost 0.5 us more.  32x32 block layout: lane holds column lane%32 and, in
+    //      register e, row 8*(e/4) + 4*(lane/32) + e%4.
 #pragma unroll
     for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
@@ -466,14 +464,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
             for (int e = 0; e < 16; ++e) {
                 const int row = wm * WTM + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
                 const int col = wn * WTN + ni * 32 + (lane & 31);
-                ot[row * OS + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][e]);
+                if (m0 + row < T && n0 + col < H)
+                    __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(acc[mi][ni][e]), y + (int64_t)(m0 + row) * H + n0 + col);
             }
-    __syncthreads();
-#pragma unroll 4
-    for (int u = 0; u < BM * BN / 8 / PF_THREADS; ++u) {
-        const int idx = tid + PF_THREADS * u, row = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
-        if (m0 + row < T && n0 + c < H) store16_nt(y + (int64_t)(m0 + row) * H + n0 + c, load16(ot + row * OS + c));
-    }
 }
 
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
