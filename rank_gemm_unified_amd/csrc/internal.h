@@ -94,7 +94,7 @@ struct Plan {
     int32_t stream;         // decode: 1 = k_decode_stream (T <= 64), 0 = k_decode_wide
     int32_t ks;             // decode streaming kernel: max K steps of 32 per wave (a quarter of a split)
     // byte offsets into the workspace
-    size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row,
+    size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row, off_item_rec,
         off_ctrl, off_counters, off_v, off_ypart, off_sorted_tok, off_v16, off_spages, total;
 };
 
@@ -102,6 +102,7 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *plan);
 
 struct Ws {
     int32_t *tok_a, *tok_r, *perm, *seg_a, *seg_start, *item_seg, *item_row, *ctrl, *counters;
+    int4 *item_rec;         // prefill: per shrink work item {adapter, rank, first sorted row, rows}; adapter -1 past the last
     float *v, *ypart;
     int32_t *sorted_tok;    // decode: int4 {token, adapter or -1, rank, 0} per sorted position
     uint16_t *v16;          // prefill: v = s x A in bfloat16, [T][rp]

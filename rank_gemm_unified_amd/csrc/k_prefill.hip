@@ -20,82 +20,81 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---- shrink ------------------------------------------------------------------------------------
 constexpr int SH_ROWS = 64;   // rows per work item
-constexpr int VSPLIT = 8;     // K-splits of the shrink
+constexpr int VSPLIT = 4;     // K-splits of the shrink
+constexpr int SNS = 6;        // LDS stages of the shrink's K-tile ring (SNS - 1 tiles in flight; 4 and 8 were slower)
 
-// Grid (work items, VSPLIT).  Work item = up to 64 tokens of one adapter segment; split = a K range
-// of H / VSPLIT.  A small tiled GEMM: per K tile of 64, the item's x rows (gathered through perm) and
-// the adapter's A pages (<= 64, one per column of v) go through a double-buffered LDS stage with
-// row-contiguous 16-byte loads; four waves compute 32x32 blocks (rows 32 wm.., pages 32 wn..) with
-// 32x32x16 MFMAs.  Writes float32 partials vpart[split][t][0..r); k_v_finalize adds them in split
-// order.  (No in-kernel cross-workgroup reduction: on this chip a device-scope fence writes back
-// and invalidates the whole L2.)
+// Grid (work items + spare, VSPLIT), 256 threads.  Work item = up to 64 tokens of one adapter
+// segment, read as one record; split = a K range of H / VSPLIT.  A small tiled GEMM: per K tile of
+// 64, the item's x rows (gathered through perm) and the adapter's A pages (<= 64, one per column of
+// v) go from global memory straight into a ring of SNS LDS stages, SNS - 1 tiles ahead (the whole
+// item chain is two round trips: the record, then perm and the page-table row); four waves
+// compute 32x32 blocks (rows 32 wm.., pages 32 wn..) with 32x32x16 MFMAs.  Writes float32 partials
+// vpart[split][t][0..r); k_v_finalize adds them in split order.  (No in-kernel cross-workgroup
+// reduction: on this chip a device-scope fence writes back and invalidates the whole L2.)
 constexpr int SK = 64;                                  // K tile
-constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements
+constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements (16 KiB)
+constexpr size_t SHRINK_LDS = (size_t)SNS * SH_STAGE * 2;
 __device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ ((r >> 1) & 7)) << 3); }   // as swz
 
-__global__ __launch_bounds__(256) void k_shrink_mfma(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H, const int32_t *__restrict__ pt,
-    int32_t stride, const int32_t *__restrict__ perm, const int32_t *__restrict__ seg_a,
-    const int32_t *__restrict__ seg_start, const int32_t *__restrict__ item_seg, const int32_t *__restrict__ item_row,
-    const int32_t *__restrict__ ctrl, const int32_t *__restrict__ tok_r, float *__restrict__ vpart, int32_t T,
-    int32_t R) {
-    const int item = blockIdx.x;
-    if (item >= ctrl[CTRL_NITEMS]) return;
-    __shared__ __align__(16) uint16_t st[2][SH_STAGE];
+__global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages,
+                                                     int32_t H, const int32_t *__restrict__ pt, int32_t stride,
+                                                     const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
+                                                     float *__restrict__ vpart, int32_t T, int32_t R) {
+    const int4 rec = item_rec[blockIdx.x];
+    if (rec.x < 0) return;   // past the last work item
+    extern __shared__ __align__(16) uint16_t st[];   // SNS stages
     __shared__ int32_t s_perm[SH_ROWS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int32_t a = rec.x, r = rec.y, row0 = rec.z, n = rec.w;   // 1 <= r, 1 <= n <= 64
     const int split = blockIdx.y;
-    const int32_t sg = item_seg[item], row0 = item_row[item];
-    const int32_t n = min(seg_start[sg + 1] - row0, SH_ROWS);
-    if (tid < SH_ROWS) s_perm[tid] = perm[row0 + min(tid, n - 1)];
-    const int32_t a = seg_a[sg];
-    const int32_t *prow = pt + (int64_t)a * stride;
-    __syncthreads();
-    const int32_t r = tok_r[s_perm[0]];
     const int ktiles = H / SK;
     const int kt0 = (int)((int64_t)ktiles * split / VSPLIT), kt1 = (int)((int64_t)ktiles * (split + 1) / VSPLIT);
-    // loads: thread -> row tid/8 (+32), 16-byte piece tid%8: x rows 0..63 (gathered), page rows 0..63
-    // (pages j >= r read page j = r - 1: their columns are never stored)
-    const int lr = tid >> 3, lp = tid & 7;
+    // Loads: one fills 1 KiB of a stage, rows 8d .. 8d + 7 (d < 8: x rows, d >= 8: page rows d - 8);
+    // wave w issues d = w, w + 4 (x) and w + 8, w + 12 (pages).  Lane l lands in row 8d + l / 8, slot
+    // l % 8, which holds piece (l % 8) ^ ((row >> 1) & 7): the piece the lane fetches.  x rows past the
+    // item read its last row and pages past r read page r - 1: their products are never stored.
     const uint16_t *src[4];
-    src[0] = x + (int64_t)s_perm[lr] * H + lp * 8;
-    src[1] = x + (int64_t)s_perm[lr + 32] * H + lp * 8;
-    src[2] = pages + (int64_t)prow[min(lr, r - 1)] * H + lp * 8;
-    src[3] = pages + (int64_t)prow[min(lr + 32, r - 1)] * H + lp * 8;
-    u32x4_t rv[4];
-    auto gload = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rv[i] = load16(src[i] + kt * SK);
-    };
-    auto lstore = [&](uint16_t *stg) {
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * (wave + 4 * i) + (lane >> 3), p = (lane & 7) ^ ((row >> 1) & 7);
+        const int32_t tk = perm[row0 + min(row, n - 1)];
+        if ((lane & 7) == 0) s_perm[row] = tk;
+        src[i] = x + (int64_t)tk * H + p * 8;
+        const int32_t pid = pt[(int64_t)a * stride + min(row, r - 1)];   // checked by the grouping kernel
+        src[2 + i] = pages + (int64_t)pid * H + p * 8;
+    }
+    auto dma = [&](int kt, uint16_t *stg) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store16(stg + sswz(lr + 32 * i, lp), rv[i]);
+        for (int i = 0; i < 4; ++i)
+            lds_gload16(src[i] + kt * SK, (lds_void *)(stg + (8 * (wave + 4 * i)) * SK));
     };
+    const int nkt = kt1 - kt0;
+    // SNS - 1 tiles in flight; tiles past the range reload the first (never read)
+#pragma unroll
+    for (int u = 0; u < SNS - 1; ++u) dma(kt0 + (u < nkt ? u : 0), st + u * SH_STAGE);
     const int wm = wave >> 1, wn = wave & 1;
     const int frow = lane & 31, fk = lane >> 5;
     f32x16_t acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    if (kt0 < kt1) {
-        gload(kt0);
-        lstore(st[0]);
-        __syncthreads();
-        for (int kt = kt0; kt < kt1; ++kt) {
-            const int sidx = (kt - kt0) & 1;
-            const bool more = kt + 1 < kt1;
-            if (more) gload(kt + 1);
-            const uint16_t *S = st[sidx];
+    for (int u = 0; u < nkt; ++u) {
+        // tile u has landed once the SNS - 2 younger tiles (4 loads each per wave) may still be in flight
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(4 * (SNS - 2)) : "memory");
+        __builtin_amdgcn_s_barrier();   // every wave's share of tile u is in; tile u - 1 is no longer read
+        asm volatile("" ::: "memory");
+        const int un = u + SNS - 1;
+        dma(kt0 + (un < nkt ? un : 0), st + (un % SNS) * SH_STAGE);
+        const uint16_t *S = st + (u % SNS) * SH_STAGE;
 #pragma unroll
-            for (int ks = 0; ks < SK / 16; ++ks) {
-                const u32x4_t fa = load16(S + sswz(wm * 32 + frow, ks * 2 + fk));
-                const u32x4_t fb = load16(S + sswz(SH_ROWS + wn * 32 + frow, ks * 2 + fk));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa),
-                                                              __builtin_bit_cast(bf16x8_t, fb), acc, 0, 0, 0);
-            }
-            if (more) lstore(st[sidx ^ 1]);
-            __syncthreads();
+        for (int ks = 0; ks < SK / 16; ++ks) {
+            const u32x4_t fa = load16(S + sswz(wm * 32 + frow, ks * 2 + fk));
+            const u32x4_t fb = load16(S + sswz(SH_ROWS + wn * 32 + frow, ks * 2 + fk));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa),
+                                                          __builtin_bit_cast(bf16x8_t, fb), acc, 0, 0, 0);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads have landed before the kernel ends
+    __syncthreads();   // s_perm
     // 32x32 block layout: lane holds column (page) lane%32 and, in register e, row 8 (e/4) + 4 (lane/32) + e%4
     float *vout = vpart + (int64_t)split * T * R;
     const int j = wn * 32 + (lane & 31);
@@ -476,13 +475,14 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
         hipError_t e = hipFuncSetAttribute((const void *)k_prefill_main, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)MAIN_LDS);
         if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)k_shrink_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)SHRINK_LDS);
+        if (e != hipSuccess) return e;
         attr_set = true;
     }
     if (plan.vsplit != VSPLIT) return hipErrorInvalidValue;
     dim3 g1(plan.n_items_max, VSPLIT);
-    hipLaunchKernelGGL(k_shrink_mfma, g1, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)p->pages, p->hidden,
-                       pt, 2 * p->max_rank, ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.ctrl,
-                       ws.tok_r, ws.v, (int32_t)plan.T, plan.rp);
+    hipLaunchKernelGGL(k_shrink_mfma, g1, dim3(256), SHRINK_LDS, s, (const uint16_t *)x, (const uint16_t *)p->pages,
+                       p->hidden, pt, 2 * p->max_rank, ws.perm, ws.item_rec, ws.v, (int32_t)plan.T, plan.rp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nthr = plan.T * (plan.rp / 4);

@@ -100,7 +100,9 @@ __device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int
 //     checked after they arrive (entries [0, 2r) hold pages in range, entry 2r is -1 when 2r < stride).
 // Tokens of an adapter with rank 0, a bad rank or a bad row get no low-rank term.  Segments are in
 // adapter order; tokens of one adapter land in perm in an unspecified order (LDS atomics): no result
-// depends on the order of tokens within a segment.
+// depends on the order of tokens within a segment.  Work items (`chunk` sorted rows of one segment) are
+// written as item_seg / item_row and as one record {adapter, rank, first row, rows} each, with
+// adapter -1 from the last item up to n_items_max, so a kernel reads its item in one load.
 // LDS: cnt | uidx | ulist | rk (max_adapters each) | scratch[3 * 17].
 constexpr int KPT = 8;
 constexpr int32_t F_OFF = 1 << 30;   // cnt flag: the adapter's tokens get no low-rank term
@@ -110,7 +112,8 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     int32_t stride, int32_t T, int32_t max_adapters, int32_t max_rank, int64_t num_pages, int32_t chunk,
     int32_t *__restrict__ tok_a, int32_t *__restrict__ tok_r, int32_t *__restrict__ perm,
     int32_t *__restrict__ seg_a, int32_t *__restrict__ seg_start, int32_t *__restrict__ item_seg,
-    int32_t *__restrict__ item_row, int32_t *__restrict__ ctrl, int32_t *__restrict__ counters,
+    int32_t *__restrict__ item_row, int4 *__restrict__ item_rec, int32_t n_items_max,
+    int32_t *__restrict__ ctrl, int32_t *__restrict__ counters,
     int32_t n_counters, int *__restrict__ err) {
     extern __shared__ int32_t lds[];
     int32_t *cnt = lds, *uidx = lds + max_adapters, *ulist = lds + 2 * max_adapters, *rk = lds + 3 * max_adapters;
@@ -212,9 +215,11 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
             for (int32_t r0 = cnt[a]; r0 < next; r0 += chunk, ++it) {
                 item_seg[it] = sg;
                 item_row[it] = r0;
+                item_rec[it] = int4{a, rk[a], r0, min(next - r0, chunk)};
             }
         }
     }
+    for (int it = nitems + tid; it < n_items_max; it += SEG_THREADS) item_rec[it] = int4{-1, 0, 0, 0};
     if (tid == 0) {
         seg_start[nseg] = nvalid;
         ctrl[CTRL_NSEG] = nseg;
@@ -296,7 +301,8 @@ hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws, c
     }
     hipLaunchKernelGGL(k_segments, dim3(1), dim3(SEG_THREADS), lds, s, ids, ranks, pt, 2 * p->max_rank,
                        (int32_t)plan.T, p->max_adapters, p->max_rank, p->num_pages, plan.chunk, ws.tok_a, ws.tok_r,
-                       ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.ctrl, ws.counters,
+                       ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.item_rec, plan.n_items_max,
+                       ws.ctrl, ws.counters,
                        plan.n_counters, p->dev_err);
     return hipGetLastError();
 }

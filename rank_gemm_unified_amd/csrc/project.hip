@@ -60,7 +60,7 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
             pl->ysplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({256 / pl->n_tiles, nck, 8}));
         }
     } else if (pl->path == PATH_PREFILL) {
-        pl->vsplit = 8;
+        pl->vsplit = 4;
         pl->n_tiles = 0;
     }
     pl->n_counters = 0;   // no kernel uses arrival counters (cross-workgroup sums go through kernel boundaries)
@@ -73,6 +73,7 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     pl->off_seg_start = take((T + 2) * 4);
     pl->off_item_seg = take((size_t)pl->n_items_max * 4);
     pl->off_item_row = take((size_t)pl->n_items_max * 4);
+    pl->off_item_rec = take((size_t)pl->n_items_max * 16);
     pl->off_ctrl = take(CTRL_WORDS * 4);
     pl->off_counters = take((size_t)std::max(pl->n_counters, 1) * 4);
     const int64_t sv = pl->path == PATH_DECODE ? pl->ysplit : 1;
@@ -95,6 +96,7 @@ Ws carve(void *base, const Plan &pl) {
     w.seg_start = (int32_t *)(b + pl.off_seg_start);
     w.item_seg = (int32_t *)(b + pl.off_item_seg);
     w.item_row = (int32_t *)(b + pl.off_item_row);
+    w.item_rec = (int4 *)(b + pl.off_item_rec);
     w.ctrl = (int32_t *)(b + pl.off_ctrl);
     w.counters = (int32_t *)(b + pl.off_counters);
     w.v = (float *)(b + pl.off_v);
