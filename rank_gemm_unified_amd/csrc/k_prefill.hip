@@ -162,17 +162,30 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
-    // tile order: consecutive workgroups go to the 8 XCDs in turn, so (when the tile count allows)
-    // each XCD takes a contiguous run of the order below; the order walks groups of 4 row tiles
-    // across all column tiles, so an XCD's tiles share x rows and W columns in its L2
+    // Tile order.  The first P0 = roundup(n_tiles_n, 8) workgroups take the last row of tiles, one
+    // tile each, spread over the XCDs: when decode rows (one adapter each) follow the prefill rows,
+    // that row holds most of the batch's distinct adapters and the longest low-rank term, so it
+    // starts first (the rest of the grid then runs beside it).  The others go to the 8 XCDs in turn
+    // (consecutive workgroups), each XCD taking a contiguous run of an order that walks groups of 4
+    // row tiles across all column tiles, so an XCD's tiles share x rows and W columns in its L2.
+    // Workgroups past the last tile of either part leave at once.
     int mt, nt;
     {
-        const int n_tiles = gridDim.x, tm = n_tiles / n_tiles_n;
-        const int t = (n_tiles & 7) == 0 ? (blockIdx.x & 7) * (n_tiles >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-        constexpr int GM = 4;
-        const int grp = GM * n_tiles_n, g = t / grp, fm = g * GM, gsz = min(tm - fm, GM);
-        mt = fm + (t % grp) % gsz;
-        nt = (t % grp) / gsz;
+        const int tm = (T + BM - 1) / BM, P0 = (n_tiles_n + 7) / 8 * 8;
+        const int b = blockIdx.x;
+        if (b < P0) {
+            if (b >= n_tiles_n) return;
+            mt = tm - 1;
+            nt = b;
+        } else {
+            const int rest = (tm - 1) * n_tiles_n, G = gridDim.x - P0, b2 = b - P0;   // G: multiple of 8
+            const int t = (b2 & 7) * (G >> 3) + (b2 >> 3);
+            if (t >= rest) return;
+            constexpr int GM = 4;
+            const int grp = GM * n_tiles_n, g = t / grp, fm = g * GM, gsz = min(tm - 1 - fm, GM);
+            mt = fm + (t % grp) % gsz;
+            nt = (t % grp) / gsz;
+        }
     }
     const int m0 = mt * BM, n0 = nt * BN;
 
@@ -491,7 +504,8 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
     const int tn = (p->hidden + BN - 1) / BN, tm = (int)((plan.T + BM - 1) / BM);
-    hipLaunchKernelGGL(k_prefill_main, dim3(tm * tn), dim3(PF_THREADS), MAIN_LDS, s, (const uint16_t *)x, (const uint16_t *)W,
+    const int grid = (tn + 7) / 8 * 8 + ((tm - 1) * tn + 7) / 8 * 8;   // the last row of tiles, then the rest
+    hipLaunchKernelGGL(k_prefill_main, dim3(grid), dim3(PF_THREADS), MAIN_LDS, s, (const uint16_t *)x, (const uint16_t *)W,
                        (const uint16_t *)p->pages, pt, 2 * p->max_rank, ws.tok_a, ws.tok_r, ws.v16,
                        plan.rp, (int32_t)plan.T, p->hidden, tn, (uint16_t *)y);
     return hipGetLastError();
