@@ -39,25 +39,26 @@ __device__ int32_t block_exclusive_scan(int32_t *a, int32_t n, int32_t *scratch)
     return total;
 }
 
-// Wave-aggregated LDS counter update: every lane with key >= 0 adds 1 to cnt[key]; the lanes sharing
-// a key are served by one atomic (issued by the lowest of them), and each gets old + its rank among
-// them.  Returns -1 for lanes with key < 0.  (Tokens of one adapter are mostly neighbours, so a wave
-// holds few distinct keys; per-lane atomics on a handful of counters would serialize.)
+// LDS counter update: every lane with key >= 0 adds 1 to cnt[key] and gets old + its rank among the
+// lanes of its key; -1 for lanes with key < 0.  A wave whose tokens share one key (a prefill run: the
+// usual case) issues one atomic for all of them, since per-lane atomics on one counter serialize; a
+// wave with several keys (decode-style rows, one adapter each) issues one atomic per lane, and lanes
+// sharing a key get distinct slots in an unspecified order (no result depends on the order of tokens
+// within a segment).  Looping over the distinct keys instead cost a few LDS round trips per key.
 __device__ __forceinline__ int32_t wave_add_rank(int32_t *cnt, int32_t key) {
     const int lane = threadIdx.x & 63;
-    int32_t pos = -1;
-    uint64_t remaining = __ballot(key >= 0);
-    while (remaining) {
-        const int leader = __ffsll((unsigned long long)remaining) - 1;
-        const int32_t lkey = __shfl(key, leader, 64);
-        const uint64_t m = __ballot(key == lkey);
+    const uint64_t valid = __ballot(key >= 0);
+    if (!valid) return -1;
+    const int leader = __ffsll((unsigned long long)valid) - 1;
+    const int32_t lkey = __shfl(key, leader, 64);
+    const uint64_t m = __ballot(key == lkey);
+    if (m == valid) {
         int32_t old = 0;
         if (lane == leader) old = atomicAdd(&cnt[lkey], __popcll(m));
         old = __shfl(old, leader, 64);
-        if (key == lkey) pos = old + __popcll(m & ((1ull << lane) - 1ull));
-        remaining &= ~m;
+        return key >= 0 ? old + __popcll(m & ((1ull << lane) - 1ull)) : -1;
     }
-    return pos;
+    return key >= 0 ? atomicAdd(&cnt[key], 1) : -1;
 }
 
 // Exclusive scan of three arrays at once (same layout as block_exclusive_scan); returns the totals.
@@ -104,7 +105,7 @@ __device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int
 // written as item_seg / item_row and as one record {adapter, rank, first row, rows} each, with
 // adapter -1 from the last item up to n_items_max, so a kernel reads its item in one load.
 // LDS: cnt | uidx | ulist | rk (max_adapters each) | scratch[3 * 17].
-constexpr int KPT = 8;
+constexpr int KPT = 16;   // tokens per thread held in registers (T <= 16384 reads the ids once)
 constexpr int32_t F_OFF = 1 << 30;   // cnt flag: the adapter's tokens get no low-rank term
 
 __global__ __launch_bounds__(SEG_THREADS) void k_segments(
@@ -132,11 +133,14 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
 #pragma unroll
     for (int u = 0; u < KPT; ++u) key[u] = -1;
     for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
+        // slots u with t0 + u SEG_THREADS >= T hold no token in any lane: skipped (a uniform test)
         int32_t a[KPT];
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) a[u] = ids[min(t0 + u * SEG_THREADS + tid, T - 1)];
+        for (int u = 0; u < KPT; ++u)
+            if (t0 + u * SEG_THREADS < T) a[u] = ids[min(t0 + u * SEG_THREADS + tid, T - 1)];
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
+            if (t0 + u * SEG_THREADS >= T) break;
             const int t = t0 + u * SEG_THREADS + tid;
             int32_t k = -1;
             if (t < T && a[u] != -1) {
@@ -234,6 +238,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     for (int t0 = 0; t0 < T; t0 += KPT * SEG_THREADS) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
+            if (t0 + u * SEG_THREADS >= T) break;
             const int t = t0 + u * SEG_THREADS + tid;
             int32_t k = t < T ? (cached ? key[u] : tok_a[t]) : -1;
             if (k >= 0 && (k + 1 < max_adapters ? uidx[k + 1] : nseg) == uidx[k]) k = -1;
