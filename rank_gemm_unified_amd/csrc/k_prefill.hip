@@ -21,8 +21,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // ---- shrink ------------------------------------------------------------------------------------
 constexpr int SH_ROWS = 64;   // rows per work item
 constexpr int VSPLIT = 4;     // K-splits of the shrink
-constexpr int SNS = 6;        // LDS stages of the shrink's K-tile ring (SNS - 1 tiles in flight; 4 and 8 were slower)
 
+// SNS LDS stages of 16 KiB form the K-tile ring (SNS - 1 tiles in flight).  Six stages (one
+// workgroup per CU) when the work items fit one round of the chip (T <= 4096), else four (two per
+// CU): measured best at 4096 and at 8448 rows.
+//
 // Grid (work items + spare, VSPLIT), 256 threads.  Work item = up to 64 tokens of one adapter
 // segment, read as one record; split = a K range of H / VSPLIT.  A small tiled GEMM: per K tile of
 // 64, the item's x rows (gathered through perm) and the adapter's A pages (<= 64, one per column of
@@ -33,9 +36,9 @@ constexpr int SNS = 6;        // LDS stages of the shrink's K-tile ring (SNS - 1
 // reduction: on this chip a device-scope fence writes back and invalidates the whole L2.)
 constexpr int SK = 64;                                  // K tile
 constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements (16 KiB)
-constexpr size_t SHRINK_LDS = (size_t)SNS * SH_STAGE * 2;
 __device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ ((r >> 1) & 7)) << 3); }   // as swz
 
+template <int SNS>
 __global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages,
                                                      int32_t H, const int32_t *__restrict__ pt, int32_t stride,
                                                      const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
@@ -488,14 +491,24 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
         hipError_t e = hipFuncSetAttribute((const void *)k_prefill_main, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)MAIN_LDS);
         if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)k_shrink_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)SHRINK_LDS);
+        e = hipFuncSetAttribute((const void *)k_shrink_mfma<6>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(6 * SH_STAGE * 2));
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)k_shrink_mfma<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(4 * SH_STAGE * 2));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     if (plan.vsplit != VSPLIT) return hipErrorInvalidValue;
     dim3 g1(plan.n_items_max, VSPLIT);
-    hipLaunchKernelGGL(k_shrink_mfma, g1, dim3(256), SHRINK_LDS, s, (const uint16_t *)x, (const uint16_t *)p->pages,
-                       p->hidden, pt, 2 * p->max_rank, ws.perm, ws.item_rec, ws.v, (int32_t)plan.T, plan.rp);
+    if (plan.T <= 4096)
+        hipLaunchKernelGGL(k_shrink_mfma<6>, g1, dim3(256), 6 * SH_STAGE * 2, s, (const uint16_t *)x,
+                           (const uint16_t *)p->pages, p->hidden, pt, 2 * p->max_rank, ws.perm, ws.item_rec, ws.v,
+                           (int32_t)plan.T, plan.rp);
+    else
+        hipLaunchKernelGGL(k_shrink_mfma<4>, g1, dim3(256), 4 * SH_STAGE * 2, s, (const uint16_t *)x,
+                           (const uint16_t *)p->pages, p->hidden, pt, 2 * p->max_rank, ws.perm, ws.item_rec, ws.v,
+                           (int32_t)plan.T, plan.rp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nthr = plan.T * (plan.rp / 4);
