@@ -62,12 +62,18 @@ struct lora_pool {
     std::unordered_map<int64_t, std::vector<int64_t>> kv;
     int64_t kv_total = 0, adapter_total = 0;
     int64_t n_loads = 0, n_evictions = 0, bytes_loaded = 0;
-    // library-owned device/host buffers
-    void *staging = nullptr;          // device, staging_bytes
+    // library-owned device/host buffers: a ring of LOAD_RING load buffers, so that a load waits (on
+    // the host) only for the load LOAD_RING calls earlier, never for the one just before it
+    static constexpr int LOAD_RING = 2;
+    struct LoadBuf {
+        void *staging = nullptr;      // device, staging_bytes
+        int32_t *rows_dev = nullptr;  // device, n_slots * 2 * max_rank int32
+        int32_t *rows_host = nullptr; // pinned host, same size
+        hipEvent_t done = nullptr;    // recorded after the load that last used this buffer
+    };
+    LoadBuf load_buf[LOAD_RING];
+    int load_next = 0;
     size_t staging_bytes = 0;
-    int32_t *rows_dev = nullptr;      // device, n_slots * 2 * max_rank int32
-    int32_t *rows_host = nullptr;     // pinned host, same size
-    hipEvent_t staging_done = nullptr;
     int *dev_err = nullptr;           // device error word
     // opt-in per-kernel timing: 4 events per recorded call
     std::vector<hipEvent_t> prof_events;

@@ -53,12 +53,14 @@ static void destroy(lora_pool *p) {
     if (!p) return;
     if (!p->bookkeeping_only) {
         DeviceGuard g(p->device);
-        if (p->staging_done) (void)hipEventSynchronize(p->staging_done);
-        if (p->staging) (void)hipFree(p->staging);
-        if (p->rows_dev) (void)hipFree(p->rows_dev);
+        for (auto &b : p->load_buf) {
+            if (b.done) (void)hipEventSynchronize(b.done);
+            if (b.staging) (void)hipFree(b.staging);
+            if (b.rows_dev) (void)hipFree(b.rows_dev);
+            if (b.rows_host) (void)hipHostFree(b.rows_host);
+            if (b.done) (void)hipEventDestroy(b.done);
+        }
         if (p->dev_err) (void)hipFree(p->dev_err);
-        if (p->rows_host) (void)hipHostFree(p->rows_host);
-        if (p->staging_done) (void)hipEventDestroy(p->staging_done);
         for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
     }
     delete p;
@@ -129,11 +131,16 @@ extern "C" int lora_pool_create(void *pages, int64_t num_pages, int32_t hidden, 
         p->staging_bytes = std::max(slot_bytes, std::min(want, (size_t)64 << 20));
         const size_t rows_bytes = (size_t)n_slots * 2 * max_rank * sizeof(int32_t);
         const size_t pt_bytes = (size_t)n_slots * max_adapters * 2 * max_rank * sizeof(int32_t);
-        if ((e = hipMalloc(&p->staging, p->staging_bytes)) != hipSuccess ||
-            (e = hipMalloc((void **)&p->rows_dev, rows_bytes)) != hipSuccess ||
-            (e = hipMalloc((void **)&p->dev_err, 64)) != hipSuccess ||
-            (e = hipHostMalloc((void **)&p->rows_host, rows_bytes, hipHostMallocDefault)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&p->staging_done, hipEventDisableTiming)) != hipSuccess ||
+        for (auto &b : p->load_buf) {
+            if ((e = hipMalloc(&b.staging, p->staging_bytes)) != hipSuccess ||
+                (e = hipMalloc((void **)&b.rows_dev, rows_bytes)) != hipSuccess ||
+                (e = hipHostMalloc((void **)&b.rows_host, rows_bytes, hipHostMallocDefault)) != hipSuccess ||
+                (e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming)) != hipSuccess) {
+                destroy(p);
+                return hip_error(e, "lora_pool_create load buffers");
+            }
+        }
+        if ((e = hipMalloc((void **)&p->dev_err, 64)) != hipSuccess ||
             (e = hipMemset(p->dev_err, 0, 64)) != hipSuccess ||
             (e = hipMemset(page_table, 0xff, pt_bytes)) != hipSuccess ||
             (e = hipDeviceSynchronize()) != hipSuccess) {
@@ -199,35 +206,38 @@ static int copy_adapter(lora_pool *p, const Adapter &ad, int32_t aid, const void
                         hipStream_t s) {
     DeviceGuard g(p->device);
     const int32_t r = ad.rank, stride = 2 * p->max_rank, H = p->hidden, S = p->n_slots;
-    LP_HIP(hipEventSynchronize(p->staging_done));          // rows_host / staging free again
+    // the next load buffer; the host waits only if the load that used it last is still queued
+    lora_pool::LoadBuf &lb = p->load_buf[p->load_next];
+    p->load_next = (p->load_next + 1) % lora_pool::LOAD_RING;
+    LP_HIP(hipEventSynchronize(lb.done));
     for (int32_t sl = 0; sl < S; ++sl) {
-        int32_t *row = p->rows_host + (size_t)sl * stride;
+        int32_t *row = lb.rows_host + (size_t)sl * stride;
         for (int32_t j = 0; j < stride; ++j)
             row[j] = j < 2 * r ? (int32_t)ad.pages[(size_t)sl * 2 * r + j] : -1;
     }
-    LP_HIP(hipMemcpyAsync(p->rows_dev, p->rows_host, (size_t)S * stride * sizeof(int32_t),
+    LP_HIP(hipMemcpyAsync(lb.rows_dev, lb.rows_host, (size_t)S * stride * sizeof(int32_t),
                           hipMemcpyHostToDevice, s));
     if (r > 0) {
         const size_t block = (size_t)r * H * p->elem;   // one slot's A_t (or B) in bytes
         if (device_pointer(A_t) && device_pointer(B)) {
-            LP_HIP(launch_scatter_rows(p->pages, H, p->elem, A_t, B, (int64_t)r * H, 0, S, r, p->rows_dev,
+            LP_HIP(launch_scatter_rows(p->pages, H, p->elem, A_t, B, (int64_t)r * H, 0, S, r, lb.rows_dev,
                                        stride, s));
         } else {
             const int32_t per = (int32_t)std::max<size_t>(1, p->staging_bytes / (2 * block));
             for (int32_t s0 = 0; s0 < S; s0 += per) {
                 const int32_t n = std::min(per, S - s0);
-                char *stA = (char *)p->staging, *stB = stA + (size_t)n * block;
+                char *stA = (char *)lb.staging, *stB = stA + (size_t)n * block;
                 LP_HIP(hipMemcpyAsync(stA, (const char *)A_t + (size_t)s0 * block, (size_t)n * block,
                                       hipMemcpyDefault, s));
                 LP_HIP(hipMemcpyAsync(stB, (const char *)B + (size_t)s0 * block, (size_t)n * block,
                                       hipMemcpyDefault, s));
                 LP_HIP(launch_scatter_rows(p->pages, H, p->elem, stA, stB, (int64_t)r * H, s0, n, r,
-                                           p->rows_dev, stride, s));
+                                           lb.rows_dev, stride, s));
             }
         }
     }
-    LP_HIP(launch_write_rows(p->page_table, p->max_adapters, stride, aid, p->rows_dev, S, s));
-    LP_HIP(hipEventRecord(p->staging_done, s));
+    LP_HIP(launch_write_rows(p->page_table, p->max_adapters, stride, aid, lb.rows_dev, S, s));
+    LP_HIP(hipEventRecord(lb.done, s));
     return LORA_OK;
 }
 
