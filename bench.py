@@ -116,13 +116,114 @@ def cpu_baseline(w, seconds, slots):
                       f"scaled to {slots} projection(s) per step"}
 
 
+def prefetch_bench(args, rg, torch):
+    """Adapter prefetch ("S-LoRA, in depth", section "Scheduling: prefetch, clustering and early
+    abort": the next batch's adapters are copied from pinned host memory on a separate stream while
+    the current batch computes).  Eight 32 MiB adapters (rank 16 over q/k/v/o of 32 layers at
+    H = 4096, the pages' example) are loaded into a 128-slot pool on a copy stream: alone, and while
+    the 64-token decode projection steps run on the compute stream.  Loads are issued from a second
+    host thread (the library releases the interpreter lock inside each call), so a load that waits
+    for a free load buffer does not hold up the decode issue loop."""
+    import threading
+    from workloads import build
+    dev = torch.device("cuda:0")
+    H, SLOTS, RANK, NAD = 4096, 128, 16, 8
+    ad_bytes = 2 * RANK * SLOTS * H * 2
+    cp = rg.Pool(NAD * 2 * RANK * SLOTS + 64, H, rg.LORA_BF16, n_slots=SLOTS, max_adapters=NAD, max_rank=RANK)
+    g = torch.Generator().manual_seed(20251)
+    host = []
+    for a in range(NAD):
+        pair = []
+        for _ in range(2):
+            t = torch.empty((SLOTS, RANK, H), dtype=torch.bfloat16, pin_memory=True)
+            t.copy_((torch.randn((SLOTS, RANK, H), generator=g) * 0.02).to(torch.bfloat16))
+            pair.append(t)
+        host.append(pair)
+    copy = torch.cuda.Stream()   # default priority, like every stream here
+    comp = torch.cuda.current_stream()
+
+    def load_all():
+        for a in range(NAD):
+            rg.lora_pool_load_adapter(cp.handle, a, RANK, host[a][0], host[a][1], stream=copy)
+
+    def evict_all():
+        for a in range(NAD):
+            rg.lora_pool_release_adapter(cp.handle, a)
+            rg.lora_pool_evict_adapter(cp.handle, a, stream=copy)
+        torch.cuda.synchronize()
+
+    # the compute side: the default decode workload, rotated over a few replicas
+    w = build("decode", device="cuda")
+    d_ids, d_ranks, d_scale = (torch.as_tensor(v, device=dev) for v in (w.ids, w.ranks, w.scales))
+    reps = []
+    for _ in range(8):
+        pool = rg.Pool(w.num_pages, w.hidden, rg.LORA_BF16, n_slots=1, max_adapters=w.max_adapters,
+                       free_order=w.free_order)
+        assert all(st == 0 for st in pool.run_ops(w.ops, w.ranks, w.adapter))
+        reps.append((pool, w.W(0).clone(), w.x().clone(), torch.empty_like(w.x())))
+    ws = torch.empty(rg.lora_project_workspace_size(reps[0][0].handle, w.T), dtype=torch.uint8, device=dev)
+
+    def decode(n):
+        for i in range(n):
+            pool, W, x, y = reps[i % len(reps)]
+            rg._lib.lora_project(pool.handle, x.data_ptr(), W.data_ptr(), pool.table[0].data_ptr(), d_ids.data_ptr(),
+                                 d_ranks.data_ptr(), d_scale.data_ptr(), w.T, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 comp.cuda_stream)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    N = 500
+    # warm-up of both sides
+    load_all(); torch.cuda.synchronize(); evict_all()
+    decode(50); torch.cuda.synchronize()
+    # 1. loads alone
+    a0, a1 = ev(), ev()
+    a0.record(copy); load_all(); a1.record(copy); torch.cuda.synchronize()
+    t_load = a0.elapsed_time(a1) / 1e3
+    evict_all()
+    # 2. decode alone
+    d0, d1 = ev(), ev()
+    d0.record(comp); decode(N); d1.record(comp); torch.cuda.synchronize()
+    t_dec = d0.elapsed_time(d1) / 1e3
+    # 3. both: the loads start with the decode steps
+    c0, c1, e0, e1 = ev(), ev(), ev(), ev()
+    e0.record(comp); c0.record(copy)
+    th = threading.Thread(target=lambda: (load_all(), c1.record(copy)))
+    th.start()
+    decode(N)
+    e1.record(comp)
+    th.join()
+    torch.cuda.synchronize()
+    t_dec_ov = e0.elapsed_time(e1) / 1e3
+    t_load_ov = c0.elapsed_time(c1) / 1e3
+    t_both = max(t_dec_ov, e0.elapsed_time(c1) / 1e3)
+    hidden = (t_dec + t_load - t_both) / t_load
+    out = {
+        "metric": "adapter prefetch: host-to-pool copy rate, alone and beside the decode projection",
+        "value": NAD * ad_bytes / t_load_ov / 1e9, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+        "data": "synthetic (seeded; pinned host memory)",
+        "config": {"workload": "8 adapters of 32 MiB (rank 16, q/k/v/o of 32 layers, H=4096 bf16) into a 128-slot "
+                               "pool on a copy stream, beside 64-token decode steps (H=4096, 32 adapters)",
+                   "adapter_bytes": ad_bytes, "adapters": NAD, "decode_steps": N},
+        "load_alone_GBps": NAD * ad_bytes / t_load / 1e9, "load_alone_ms_per_adapter": t_load / NAD * 1e3,
+        "load_beside_decode_GBps": NAD * ad_bytes / t_load_ov / 1e9,
+        "load_beside_decode_ms_per_adapter": t_load_ov / NAD * 1e3,
+        "decode_alone_us_per_step": t_dec / N * 1e6, "decode_beside_loads_us_per_step": t_dec_ov / N * 1e6,
+        "loads_hidden_fraction": hidden,
+    }
+    cp.close()
+    for r in reps:
+        r[0].close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny", "stack13b"],
-                    help="stack13b runs one layer (its q/k/v/o slots) of the 40-layer stack")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny", "stack13b", "prefetch"],
+                    help="stack13b runs one layer (its q/k/v/o slots) of the 40-layer stack; prefetch measures "
+                         "adapter loads from pinned host memory beside the decode projection")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
     ap.add_argument("--profile-calls", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -154,6 +255,9 @@ def main():
             dst_t.copy_(src_t)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 20}), flush=True)
+        return
+    if args.workload == "prefetch":
+        prefetch_bench(args, rg, torch)
         return
     w = build(args.workload, device="cuda", layers=1 if args.workload == "stack13b" else None)
     slots = list(range(w.n_slots))
