@@ -133,7 +133,11 @@ int lora_pool_free(lora_pool *pool);
  * A_t and B may be host (pageable or pinned) or device memory; they are read during the call
  * for pageable memory and, otherwise, by work on `stream`: keep them alive and unchanged until
  * the stream has passed this call.  Both may be NULL when rank == 0 or the pool is
- * bookkeeping-only.  The copies and the page-table update are enqueued on `stream`.
+ * bookkeeping-only.  The copies and the page-table update are enqueued on `stream`, so with
+ * pinned memory and a stream of its own a load overlaps projections on other streams (section
+ * "Scheduling: prefetch, clustering and early abort"); make the first projection that uses the
+ * adapter wait for `stream` (an event).  Host rows are staged through one of two load buffers per
+ * pool: the call waits on the host only while the load two calls earlier is still queued.
  * Errors: LORA_EINVAL, LORA_ERANK (rank > max_rank), LORA_EEXIST, LORA_ENOMEM, LORA_EHIP.
  */
 int lora_pool_load_adapter(lora_pool *pool, int32_t adapter_id, int32_t rank, const void *A_t,
