@@ -65,6 +65,13 @@ enum lora_dtype {
     LORA_BF16 = 1       /* ... in bfloat16; products accumulate in float32                      */
 };
 
+enum lora_victim_rule {         /* which idle adapter a load that is short of pages evicts first */
+    LORA_VICTIM_LOAD_ORDER = 0, /* oldest load first: the pool sketch's rule (the default)        */
+    LORA_VICTIM_LRU = 1,        /* least recently admitted first                                  */
+    LORA_VICTIM_FARTHEST = 2    /* next request in the lookahead farthest first (Belady's rule);
+                                   adapters beyond the lookahead last-admitted-longest-ago first  */
+};
+
 #define LORA_MAX_RANK 64        /* largest rank a pool can be created for                       */
 #define LORA_MAX_ADAPTERS 8192  /* largest adapter id + 1                                       */
 
@@ -142,6 +149,19 @@ int lora_pool_free(lora_pool *pool);
  */
 int lora_pool_load_adapter(lora_pool *pool, int32_t adapter_id, int32_t rank, const void *A_t,
                            const void *B, void *stream);
+
+/* Choose the victim rule for idle-adapter eviction (enum lora_victim_rule).  The pool sketch of
+ * "S-LoRA, in depth" (section "Unified paging") evicts idle adapters in load order; the MoE-offload
+ * page ("Cache the Experts You Will Need", sections "A better eviction rule cuts transfers without
+ * changing routing" and "Limited foresight") compares least-recently-used eviction with evicting the
+ * entry whose next request lies farthest ahead, given a window of upcoming requests.  A "use" is a
+ * call of lora_pool_load_adapter that names the adapter (resident or not).  Errors: LORA_EINVAL. */
+int lora_pool_set_victim_rule(lora_pool *pool, int32_t rule);
+
+/* The upcoming adapter requests the farthest-future rule looks at: `n` host ids, soonest first (for
+ * a scheduler, its waiting queue).  Copied; n == 0 clears it.  Adapters that do not occur count as
+ * needed after every one that does.  Errors: LORA_EINVAL (n < 0, or ids NULL with n > 0). */
+int lora_pool_set_lookahead(lora_pool *pool, const int32_t *adapter_ids, int64_t n);
 
 /* One user of the adapter finished (refcount - 1).  At zero users it stays resident but idle and
  * becomes evictable.  Errors: LORA_ENOENT (not resident), LORA_EINVAL (already idle). */

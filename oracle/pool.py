@@ -16,7 +16,17 @@ Extensions beyond the sketch (each an explicit reading):
   * ``n_slots`` = layers * projections; within one adapter's page list, slot s owns entries
     [2 r s, 2 r (s+1)), A's columns first then B's rows;
   * reloading a resident adapter at a different rank is an error ("eexist");
-  * ``release`` drops one user, ``evict`` reclaims one idle adapter, ``free_kv`` ends a request.
+  * ``release`` drops one user, ``evict`` reclaims one idle adapter, ``free_kv`` ends a request;
+  * the order in which idle adapters are evicted (the victim rule) is selectable:
+      - "load_order": oldest load first, the sketch's rule (an adapter evicted and loaded again
+        counts from its new load);
+      - "lru": least recently used first, where a use is an admission (``ensure_adapter``) --
+        the rule the MoE-offload page ("Cache the Experts You Will Need") measures as LRU;
+      - "farthest": the adapter whose next request in the caller's lookahead (upcoming adapter
+        ids, soonest first) lies farthest, as Belady's rule on that page; adapters with no request
+        in the lookahead count as farthest and, as in its "Limited foresight" paragraph, are
+        ordered among themselves least recently used first; ties inside the lookahead cannot occur
+        (each position names one adapter).
 """
 from __future__ import annotations
 
@@ -63,7 +73,14 @@ def tp_comm_base(n_gpus: int, tokens: int, hidden: int) -> float:
 class UnifiedPoolModel:
     """Host-side page bookkeeping of one pool; page contents are not modelled."""
 
-    def __init__(self, num_pages: int, free_order=None):
+    VICTIM_RULES = ("load_order", "lru", "farthest")
+
+    def __init__(self, num_pages: int, free_order=None, victim: str = "load_order"):
+        assert victim in self.VICTIM_RULES, victim
+        self.victim = victim
+        self.lookahead: list[int] = []
+        self.tick = 0
+        self.last_use: dict[int, int] = {}
         self.num_pages = int(num_pages)
         if free_order is None:
             self.free = list(range(self.num_pages))
@@ -78,11 +95,17 @@ class UnifiedPoolModel:
     def _take(self, n: int) -> list:
         return [self.free.pop() for _ in range(n)]
 
+    def set_lookahead(self, ids) -> None:
+        """Upcoming adapter requests, soonest first (the waiting queue a scheduler can see)."""
+        self.lookahead = [int(a) for a in ids]
+
     def ensure_adapter(self, aid: int, rank: int, n_slots: int) -> str:
         if aid in self.adapter_pages:
             if self.adapter_rank[aid] != rank:
                 return "eexist"
             self.adapter_refs[aid] += 1
+            self.tick += 1
+            self.last_use[aid] = self.tick
             return "ok"
         need = 2 * rank * n_slots
         if len(self.free) < need and not self.evict_idle_adapters(need):
@@ -90,10 +113,24 @@ class UnifiedPoolModel:
         self.adapter_pages[aid] = self._take(need)
         self.adapter_rank[aid] = rank
         self.adapter_refs[aid] = 1
+        self.tick += 1
+        self.last_use[aid] = self.tick
         return "ok"
 
+    def victim_order(self) -> list:
+        """The idle adapters in the order the victim rule evicts them."""
+        idle = [a for a, n in self.adapter_refs.items() if n == 0]   # load order
+        if self.victim == "lru":
+            idle.sort(key=lambda a: self.last_use[a])
+        elif self.victim == "farthest":
+            far = len(self.lookahead)
+            def next_use(a):
+                return self.lookahead.index(a) if a in self.lookahead else far
+            idle.sort(key=lambda a: (-next_use(a), self.last_use[a]))
+        return idle
+
     def evict_idle_adapters(self, need: int) -> bool:
-        for aid in [a for a, n in self.adapter_refs.items() if n == 0]:
+        for aid in self.victim_order():
             self._drop(aid)
             if len(self.free) >= need:
                 return True
@@ -103,6 +140,7 @@ class UnifiedPoolModel:
         self.free.extend(self.adapter_pages.pop(aid))
         del self.adapter_refs[aid]
         del self.adapter_rank[aid]
+        del self.last_use[aid]
 
     def release(self, aid: int) -> str:
         if aid not in self.adapter_refs:

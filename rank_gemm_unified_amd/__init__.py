@@ -20,6 +20,7 @@ LORA_OK, LORA_EINVAL, LORA_ENOMEM, LORA_ENOENT = 0, -1, -2, -3
 LORA_ERANK, LORA_EBUSY, LORA_EEXIST, LORA_EHIP, LORA_EDEVICE = -4, -5, -6, -7, -8
 LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_RANK, LORA_MAX_ADAPTERS = 64, 8192
+LORA_VICTIM_LOAD_ORDER, LORA_VICTIM_LRU, LORA_VICTIM_FARTHEST = 0, 1, 2
 STATUS_NAMES = {0: "ok", -1: "einval", -2: "enomem", -3: "enoent", -4: "erank", -5: "ebusy",
                 -6: "eexist", -7: "ehip", -8: "edevice"}
 
@@ -54,6 +55,8 @@ _SIGS = {
     "lora_pool_free": (ctypes.c_int, [_vp]),
     "lora_pool_load_adapter": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "lora_pool_release_adapter": (ctypes.c_int, [_vp, _i32]),
+    "lora_pool_set_victim_rule": (ctypes.c_int, [_vp, _i32]),
+    "lora_pool_set_lookahead": (ctypes.c_int, [_vp, _vp, _i64]),
     "lora_pool_evict_adapter": (ctypes.c_int, [_vp, _i32, _vp]),
     "lora_pool_grow_kv": (ctypes.c_int, [_vp, _i64, _i32, _vp]),
     "lora_pool_free_kv": (ctypes.c_int, [_vp, _i64]),
@@ -140,6 +143,17 @@ def lora_pool_free(pool):
 def lora_pool_load_adapter(pool, adapter_id, rank, A_t, B, stream=None, check=True):
     rc = _lib.lora_pool_load_adapter(pool, adapter_id, rank, _ptr(A_t), _ptr(B), _stream(stream))
     return _check(rc, "lora_pool_load_adapter") if check else rc
+
+
+def lora_pool_set_victim_rule(pool, rule, check=True):
+    rc = _lib.lora_pool_set_victim_rule(pool, rule)
+    return _check(rc, "lora_pool_set_victim_rule") if check else rc
+
+
+def lora_pool_set_lookahead(pool, adapter_ids, check=True):
+    ids = np.ascontiguousarray(adapter_ids, dtype=np.int32)
+    rc = _lib.lora_pool_set_lookahead(pool, ids.ctypes.data if ids.size else None, ids.size)
+    return _check(rc, "lora_pool_set_lookahead") if check else rc
 
 
 def lora_pool_release_adapter(pool, adapter_id, check=True):

@@ -36,6 +36,7 @@ enum : int {
 struct Adapter {
     int32_t rank = 0;
     int32_t users = 0;
+    int64_t last_use = 0;         // admission tick of the latest load call that named it
     std::vector<int64_t> pages;   // 2 * rank * n_slots, list order
 };
 
@@ -59,6 +60,9 @@ struct lora_pool {
     std::vector<int64_t> free_list;                        // allocation pops from the back
     std::unordered_map<int32_t, lorapool::Adapter> adapters;
     std::vector<int32_t> load_order;                       // resident ids, oldest first
+    int32_t victim_rule = LORA_VICTIM_LOAD_ORDER;          // which idle adapter goes first
+    std::vector<int32_t> lookahead;                        // upcoming adapter requests, soonest first
+    int64_t tick = 0;                                      // admissions so far
     std::unordered_map<int64_t, std::vector<int64_t>> kv;
     int64_t kv_total = 0, adapter_total = 0;
     int64_t n_loads = 0, n_evictions = 0, bytes_loaded = 0;

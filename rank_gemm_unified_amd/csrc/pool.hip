@@ -178,12 +178,33 @@ static int clear_rows(lora_pool *p, int32_t aid, hipStream_t s) {
     return LORA_OK;
 }
 
-// Evict idle adapters oldest-first until `need` pages are free; true if enough are free.
-static int evict_idle(lora_pool *p, int64_t need, hipStream_t s, bool *enough) {
+// The idle adapters in the order the pool's victim rule evicts them (load order, least recently
+// admitted first, or next request in the lookahead farthest first with the ones beyond it least
+// recently admitted first).
+static std::vector<int32_t> victim_order(lora_pool *p) {
     std::vector<int32_t> idle;
     for (int32_t a : p->load_order)
         if (p->adapters[a].users == 0) idle.push_back(a);
-    for (int32_t a : idle) {
+    if (p->victim_rule == LORA_VICTIM_LRU) {
+        std::stable_sort(idle.begin(), idle.end(),
+                         [&](int32_t a, int32_t b) { return p->adapters[a].last_use < p->adapters[b].last_use; });
+    } else if (p->victim_rule == LORA_VICTIM_FARTHEST) {
+        const int64_t far = (int64_t)p->lookahead.size();
+        std::unordered_map<int32_t, int64_t> next;
+        for (int64_t i = far - 1; i >= 0; --i) next[p->lookahead[(size_t)i]] = i;   // first occurrence wins
+        auto nx = [&](int32_t a) { auto it = next.find(a); return it == next.end() ? far : it->second; };
+        std::stable_sort(idle.begin(), idle.end(), [&](int32_t a, int32_t b) {
+            const int64_t na = nx(a), nb = nx(b);
+            if (na != nb) return na > nb;
+            return p->adapters[a].last_use < p->adapters[b].last_use;
+        });
+    }
+    return idle;
+}
+
+// Evict idle adapters in victim order until `need` pages are free; true if enough are free.
+static int evict_idle(lora_pool *p, int64_t need, hipStream_t s, bool *enough) {
+    for (int32_t a : victim_order(p)) {
         drop_adapter(p, a);
         int rc = clear_rows(p, a, s);
         if (rc) return rc;
@@ -259,6 +280,7 @@ extern "C" int lora_pool_load_adapter(lora_pool *p, int32_t aid, int32_t rank, c
             return set_error(LORA_EEXIST, "lora_pool_load_adapter: adapter %d is resident at rank %d, not %d", aid,
                              it->second.rank, rank);
         it->second.users++;
+        it->second.last_use = ++p->tick;
         return LORA_OK;
     }
     const int64_t need = (int64_t)2 * rank * p->n_slots;
@@ -287,9 +309,33 @@ extern "C" int lora_pool_load_adapter(lora_pool *p, int32_t aid, int32_t rank, c
         p->bytes_loaded += need * (int64_t)p->hidden * p->elem;
     }
     p->adapter_total += need;
+    ad.last_use = ++p->tick;
     p->adapters.emplace(aid, std::move(ad));
     p->load_order.push_back(aid);
     p->n_loads++;
+    return LORA_OK;
+}
+
+extern "C" int lora_pool_set_victim_rule(lora_pool *p, int32_t rule) {
+    clear_error();
+    if (!p) return set_error(LORA_EINVAL, "lora_pool_set_victim_rule: pool is NULL");
+    if (rule != LORA_VICTIM_LOAD_ORDER && rule != LORA_VICTIM_LRU && rule != LORA_VICTIM_FARTHEST)
+        return set_error(LORA_EINVAL, "lora_pool_set_victim_rule: unknown rule %d", rule);
+    std::lock_guard<std::mutex> lk(p->mu);
+    p->victim_rule = rule;
+    return LORA_OK;
+}
+
+extern "C" int lora_pool_set_lookahead(lora_pool *p, const int32_t *ids, int64_t n) {
+    clear_error();
+    if (!p) return set_error(LORA_EINVAL, "lora_pool_set_lookahead: pool is NULL");
+    if (n < 0 || (n > 0 && !ids)) return set_error(LORA_EINVAL, "lora_pool_set_lookahead: %lld ids at %p", (long long)n, (const void *)ids);
+    std::lock_guard<std::mutex> lk(p->mu);
+    try {
+        p->lookahead.assign(ids, ids + n);
+    } catch (...) {
+        return set_error(LORA_ENOMEM, "lora_pool_set_lookahead: out of host memory");
+    }
     return LORA_OK;
 }
 

@@ -150,6 +150,56 @@ def test_random_ops_match_model():
             rg.lora_pool_free(pool)
 
 
+_RULES = {"load_order": rg.LORA_VICTIM_LOAD_ORDER, "lru": rg.LORA_VICTIM_LRU, "farthest": rg.LORA_VICTIM_FARTHEST}
+
+
+@pytest.mark.parametrize("victim", list(_RULES))
+def test_victim_rules_match_model(victim):
+    """Admission traffic that keeps the pool short of pages: the library's evictions under each
+    victim rule (with a lookahead that changes as the trace goes on) match the pool model's."""
+    rng = np.random.default_rng(11 + _RULES[victim])
+    for trial in range(20):
+        n_slots = int(rng.integers(1, 3))
+        n = int(rng.integers(40, 160))
+        model = UnifiedPoolModel(n, victim=victim)
+        pool = _bk_pool(n, n_slots, max_adapters=12, max_rank=8, free_order=None)
+        try:
+            assert rg.lora_pool_set_victim_rule(pool, _RULES[victim]) == 0
+            ranks = rng.integers(1, 9, 12)
+            held = []
+            for step in range(200):
+                if step % 7 == 0:
+                    la = [int(a) for a in rng.integers(0, 12, int(rng.integers(0, 10)))]
+                    model.set_lookahead(la)
+                    rg.lora_pool_set_lookahead(pool, la)
+                if held and rng.random() < 0.5:
+                    a = held.pop(int(rng.integers(0, len(held))))
+                    want, got = model.release(a), rg.lora_pool_release_adapter(pool, a, check=False)
+                else:
+                    a = int(rng.integers(0, 12))
+                    want = model.ensure_adapter(a, int(ranks[a]), n_slots)
+                    got = rg.lora_pool_load_adapter(pool, a, int(ranks[a]), None, None, stream=0, check=False)
+                    if want == "ok":
+                        held.append(a)
+                assert got == _model_status(want), (trial, step, rg.lora_last_error())
+                assert rg.lora_pool_free_list(pool) == model.free
+            assert rg.lora_pool_resident(pool) == list(model.adapter_pages)
+        finally:
+            rg.lora_pool_free(pool)
+
+
+def test_victim_rule_arguments():
+    pool = _bk_pool(16, 1, max_adapters=4, max_rank=4, free_order=None)
+    try:
+        assert rg.lora_pool_set_victim_rule(pool, 3, check=False) == rg.LORA_EINVAL
+        assert rg.lora_pool_set_lookahead(pool, [], check=False) == 0
+        assert rg._lib.lora_pool_set_lookahead(pool, None, 2) == rg.LORA_EINVAL
+        assert rg._lib.lora_pool_set_lookahead(pool, None, -1) == rg.LORA_EINVAL
+        assert rg.lora_pool_set_victim_rule(None, 0, check=False) == rg.LORA_EINVAL
+    finally:
+        rg.lora_pool_free(pool)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "many"])
 def test_workload_plans_match_model(name):
     w = build(name)

@@ -148,3 +148,77 @@ def test_expected_page_rows():
     rows = expected_page_rows(pt, 0, 2, At, B)
     assert [p for p, _ in rows] == [5, 9, 2, 7]
     assert np.array_equal(rows[0][1], At[0]) and np.array_equal(rows[3][1], B[1])
+
+
+# ---- victim rules ------------------------------------------------------------------------------
+# Three adapters of rank 2 on one slot (4 pages each) fill a 12-page pool.  Worked by hand from
+# the rules' definitions (oracle/pool.py header): after "0, 1, 2 loaded and released, then 0
+# admitted again and released", a fourth adapter needs 4 pages and one idle adapter must go.
+#   load order: 0 was loaded first (its second admission is not a load)            -> evict 0
+#   lru:        last uses 0 @4, 1 @2, 2 @3                                          -> evict 1
+#   farthest, lookahead [1, 0, 2]: next uses 1 @0, 0 @1, 2 @2                       -> evict 2
+#   farthest, lookahead [1]: 0 and 2 are beyond it, least recently used of them     -> evict 2
+#   farthest, lookahead [2]: 0 and 1 are beyond it, least recently used of them     -> evict 1
+@pytest.mark.parametrize("victim,lookahead,evicted", [
+    ("load_order", [], 0), ("lru", [], 1), ("farthest", [1, 0, 2], 2), ("farthest", [1], 2),
+    ("farthest", [2], 1), ("farthest", [], 1)])
+def test_victim_rules_hand_trace(victim, lookahead, evicted):
+    m = UnifiedPoolModel(12, victim=victim)
+    for a in (0, 1, 2, 0):
+        assert m.ensure_adapter(a, 2, 1) == "ok"
+        assert m.release(a) == "ok"
+    m.set_lookahead(lookahead)
+    assert m.ensure_adapter(3, 2, 1) == "ok"
+    assert sorted(m.adapter_pages) == sorted({0, 1, 2, 3} - {evicted})
+    assert len(m.free) == 0
+
+
+def _min_loads(seq, cap):
+    """Fewest loads any schedule needs to serve `seq` one request at a time with room for `cap`
+    adapters: exhaustive search over every choice of victim (memoised on the resident set)."""
+    from functools import lru_cache
+
+    @lru_cache(maxsize=None)
+    def f(i, res):
+        if i == len(seq):
+            return 0
+        a = seq[i]
+        if a in res:
+            return f(i + 1, res)
+        if len(res) < cap:
+            return 1 + f(i + 1, res | {a})
+        return 1 + min(f(i + 1, (res - {v}) | {a}) for v in res)
+    return f(0, frozenset())
+
+
+def _loads(seq, cap, victim, foresight=None):
+    """Loads the pool model makes serving `seq` (admit, then release, each request), adapters of
+    rank 1 on one slot (2 pages each), `cap` of them fitting."""
+    m = UnifiedPoolModel(2 * cap, victim=victim)
+    n = 0
+    for i, a in enumerate(seq):
+        rest = seq[i + 1:]
+        m.set_lookahead(rest if foresight is None else rest[:foresight])
+        n += a not in m.adapter_pages
+        assert m.ensure_adapter(a, 1, 1) == "ok"
+        assert m.release(a) == "ok"
+    return n
+
+
+def test_farthest_with_full_lookahead_is_optimal():
+    """For one request at a time and equal sizes, evicting the adapter needed farthest in the future
+    makes the fewest loads (Belady's rule, cited on the MoE-offload page); checked against the
+    exhaustive search on random short traces, and no other rule does better."""
+    rng = np.random.default_rng(7)
+    worse = 0
+    for trial in range(120):
+        cap = int(rng.integers(2, 4))
+        seq = [int(a) for a in rng.integers(0, cap + 3, int(rng.integers(6, 13)))]
+        best = _min_loads(tuple(seq), cap)
+        assert _loads(seq, cap, "farthest") == best, (seq, cap)
+        for victim in ("lru", "load_order"):
+            got = _loads(seq, cap, victim)
+            assert got >= best
+            worse += got > best
+        assert _loads(seq, cap, "farthest", foresight=1) >= best
+    assert worse > 0   # the traces do separate the rules
