@@ -216,14 +216,81 @@ def prefetch_bench(args, rg, torch):
     print(json.dumps(out), flush=True)
 
 
+def adapter_sweep_bench(args, rg, torch):
+    """The load test of "S-LoRA, in depth" (section "What to do next"): the projection with 1, 10,
+    100 and 1,000 adapters in play at the configs' rank mix (uniform over {8, 16, 32, 64}), for a
+    64-token and a 256-token decode batch at H = 4096 (ids uniform over the adapters): mean time per
+    call, tokens/s and the 99th percentile of single calls (HIP events around each call, minus the
+    events' own cost measured by an event-free loop)."""
+    import numpy as np
+    from workloads import custom
+    dev = torch.device("cuda:0")
+    rows = []
+    for T in (64, 256):
+        for K in (1, 10, 100, 1000):
+            rng = np.random.default_rng(1000 * T + K)
+            ranks = rng.choice([8, 16, 32, 64], K).astype(np.int32)
+            ids = rng.integers(0, K, T).astype(np.int32)
+            w = custom(4096, ranks, ids, device="cuda", seed=77 + K + T)
+            d_ids, d_ranks, d_scale = (torch.as_tensor(v, device=dev) for v in (w.ids, w.ranks, w.scales))
+            reps = []
+            for _ in range(4):
+                pool = rg.Pool(w.num_pages, w.hidden, rg.LORA_BF16, n_slots=1, max_adapters=K, free_order=w.free_order)
+                assert all(st == 0 for st in pool.run_ops(w.ops, w.ranks, w.adapter))
+                reps.append((pool, w.W(0).clone(), w.x().clone(), torch.empty_like(w.x())))
+            w.drop_cache("AB")
+            ws = torch.empty(rg.lora_project_workspace_size(reps[0][0].handle, T), dtype=torch.uint8, device=dev)
+            sh = torch.cuda.current_stream().cuda_stream
+
+            def call(i):
+                pool, W, x, y = reps[i % len(reps)]
+                rg._lib.lora_project(pool.handle, x.data_ptr(), W.data_ptr(), pool.table[0].data_ptr(),
+                                     d_ids.data_ptr(), d_ranks.data_ptr(), d_scale.data_ptr(), T, y.data_ptr(),
+                                     ws.data_ptr(), ws.numel(), sh)
+            N = 600
+            for i in range(50):
+                call(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(N):
+                call(i)
+            b.record()
+            torch.cuda.synchronize()
+            mean_us = a.elapsed_time(b) / N * 1e3
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(N + 1)]
+            evs[0].record()
+            for i in range(N):
+                call(i)
+                evs[i + 1].record()
+            torch.cuda.synchronize()
+            per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(N)])
+            gap = max(0.0, per.mean() - mean_us)     # each interval also holds its closing event
+            distinct = len({int(v) for v in ids})
+            rows.append({"tokens": T, "adapters": K, "distinct_in_batch": distinct, "us_per_call": mean_us,
+                         "tokens_per_s": T / (mean_us / 1e6), "p99_us": float(np.percentile(per, 99)) - gap,
+                         "p50_us": float(np.percentile(per, 50)) - gap})
+            log(f"T={T} adapters={K} distinct={distinct}: {mean_us:.2f} us/call, p99 {rows[-1]['p99_us']:.2f} us")
+            for r in reps:
+                r[0].close()
+    out = {"metric": "multi-LoRA projection with 1, 10, 100, 1000 adapters: tokens/s and p99 per call",
+           "value": rows[-1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+           "data": "synthetic (seeded; inputs resident in HBM)",
+           "config": {"workload": "H=4096 bf16 decode batches of 64 and 256 tokens, ids uniform over 1/10/100/1000 "
+                                  "adapters of ranks U{8,16,32,64}; value = 256 tokens, 1000 adapters"},
+           "sweep": rows}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny", "stack13b", "prefetch"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny", "stack13b", "prefetch", "adapters"],
                     help="stack13b runs one layer (its q/k/v/o slots) of the 40-layer stack; prefetch measures "
-                         "adapter loads from pinned host memory beside the decode projection")
+                         "adapter loads from pinned host memory beside the decode projection; adapters runs the "
+                         "1/10/100/1000-adapter load test")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
     ap.add_argument("--profile-calls", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -258,6 +325,9 @@ def main():
         return
     if args.workload == "prefetch":
         prefetch_bench(args, rg, torch)
+        return
+    if args.workload == "adapters":
+        adapter_sweep_bench(args, rg, torch)
         return
     w = build(args.workload, device="cuda", layers=1 if args.workload == "stack13b" else None)
     slots = list(range(w.n_slots))
