@@ -19,6 +19,7 @@ the fp64 CPU oracle timed on this host as a baseline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -291,6 +292,9 @@ def main():
                     help="stack13b runs one layer (its q/k/v/o slots) of the 40-layer stack; prefetch measures "
                          "adapter loads from pinned host memory beside the decode projection; adapters runs the "
                          "1/10/100/1000-adapter load test")
+    ap.add_argument("--fuse-slots", action="store_true",
+                    help="project the slots that read the same x (a layer's q, k, v) in one lora_project_slots "
+                         "call (up to 4 slots per call) instead of one lora_project call per slot")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
     ap.add_argument("--profile-calls", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -357,16 +361,40 @@ def main():
         reps.append((pool, Ws, xs, ys))
         if w.name in ("many", "stack13b"):
             w.drop_cache("AB")
+    # the calls of one step: one per slot, or (--fuse-slots) one per run of up to LORA_MAX_CALL_SLOTS
+    # slots that read the same x
+    groups = []
+    for s in slots:
+        if (args.fuse_slots and groups and w.slot_x[groups[-1][0]] == w.slot_x[s]
+                and len(groups[-1]) < rg.LORA_MAX_CALL_SLOTS):
+            groups[-1].append(s)
+        else:
+            groups.append([s])
     # one workspace shared by every replica, as a caller issuing the calls on one stream would
-    ws = torch.empty(max(rg.lora_project_workspace_size(p.handle, w.T) for p, *_ in reps), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(rg.lora_project_slots_workspace_size(p.handle, len(g), w.T) for p, *_ in reps
+                         for g in groups), dtype=torch.uint8, device=dev)
     wsb = ws.numel()
-    log(f"replicas: {R}")
+    log(f"replicas: {R}; calls per step: {[list(g) for g in groups]}")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    if args.fuse_slots:   # argument arrays built once per replica, outside the timed loop
+        fused = []
+        for pool, Ws, xs, ys in reps:
+            calls = []
+            for g in groups:
+                n = len(g)
+                calls.append((n, (ctypes.c_int32 * n)(*g), xs[w.slot_x[g[0]]].data_ptr(),
+                              (ctypes.c_void_p * n)(*[Ws[s].data_ptr() for s in g]),
+                              (ctypes.c_void_p * n)(*[ys[s].data_ptr() for s in g])))
+            fused.append(calls)
 
     def step(i):
         pool, Ws, xs, ys = reps[i % R]
+        if args.fuse_slots:
+            for n, sl, xp, wp, yp in fused[i % R]:
+                rg._lib.lora_project_slots(pool.handle, n, sl, xp, wp, d_ids.data_ptr(), d_ranks.data_ptr(),
+                                           d_scale.data_ptr(), w.T, yp, ws.data_ptr(), wsb, sh)
+            return
         for s in slots:
             rg._lib.lora_project(pool.handle, xs[w.slot_x[s]].data_ptr(), Ws[s].data_ptr(), pool.table[s].data_ptr(),
                                  d_ids.data_ptr(), d_ranks.data_ptr(), d_scale.data_ptr(), w.T, ys[s].data_ptr(),
@@ -391,7 +419,7 @@ def main():
     # per-kernel device time from HIP events on the launch stream (separate loop: events add gaps)
     calls_per_rep = max(1, args.profile_calls // R)
     for pool, *_ in reps:
-        rg.lora_profile_start(pool.handle, calls_per_rep * len(slots))
+        rg.lora_profile_start(pool.handle, calls_per_rep * len(groups))
     for i in range(calls_per_rep * R):
         step(i)
     torch.cuda.synchronize()
@@ -407,7 +435,8 @@ def main():
     # per-interval cost is (sum of the kernel intervals - event-free time per call) / intervals.
     decode_like = w.dtype == "bf16" and w.T <= 256
     keys = ["first_us", "second_us"] if decode_like else ["group_us", "first_us", "second_us"]
-    call_us = ms_per_step * 1e3 / len(slots)
+    call_us = ms_per_step * 1e3 / len(groups)
+    per_call = len(slots) / len(groups)   # slots one launch projects, on average
     event_gap_us = max(0.0, (sum(avg[k] for k in keys) - call_us) / len(keys))
     log(f"kernel event intervals (us): {avg} over {prof['calls']} calls; per-interval event cost {event_gap_us:.2f} us")
 
@@ -416,25 +445,25 @@ def main():
     second_us = avg["second_us"] - event_gap_us
     if decode_like:
         stream_kernel = w.T <= 64 and w.hidden <= 8192
-        achieved = info["decode_first_bytes"] / (first_us / 1e6) / 1e9
+        achieved = info["decode_first_bytes"] * per_call / (first_us / 1e6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "kernel": ("k_decode_stream (W stream + MFMA partials, gathered-A shrink)" if stream_kernel else
                            "k_decode_wide (x and W through LDS + MFMA partials, shrink work units)"),
-                "algorithmic_bytes_per_launch": info["decode_first_bytes"], "avg_launch_us": first_us,
+                "algorithmic_bytes_per_launch": info["decode_first_bytes"] * per_call, "avg_launch_us": first_us,
                 "traffic": (traffic_from_profiles("decode_stream", os.path.join(src, "k_decode.hip")) if stream_kernel
                             else traffic_from_profiles("decode_wide", os.path.join(src, "k_decode_wide.hip"))),
                 "timing": "HIP events around each launch on its stream, minus the per-interval event cost "
                           f"({event_gap_us:.2f} us, from the event-free timed loop)",
                 "second_kernel": {"kernel": "k_decode_finish (partials + gathered-B expand + rounding)",
                                   "avg_launch_us": second_us,
-                                  "achieved_GBps": info["decode_second_bytes"] / (second_us / 1e6) / 1e9}}
+                                  "achieved_GBps": info["decode_second_bytes"] * per_call / (second_us / 1e6) / 1e9}}
     else:
-        achieved = info["prefill_second_flops"] / (second_us / 1e6) / 1e12
+        achieved = info["prefill_second_flops"] * per_call / (second_us / 1e6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                 "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)",
-                "algorithmic_flops_per_launch": info["prefill_second_flops"], "avg_launch_us": second_us,
+                "algorithmic_flops_per_launch": info["prefill_second_flops"] * per_call, "avg_launch_us": second_us,
                 "traffic": traffic_from_profiles("prefill_main", os.path.join(src, "k_prefill.hip")),
                 "timing": "HIP events around each launch on its stream, minus the per-interval event cost "
                           f"({event_gap_us:.2f} us, from the event-free timed loop)"}
@@ -459,7 +488,8 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; inputs resident in HBM)",
         "config": {"workload": desc, "hidden": w.hidden, "tokens": w.T, "projections_per_step": len(slots),
                    "adapters": w.max_adapters, "distinct_adapters_in_batch": info["distinct_adapters"],
-                   "replicas_rotated": R, "parallelism": "single GPU"},
+                   "replicas_rotated": R, "parallelism": "single GPU",
+                   "calls_per_step": [list(g) for g in groups]},
         "step_algorithmic_bytes": info["bytes"], "step_algorithmic_flops": info["flops"],
         "step_hbm_GBps": info["bytes"] / (ms_per_step / 1e3) / 1e9,
         "step_hbm_frac": info["bytes"] / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,

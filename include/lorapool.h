@@ -247,6 +247,32 @@ int lora_project(lora_pool *pool, const void *x, const void *W, const int32_t *p
                  const int32_t *adapter_ids, const int32_t *ranks, const float *scale, int64_t T,
                  void *y, void *workspace, size_t workspace_bytes, void *stream);
 
+#define LORA_MAX_CALL_SLOTS 4   /* most slots one lora_project_slots call takes                    */
+
+/* Bytes of device workspace lora_project_slots needs for n slots and T tokens (0 if n is out of
+ * range): n times lora_project_workspace_size. */
+size_t lora_project_slots_workspace_size(const lora_pool *pool, int32_t n, int64_t T);
+
+/*
+ * The projection for n (1..LORA_MAX_CALL_SLOTS) slots that share the same tokens: the q, k and v
+ * projections of a layer read one x ("S-LoRA, in depth": an adapter has A and B for each of the
+ * projections of each layer, and the base product is batched over all tokens).  For each z < n,
+ *     y[z][t] = x[t] W[z] + s[a] * (x[t] A_{slots[z],a}) B_{slots[z],a},    a = adapter_ids[t],
+ * exactly what lora_project gives for that slot (bit for bit: every sum runs in the same order).
+ * One call groups the tokens once and launches each stage once for all n slots, so the base
+ * GEMM's tiles of the n slots share the chip (better load balance than n calls).
+ *   slots        host int32 [n], distinct or not, each in [0, n_slots); page tables are the pool's
+ *   W, y         host arrays of n device pointers, as lora_project's W and y; no two outputs may
+ *                overlap each other or x
+ *   workspace    >= lora_project_slots_workspace_size(pool, n, T) bytes, 256-byte aligned
+ * The rest as lora_project.  Float32 pools run the slots one after another.
+ * Errors (host-side, before any device work): LORA_EINVAL, LORA_EHIP.
+ */
+int lora_project_slots(lora_pool *pool, int32_t n, const int32_t *slots, const void *x,
+                       const void *const *W, const int32_t *adapter_ids, const int32_t *ranks,
+                       const float *scale, int64_t T, void *const *y, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 /*
  * Debug view of the gather: for every token t (input order) writes the pages its projection reads
  * into page_ids_out[t][0..2*max_rank) (device int32): entries 0..r-1 its A columns, r..2r-1 its B

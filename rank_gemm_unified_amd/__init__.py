@@ -21,6 +21,7 @@ LORA_ERANK, LORA_EBUSY, LORA_EEXIST, LORA_EHIP, LORA_EDEVICE = -4, -5, -6, -7, -
 LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_RANK, LORA_MAX_ADAPTERS = 64, 8192
 LORA_VICTIM_LOAD_ORDER, LORA_VICTIM_LRU, LORA_VICTIM_FARTHEST = 0, 1, 2
+LORA_MAX_CALL_SLOTS = 4
 STATUS_NAMES = {0: "ok", -1: "einval", -2: "enomem", -3: "enoent", -4: "erank", -5: "ebusy",
                 -6: "eexist", -7: "ehip", -8: "edevice"}
 
@@ -69,6 +70,8 @@ _SIGS = {
     "lora_pool_free_list": (ctypes.c_int, [_vp, _vp, _i64, _P64]),
     "lora_pool_resident": (ctypes.c_int, [_vp, _vp, _i32, _P32]),
     "lora_project_workspace_size": (_sz, [_vp, _i64]),
+    "lora_project_slots_workspace_size": (_sz, [_vp, _i32, _i64]),
+    "lora_project_slots": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_debug_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp]),
     "lora_check_device_errors": (ctypes.c_int, [_vp]),
@@ -251,6 +254,25 @@ def lora_project(pool, x, W, page_table, adapter_ids, ranks, scale, T, y, worksp
     return _check(rc, "lora_project") if check else rc
 
 
+def lora_project_slots_workspace_size(pool, n, T):
+    return _lib.lora_project_slots_workspace_size(pool, n, T)
+
+
+def lora_project_slots(pool, slots, x, Ws, adapter_ids, ranks, scale, T, ys, workspace, workspace_bytes=None,
+                       stream=None, check=True):
+    """slots: sequence of slot indices; Ws, ys: sequences of tensors (or addresses), one per slot."""
+    n = len(slots)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    wp = (ctypes.c_void_p * max(n, 1))(*[_ptr(w) for w in Ws])
+    yp = (ctypes.c_void_p * max(n, 1))(*[_ptr(y) for y in ys])
+    rc = _lib.lora_project_slots(pool, n, sl.ctypes.data, _ptr(x), ctypes.cast(wp, ctypes.c_void_p),
+                                 _ptr(adapter_ids), _ptr(ranks), _ptr(scale), T, ctypes.cast(yp, ctypes.c_void_p),
+                                 _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(rc, "lora_project_slots") if check else rc
+
+
 def lora_debug_gather(pool, page_table, adapter_ids, ranks, T, out, stream=None, check=True):
     rc = _lib.lora_debug_gather(pool, _ptr(page_table), _ptr(adapter_ids), _ptr(ranks), T, _ptr(out),
                                 _stream(stream))
@@ -352,6 +374,16 @@ class Pool:
 
     def run_ops(self, ops, ranks, adapter_weights, stream=None):
         return run_pool_ops(self.handle, ops, ranks, adapter_weights, stream)
+
+    def project_slots(self, slots, x, Ws, adapter_ids, ranks, scale, ys=None, stream=None):
+        T = x.shape[0]
+        if ys is None:
+            ys = [self.torch.empty_like(x) for _ in slots]
+        need = lora_project_slots_workspace_size(self.handle, len(slots), T)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=self.pages.device)
+        lora_project_slots(self.handle, slots, x, Ws, adapter_ids, ranks, scale, T, ys, self._ws, stream=stream)
+        return ys
 
     def project(self, slot, x, W, adapter_ids, ranks, scale, y=None, stream=None):
         T = x.shape[0]

@@ -120,6 +120,26 @@ struct Ws {
 };
 Ws carve(void *base, const Plan &plan);
 
+// Per-slot pointers of one call: up to MAX_CALL_SLOTS slots that share x and the tokens' adapter
+// ids (the q, k and v projections of a layer).  The argument of the several-slot kernels, indexed
+// by blockIdx.z (a one-slot call launches the one-slot kernels, whose arguments are the slot's
+// pointers themselves); the token grouping of the prefill path lives in slot 0's workspace region
+// and serves every slot.
+constexpr int MAX_CALL_SLOTS = 4;
+struct SlotPtrs {
+    const void *W[MAX_CALL_SLOTS];
+    void *y[MAX_CALL_SLOTS];
+    const int32_t *pt[MAX_CALL_SLOTS];   // the slot's page table [max_adapters][2 max_rank]
+    float *v[MAX_CALL_SLOTS];            // workspace regions, one per slot
+    uint16_t *v16[MAX_CALL_SLOTS];
+    float *ypart[MAX_CALL_SLOTS];
+    int32_t *sorted_tok[MAX_CALL_SLOTS];
+    int32_t *spages[MAX_CALL_SLOTS];
+};
+struct SlotRows {   // the page tables alone (the grouping kernel checks every slot's rows)
+    const int32_t *pt[MAX_CALL_SLOTS];
+};
+
 // ctrl[] slots written by the segment kernel
 enum : int { CTRL_NSEG = 0, CTRL_NITEMS = 1, CTRL_NVALID = 2, CTRL_WORDS = 64 };
 
@@ -134,19 +154,18 @@ hipError_t launch_scatter_rows(void *pages, int32_t hidden, int32_t elem, const 
                                int32_t n_slots_chunk, int32_t rank, const int32_t *rows,
                                int32_t row_stride, hipStream_t s);
 hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws,
-                           const int32_t *ids, const int32_t *ranks, const int32_t *pt,
+                           const int32_t *ids, const int32_t *ranks, const SlotPtrs &sp, int n,
                            hipStream_t s);
 hipError_t launch_debug_gather(const lora_pool *p, const int32_t *pt, const int32_t *ids,
                                const int32_t *ranks, int64_t T, int32_t *out, hipStream_t s);
-hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
-                              const void *W, const int32_t *ids, const int32_t *ranks, const int32_t *pt,
-                              const float *scale, hipStream_t s);
-hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
-                         const void *W, const int32_t *ids, const int32_t *ranks, const int32_t *pt,
-                         const float *scale, void *y, hipStream_t s, hipEvent_t mid);
+hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
+                              const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n,
+                              hipStream_t s);
+hipError_t launch_decode(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
+                         const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
+                         hipEvent_t mid);
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
-                          const void *W, const int32_t *pt, const float *scale, void *y,
-                          hipStream_t s, hipEvent_t mid);
+                          const float *scale, const SlotPtrs &sp, int n, hipStream_t s, hipEvent_t mid);
 hipError_t launch_f32(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
                       const void *W, const int32_t *pt, const float *scale, void *y,
                       hipStream_t s, hipEvent_t mid);

@@ -149,7 +149,7 @@ struct StreamShape {
 };
 
 template <int MB, int KQ>
-__global__ __launch_bounds__(256, 1) void k_decode_stream(
+__device__ __forceinline__ void decode_stream_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
@@ -491,6 +491,32 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     }
 }
 
+// The stream kernel for one slot, and for the n slots of one call (blockIdx.z = the slot; the slots
+// share x and the ids).  The one-slot kernel keeps the short argument block.
+template <int MB, int KQ>
+__global__ __launch_bounds__(256, 1) void k_decode_stream(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
+    int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
+    float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
+    int *__restrict__ err_word) {
+    decode_stream_body<MB, KQ>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T, H, S,
+                               n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word);
+}
+
+template <int MB, int KQ>
+__global__ __launch_bounds__(256, 1) void k_decode_stream_slots(
+    const uint16_t *__restrict__ x, const SlotPtrs sp, const uint16_t *__restrict__ pages, int64_t num_pages,
+    int32_t stride, const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const float *__restrict__ scale,
+    int32_t max_adapters, int32_t max_rank, int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP,
+    int *__restrict__ err_word) {
+    const int z = blockIdx.z;
+    decode_stream_body<MB, KQ>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks, scale,
+                               max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
+                               (int4 *)sp.sorted_tok[z], sp.spages[z], err_word);
+}
+
 // ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
 // Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Thread -> (token i of the
 // group, 8 columns c, quarter q of j: j in [16 q, 16 q + 16)).  Two dependent round trips:
@@ -500,11 +526,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
 // The four quarter threads of a token then add their x W partials and expand terms by two lane
 // shuffles (a fixed order), and one of them rounds and stores.
 template <int SY, int SV>
-__global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ sorted_tok,
-                                                       const int32_t *__restrict__ spages,
-                                                       const float *__restrict__ ypart, const float *__restrict__ vpart,
-                                                       int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
-                                                       int32_t H, int32_t T, uint16_t *__restrict__ y) {
+__device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sorted_tok, const int32_t *__restrict__ spages,
+                                                   const float *__restrict__ ypart, const float *__restrict__ vpart,
+                                                   int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
+                                                   int32_t H, int32_t T, uint16_t *__restrict__ y) {
     constexpr int SQ = (SY + 3) / 4;   // x W splits per quarter thread
     __shared__ float s_v[8][64];
     const int n0 = blockIdx.x * 64;
@@ -603,6 +628,23 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
     if (q == 0 && live_tok) store16_nt(y + (int64_t)t * H + n0 + c, pack_bf16x8(o));
 }
 
+template <int SY, int SV>
+__global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ sorted_tok, const int32_t *__restrict__ spages,
+                                                       const float *__restrict__ ypart, const float *__restrict__ vpart,
+                                                       int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
+                                                       int32_t H, int32_t T, uint16_t *__restrict__ y) {
+    decode_finish_body<SY, SV>(sorted_tok, spages, ypart, vpart, RP, pages, num_pages, H, T, y);
+}
+
+template <int SY, int SV>
+__global__ __launch_bounds__(256) void k_decode_finish_slots(const SlotPtrs sl, int32_t RP,
+                                                             const uint16_t *__restrict__ pages, int64_t num_pages,
+                                                             int32_t H, int32_t T) {
+    const int z = blockIdx.z;
+    decode_finish_body<SY, SV>((const int4 *)sl.sorted_tok[z], sl.spages[z], sl.ypart[z], sl.v[z], RP, pages,
+                               num_pages, H, T, (uint16_t *)sl.y[z]);
+}
+
 // ---- float32 pools: grouping kernel + gathered shrink + plain VALU kernel ---------------------------
 __global__ __launch_bounds__(256) void k_shrink_items_f32(
     const char *__restrict__ x, const char *__restrict__ pages, int32_t H, const int32_t *__restrict__ pt,
@@ -663,37 +705,50 @@ __global__ __launch_bounds__(256) void k_project_f32(const float *__restrict__ x
 
 // ---- launchers -----------------------------------------------------------------------------------------
 template <int MB, int KQ>
-static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                                const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
-                                hipStream_t s) {
+static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
+                                const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s) {
     constexpr size_t lds = StreamShape<MB, KQ>::LDS;
     static_assert(lds <= 160 * 1024, "stream kernel LDS");
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)k_decode_stream<MB, KQ>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)k_decode_stream_slots<MB, KQ>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_decode_stream<MB, KQ>), dim3(plan.n_tiles * plan.ysplit), dim3(256), lds, s,
-                       (const uint16_t *)x, (const uint16_t *)W, (const uint16_t *)p->pages, p->num_pages, pt,
-                       2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden,
-                       plan.ysplit, plan.n_tiles, plan.rp, ws.ypart, ws.v, (int4 *)ws.sorted_tok, ws.spages, p->dev_err);
+    if (n == 1)
+        hipLaunchKernelGGL((k_decode_stream<MB, KQ>), dim3(plan.n_tiles * plan.ysplit), dim3(256), lds, s,
+                           (const uint16_t *)x, (const uint16_t *)sp.W[0], (const uint16_t *)p->pages, p->num_pages,
+                           sp.pt[0], 2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank,
+                           (int32_t)plan.T, p->hidden, plan.ysplit, plan.n_tiles, plan.rp, sp.ypart[0], sp.v[0],
+                           (int4 *)sp.sorted_tok[0], sp.spages[0], p->dev_err);
+    else
+        hipLaunchKernelGGL((k_decode_stream_slots<MB, KQ>), dim3(plan.n_tiles * plan.ysplit, 1, n), dim3(256), lds,
+                           s, (const uint16_t *)x, sp, (const uint16_t *)p->pages, p->num_pages, 2 * p->max_rank, ids,
+                           ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.ysplit,
+                           plan.n_tiles, plan.rp, p->dev_err);
     return hipGetLastError();
 }
 
 template <int SY, int SV>
-static void launch_finish_t(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
-    dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8));
-    hipLaunchKernelGGL((k_decode_finish<SY, SV>), grid, dim3(256), 0, s, (const int4 *)ws.sorted_tok, ws.spages,
-                       ws.ypart, ws.v, plan.rp, (const uint16_t *)p->pages, p->num_pages, p->hidden, (int32_t)plan.T,
-                       (uint16_t *)y);
+static void launch_finish_t(const lora_pool *p, const Plan &plan, const SlotPtrs &sp, int n, hipStream_t s) {
+    dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8), n);
+    if (n == 1)
+        hipLaunchKernelGGL((k_decode_finish<SY, SV>), grid, dim3(256), 0, s, (const int4 *)sp.sorted_tok[0],
+                           sp.spages[0], sp.ypart[0], sp.v[0], plan.rp, (const uint16_t *)p->pages, p->num_pages,
+                           p->hidden, (int32_t)plan.T, (uint16_t *)sp.y[0]);
+    else
+        hipLaunchKernelGGL((k_decode_finish_slots<SY, SV>), grid, dim3(256), 0, s, sp, plan.rp,
+                           (const uint16_t *)p->pages, p->num_pages, p->hidden, (int32_t)plan.T);
 }
 
-static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const Ws &ws, void *y, hipStream_t s) {
+static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const SlotPtrs &sp, int n, hipStream_t s) {
     const int sy = plan.ysplit, sv = plan.ysplit;   // both decode kernels write S v partials
     switch (sy * 16 + sv) {
-#define LP_CASE(A, B) case A * 16 + B: launch_finish_t<A, B>(p, plan, ws, y, s); break;
+#define LP_CASE(A, B) case A * 16 + B: launch_finish_t<A, B>(p, plan, sp, n, s); break;
         LP_CASE(1, 1) LP_CASE(2, 1) LP_CASE(4, 1) LP_CASE(8, 1)
         LP_CASE(2, 2) LP_CASE(3, 3) LP_CASE(4, 4) LP_CASE(5, 5) LP_CASE(6, 6) LP_CASE(7, 7) LP_CASE(8, 8)
 #undef LP_CASE
@@ -702,13 +757,13 @@ static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const Ws &
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                         const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale, void *y,
-                         hipStream_t s, hipEvent_t mid) {
+hipError_t launch_decode(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
+                         const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
+                         hipEvent_t mid) {
     hipError_t e;
     if (plan.stream) {
         switch (plan.mb * 64 + plan.ks) {
-#define LP_CASE(M, K) case M * 64 + K: e = launch_stream<M, K>(p, plan, ws, x, W, ids, ranks, pt, scale, s); break;
+#define LP_CASE(M, K) case M * 64 + K: e = launch_stream<M, K>(p, plan, x, ids, ranks, scale, sp, n, s); break;
             LP_CASE(1, 1) LP_CASE(1, 2) LP_CASE(1, 4) LP_CASE(1, 8)
             LP_CASE(2, 1) LP_CASE(2, 2) LP_CASE(2, 4) LP_CASE(2, 8)
             LP_CASE(3, 1) LP_CASE(3, 2) LP_CASE(3, 4) LP_CASE(3, 8)
@@ -717,11 +772,11 @@ hipError_t launch_decode(const lora_pool *p, const Plan &plan, const Ws &ws, con
             default: return hipErrorInvalidValue;
         }
     } else {
-        e = launch_decode_wide(p, plan, ws, x, W, ids, ranks, pt, scale, s);
+        e = launch_decode_wide(p, plan, x, ids, ranks, scale, sp, n, s);
     }
     if (e != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
-    return launch_finish(p, plan, ws, y, s);
+    return launch_finish(p, plan, sp, n, s);
 }
 
 hipError_t launch_f32(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,

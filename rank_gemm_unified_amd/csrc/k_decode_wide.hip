@@ -75,7 +75,7 @@ __device__ __forceinline__ int last_leq(const int32_t *off, int n, int32_t i) {
 using namespace wide;
 
 template <int MB16>
-__global__ __launch_bounds__(NTH, 1) void k_decode_wide(
+__device__ __forceinline__ void decode_wide_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
@@ -464,34 +464,68 @@ __global__ __launch_bounds__(NTH, 1) void k_decode_wide(
     }
 }
 
+// One slot per launch, and the n slots of one call (blockIdx.z = the slot); the one-slot kernel
+// keeps the short argument block.
+template <int MB16>
+__global__ __launch_bounds__(NTH, 1) void k_decode_wide(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
+    int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
+    float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
+    int *__restrict__ err_word) {
+    decode_wide_body<MB16>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T, H, S,
+                           n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word);
+}
+
+template <int MB16>
+__global__ __launch_bounds__(NTH, 1) void k_decode_wide_slots(
+    const uint16_t *__restrict__ x, const SlotPtrs sp, const uint16_t *__restrict__ pages, int64_t num_pages,
+    int32_t stride, const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const float *__restrict__ scale,
+    int32_t max_adapters, int32_t max_rank, int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP,
+    int *__restrict__ err_word) {
+    const int z = blockIdx.z;
+    decode_wide_body<MB16>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks, scale,
+                           max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
+                           (int4 *)sp.sorted_tok[z], sp.spages[z], err_word);
+}
+
 size_t decode_wide_lds(int mb16) { return (size_t)(NSTAGE * mb16 * 16 + NWS * 64) * KC * 2 + sizeof(WideGroup); }
 
 template <int MB16>
-static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                                const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
-                                hipStream_t s) {
+static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
+                                const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s) {
     static bool attr_set = false;
     const size_t lds = decode_wide_lds(MB16);
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)k_decode_wide<MB16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)k_decode_wide_slots<MB16>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    dim3 grid((unsigned)(plan.n_tiles * plan.ysplit));
-    hipLaunchKernelGGL((k_decode_wide<MB16>), grid, dim3(NTH), lds, s, (const uint16_t *)x, (const uint16_t *)W,
-                       (const uint16_t *)p->pages, p->num_pages, pt, 2 * p->max_rank, ids, ranks, scale,
-                       p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.ysplit, plan.n_tiles, plan.rp,
-                       ws.ypart, ws.v, (int4 *)ws.sorted_tok, ws.spages, p->dev_err);
+    dim3 grid((unsigned)(plan.n_tiles * plan.ysplit), 1, n);
+    if (n == 1)
+        hipLaunchKernelGGL((k_decode_wide<MB16>), grid, dim3(NTH), lds, s, (const uint16_t *)x,
+                           (const uint16_t *)sp.W[0], (const uint16_t *)p->pages, p->num_pages, sp.pt[0],
+                           2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T,
+                           p->hidden, plan.ysplit, plan.n_tiles, plan.rp, sp.ypart[0], sp.v[0],
+                           (int4 *)sp.sorted_tok[0], sp.spages[0], p->dev_err);
+    else
+        hipLaunchKernelGGL((k_decode_wide_slots<MB16>), grid, dim3(NTH), lds, s, (const uint16_t *)x, sp,
+                           (const uint16_t *)p->pages, p->num_pages, 2 * p->max_rank, ids, ranks, scale,
+                           p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.ysplit, plan.n_tiles,
+                           plan.rp, p->dev_err);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                              const int32_t *ids, const int32_t *ranks, const int32_t *pt, const float *scale,
-                              hipStream_t s) {
+hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
+                              const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s) {
     switch (plan.mb) {
-        case 8: return launch_wide_t<8>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
-        case 16: return launch_wide_t<16>(p, plan, ws, x, W, ids, ranks, pt, scale, s);
+        case 8: return launch_wide_t<8>(p, plan, x, ids, ranks, scale, sp, n, s);
+        case 16: return launch_wide_t<16>(p, plan, x, ids, ranks, scale, sp, n, s);
         default: return hipErrorInvalidValue;
     }
 }

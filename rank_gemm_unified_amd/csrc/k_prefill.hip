@@ -39,10 +39,10 @@ constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, e
 __device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ ((r >> 1) & 7)) << 3); }   // as swz
 
 template <int SNS>
-__global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages,
-                                                     int32_t H, const int32_t *__restrict__ pt, int32_t stride,
-                                                     const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
-                                                     float *__restrict__ vpart, int32_t T, int32_t R) {
+__device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H,
+                                              const int32_t *__restrict__ pt, int32_t stride,
+                                              const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
+                                              float *__restrict__ vpart, int32_t T, int32_t R) {
     const int4 rec = item_rec[blockIdx.x];
     if (rec.x < 0) return;   // past the last work item
     extern __shared__ __align__(16) uint16_t st[];   // SNS stages
@@ -108,11 +108,30 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict_
     }
 }
 
+// One slot per launch, and the n slots of one call (blockIdx.z = the slot; the slots share x and the
+// token grouping); the one-slot kernel keeps the short argument block.
+template <int SNS>
+__global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H,
+                                                     const int32_t *__restrict__ pt, int32_t stride,
+                                                     const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
+                                                     float *__restrict__ vpart, int32_t T, int32_t R) {
+    shrink_body<SNS>(x, pages, H, pt, stride, perm, item_rec, vpart, T, R);
+}
+
+template <int SNS>
+__global__ __launch_bounds__(256) void k_shrink_mfma_slots(const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ pages, int32_t H,
+                                                           const SlotPtrs sp, int32_t stride,
+                                                           const int32_t *__restrict__ perm,
+                                                           const int4 *__restrict__ item_rec, int32_t T, int32_t R) {
+    shrink_body<SNS>(x, pages, H, sp.pt[blockIdx.z], stride, perm, item_rec, sp.v[blockIdx.z], T, R);
+}
+
 // v16[t][j] = bf16(s_a * sum_split vpart[split][t][j]) for tokens with an adapter; zero for
 // j in [r, roundup(r, 4)).  One thread per (token, 4 consecutive j).
-__global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vpart, const int32_t *__restrict__ tok_a,
-                                                    const int32_t *__restrict__ tok_r, const float *__restrict__ scale,
-                                                    int32_t T, int32_t R, uint16_t *__restrict__ v16) {
+__device__ __forceinline__ void v_finalize_body(const float *__restrict__ vpart, const int32_t *__restrict__ tok_a,
+                                              const int32_t *__restrict__ tok_r, const float *__restrict__ scale,
+                                              int32_t T, int32_t R, uint16_t *__restrict__ v16) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t t = idx / (R / 4);
     const int j0 = (int)(idx % (R / 4)) * 4;
@@ -131,6 +150,18 @@ __global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vp
     uint32_t w0 = (j0 < r ? f32_to_bf16_bits(sc * sum[0]) : 0u) | ((j0 + 1 < r ? f32_to_bf16_bits(sc * sum[1]) : 0u) << 16);
     uint32_t w1 = (j0 + 2 < r ? f32_to_bf16_bits(sc * sum[2]) : 0u) | ((j0 + 3 < r ? f32_to_bf16_bits(sc * sum[3]) : 0u) << 16);
     *reinterpret_cast<uint2 *>(v16 + t * R + j0) = make_uint2(w0, w1);
+}
+
+__global__ __launch_bounds__(256) void k_v_finalize(const float *__restrict__ vpart, const int32_t *__restrict__ tok_a,
+                                                    const int32_t *__restrict__ tok_r, const float *__restrict__ scale,
+                                                    int32_t T, int32_t R, uint16_t *__restrict__ v16) {
+    v_finalize_body(vpart, tok_a, tok_r, scale, T, R, v16);
+}
+
+__global__ __launch_bounds__(256) void k_v_finalize_slots(const SlotPtrs sp, const int32_t *__restrict__ tok_a,
+                                                          const int32_t *__restrict__ tok_r,
+                                                          const float *__restrict__ scale, int32_t T, int32_t R) {
+    v_finalize_body(sp.v[blockIdx.z], tok_a, tok_r, scale, T, R, sp.v16[blockIdx.z]);
 }
 
 // ---- base GEMM + fused expand --------------------------------------------------------------------
@@ -156,7 +187,7 @@ constexpr int DPW = (BM * BK * 2 / 1024) / PF_WAVES;   // 1 KiB tile chunks per 
 constexpr int LR_K = 64 * (BN / 8) / PF_THREADS;         // B-row pieces per thread of the low-rank term
 constexpr int LR_V = BM * (64 / 8) / PF_THREADS;         // v-row pieces per thread of the low-rank term
 
-__global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
+__device__ __forceinline__ void prefill_main_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
@@ -484,43 +515,84 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
             }
 }
 
-hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                          const int32_t *pt, const float *scale, void *y, hipStream_t s, hipEvent_t mid) {
+// One slot per launch, and the n slots of one call (blockIdx.z = the slot; the slots share x and the
+// token grouping); the one-slot kernel keeps the short argument block.
+__global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
+    const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
+    int32_t n_tiles_n, uint16_t *__restrict__ y) {
+    prefill_main_body(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y);
+}
+
+__global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_slots(
+    const uint16_t *__restrict__ x, const SlotPtrs sp, const uint16_t *__restrict__ pages, int32_t stride,
+    const int32_t *__restrict__ tok_a, const int32_t *__restrict__ tok_r, int32_t R, int32_t T, int32_t H,
+    int32_t n_tiles_n) {
+    const int z = blockIdx.z;
+    prefill_main_body(x, (const uint16_t *)sp.W[z], pages, sp.pt[z], stride, tok_a, tok_r,
+                      (const uint16_t *)sp.v16[z], R, T, H, n_tiles_n, (uint16_t *)sp.y[z]);
+}
+
+hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const float *scale,
+                          const SlotPtrs &sp, int n, hipStream_t s, hipEvent_t mid) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_prefill_main, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)MAIN_LDS);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)k_shrink_mfma<6>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(6 * SH_STAGE * 2));
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)k_shrink_mfma<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(4 * SH_STAGE * 2));
-        if (e != hipSuccess) return e;
+        const struct { const void *f; int lds; } attrs[] = {
+            {(const void *)k_prefill_main, (int)MAIN_LDS},
+            {(const void *)k_prefill_main_slots, (int)MAIN_LDS},
+            {(const void *)k_shrink_mfma<6>, (int)(6 * SH_STAGE * 2)},
+            {(const void *)k_shrink_mfma_slots<6>, (int)(6 * SH_STAGE * 2)},
+            {(const void *)k_shrink_mfma<4>, (int)(4 * SH_STAGE * 2)},
+            {(const void *)k_shrink_mfma_slots<4>, (int)(4 * SH_STAGE * 2)},
+        };
+        for (const auto &a : attrs) {
+            const hipError_t e = hipFuncSetAttribute(a.f, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds);
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
     if (plan.vsplit != VSPLIT) return hipErrorInvalidValue;
-    dim3 g1(plan.n_items_max, VSPLIT);
-    if (plan.T <= 4096)
-        hipLaunchKernelGGL(k_shrink_mfma<6>, g1, dim3(256), 6 * SH_STAGE * 2, s, (const uint16_t *)x,
-                           (const uint16_t *)p->pages, p->hidden, pt, 2 * p->max_rank, ws.perm, ws.item_rec, ws.v,
-                           (int32_t)plan.T, plan.rp);
-    else
-        hipLaunchKernelGGL(k_shrink_mfma<4>, g1, dim3(256), 4 * SH_STAGE * 2, s, (const uint16_t *)x,
-                           (const uint16_t *)p->pages, p->hidden, pt, 2 * p->max_rank, ws.perm, ws.item_rec, ws.v,
-                           (int32_t)plan.T, plan.rp);
+    const uint16_t *xh = (const uint16_t *)x, *pages = (const uint16_t *)p->pages;
+    const int32_t stride = 2 * p->max_rank, T = (int32_t)plan.T;
+    dim3 g1(plan.n_items_max, VSPLIT, n);
+    const int sns = plan.T <= 4096 ? 6 : 4;
+    const size_t sh_lds = (size_t)sns * SH_STAGE * 2;
+    if (n == 1) {
+        if (sns == 6)
+            hipLaunchKernelGGL(k_shrink_mfma<6>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
+                               ws.perm, ws.item_rec, sp.v[0], T, plan.rp);
+        else
+            hipLaunchKernelGGL(k_shrink_mfma<4>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
+                               ws.perm, ws.item_rec, sp.v[0], T, plan.rp);
+    } else {
+        if (sns == 6)
+            hipLaunchKernelGGL(k_shrink_mfma_slots<6>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp, stride,
+                               ws.perm, ws.item_rec, T, plan.rp);
+        else
+            hipLaunchKernelGGL(k_shrink_mfma_slots<4>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp, stride,
+                               ws.perm, ws.item_rec, T, plan.rp);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nthr = plan.T * (plan.rp / 4);
-    hipLaunchKernelGGL(k_v_finalize, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, ws.v, ws.tok_a, ws.tok_r,
-                       scale, (int32_t)plan.T, plan.rp, ws.v16);
+    const dim3 gf((unsigned)((nthr + 255) / 256), 1, n);
+    if (n == 1)
+        hipLaunchKernelGGL(k_v_finalize, gf, dim3(256), 0, s, sp.v[0], ws.tok_a, ws.tok_r, scale, T, plan.rp,
+                           sp.v16[0]);
+    else
+        hipLaunchKernelGGL(k_v_finalize_slots, gf, dim3(256), 0, s, sp, ws.tok_a, ws.tok_r, scale, T, plan.rp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
     const int tn = (p->hidden + BN - 1) / BN, tm = (int)((plan.T + BM - 1) / BM);
     const int grid = (tn + 7) / 8 * 8 + ((tm - 1) * tn + 7) / 8 * 8;   // the last row of tiles, then the rest
-    hipLaunchKernelGGL(k_prefill_main, dim3(grid), dim3(PF_THREADS), MAIN_LDS, s, (const uint16_t *)x, (const uint16_t *)W,
-                       (const uint16_t *)p->pages, pt, 2 * p->max_rank, ws.tok_a, ws.tok_r, ws.v16,
-                       plan.rp, (int32_t)plan.T, p->hidden, tn, (uint16_t *)y);
+    if (n == 1)
+        hipLaunchKernelGGL(k_prefill_main, dim3(grid), dim3(PF_THREADS), MAIN_LDS, s, xh, (const uint16_t *)sp.W[0],
+                           pages, sp.pt[0], stride, ws.tok_a, ws.tok_r, (const uint16_t *)sp.v16[0], plan.rp, T,
+                           p->hidden, tn, (uint16_t *)sp.y[0]);
+    else
+        hipLaunchKernelGGL(k_prefill_main_slots, dim3(grid, 1, n), dim3(PF_THREADS), MAIN_LDS, s, xh, sp, pages,
+                           stride, ws.tok_a, ws.tok_r, plan.rp, T, p->hidden, tn);
     return hipGetLastError();
 }
 

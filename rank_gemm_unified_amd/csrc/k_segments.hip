@@ -109,7 +109,7 @@ constexpr int KPT = 16;   // tokens per thread held in registers (T <= 16384 rea
 constexpr int32_t F_OFF = 1 << 30;   // cnt flag: the adapter's tokens get no low-rank term
 
 __global__ __launch_bounds__(SEG_THREADS) void k_segments(
-    const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const int32_t *__restrict__ pt,
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const SlotRows sp, int32_t n_slots_call,
     int32_t stride, int32_t T, int32_t max_adapters, int32_t max_rank, int64_t num_pages, int32_t chunk,
     int32_t *__restrict__ tok_a, int32_t *__restrict__ tok_r, int32_t *__restrict__ perm,
     int32_t *__restrict__ seg_a, int32_t *__restrict__ seg_start, int32_t *__restrict__ item_seg,
@@ -160,9 +160,13 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
         if (cnt[a] > 0) ulist[uidx[a]] = a;
     __syncthreads();
 
-    // ---- round 2: rank and page-table row of every adapter in use (stride entries each)
+    // ---- round 2: rank and page-table row of every adapter in use (stride entries each), in every
+    // slot of the call (the later kernels read these rows unchecked; one bad row turns the adapter
+    // off in all of them)
     const int32_t nent = nused * stride;
+    for (int z = 0; z < n_slots_call; ++z)   // uniform: one slot's rows at a time
     for (int e0 = tid; e0 < nent; e0 += 8 * SEG_THREADS) {
+        const int32_t *pz = z == 0 ? sp.pt[0] : z == 1 ? sp.pt[1] : z == 2 ? sp.pt[2] : sp.pt[3];
         int32_t av[8], jv[8], rv[8], ev[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
             av[u] = ulist[e / stride];
             jv[u] = e % stride;
             rv[u] = ranks[av[u]];
-            ev[u] = pt[(int64_t)av[u] * stride + jv[u]];
+            ev[u] = pz[(int64_t)av[u] * stride + jv[u]];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(128) void k_debug_gather(const int32_t *__restrict_
 static size_t segments_lds(int32_t max_adapters) { return (size_t)(4 * max_adapters + 3 * 17) * sizeof(int32_t); }
 
 hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws, const int32_t *ids,
-                           const int32_t *ranks, const int32_t *pt, hipStream_t s) {
+                           const int32_t *ranks, const SlotPtrs &sp, int n, hipStream_t s) {
     static bool attr_set = false;
     const size_t lds = segments_lds(p->max_adapters);
     if (!attr_set) {
@@ -304,7 +308,9 @@ hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws, c
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(k_segments, dim3(1), dim3(SEG_THREADS), lds, s, ids, ranks, pt, 2 * p->max_rank,
+    SlotRows rows;
+    for (int z = 0; z < MAX_CALL_SLOTS; ++z) rows.pt[z] = sp.pt[z];
+    hipLaunchKernelGGL(k_segments, dim3(1), dim3(SEG_THREADS), lds, s, ids, ranks, rows, n, 2 * p->max_rank,
                        (int32_t)plan.T, p->max_adapters, p->max_rank, p->num_pages, plan.chunk, ws.tok_a, ws.tok_r,
                        ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.item_rec, plan.n_items_max,
                        ws.ctrl, ws.counters,

@@ -117,31 +117,58 @@ extern "C" size_t lora_project_workspace_size(const lora_pool *p, int64_t T) {
     return pl.total;
 }
 
-extern "C" int lora_project(lora_pool *p, const void *x, const void *W, const int32_t *pt, const int32_t *ids,
-                            const int32_t *ranks, const float *scale, int64_t T, void *y, void *ws,
-                            size_t ws_bytes, void *stream) {
-    if (!p) return set_error(LORA_EINVAL, "lora_project: pool is NULL");
-    if (p->bookkeeping_only) return set_error(LORA_EINVAL, "lora_project: bookkeeping-only pool");
+namespace {
+
+// One call for n slots that share x, ids, ranks and scale (n = 1: lora_project).  The workspace
+// holds n regions of one plan each; the prefill path's token grouping lives in region 0 and
+// serves every slot.  Every argument is checked before any device work.
+int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void *const *W,
+                 const int32_t *const *pt, const int32_t *ids, const int32_t *ranks, const float *scale, int64_t T,
+                 void *const *y, void *ws, size_t ws_bytes, void *stream) {
+    if (!p) return set_error(LORA_EINVAL, "%s: pool is NULL", fn);
+    if (p->bookkeeping_only) return set_error(LORA_EINVAL, "%s: bookkeeping-only pool", fn);
     if (T < 0 || T > MAX_TOKENS)
-        return set_error(LORA_EINVAL, "lora_project: T = %lld not in [0, %lld]", (long long)T, (long long)MAX_TOKENS);
+        return set_error(LORA_EINVAL, "%s: T = %lld not in [0, %lld]", fn, (long long)T, (long long)MAX_TOKENS);
     if (T == 0) return LORA_OK;
-    if (!x || !W || !pt || !ids || !ranks || !scale || !y || !ws)
-        return set_error(LORA_EINVAL, "lora_project: NULL pointer argument");
-    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(ranks, 4) ||
-        !aligned(scale, 4) || !aligned(pt, 4) || !aligned(ws, 256))
-        return set_error(LORA_EINVAL, "lora_project: misaligned pointer (x, W, y: 16 B; ids, ranks, scale, "
-                                      "page_table: 4 B; workspace: 256 B)");
+    if (!x || !ids || !ranks || !scale || !ws) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
+    if (!aligned(x, 16) || !aligned(ids, 4) || !aligned(ranks, 4) || !aligned(scale, 4) || !aligned(ws, 256))
+        return set_error(LORA_EINVAL, "%s: misaligned pointer (x, W, y: 16 B; ids, ranks, scale, page_table: 4 B; "
+                                      "workspace: 256 B)", fn);
     const size_t xbytes = (size_t)T * p->hidden * p->elem;
-    const char *xb = (const char *)x, *yb = (const char *)y;
-    if (xb < yb + xbytes && yb < xb + xbytes) return set_error(LORA_EINVAL, "lora_project: y overlaps x");
+    const char *xb = (const char *)x;
+    for (int z = 0; z < n; ++z) {
+        if (!W[z] || !pt[z] || !y[z]) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
+        if (!aligned(W[z], 16) || !aligned(y[z], 16) || !aligned(pt[z], 4))
+            return set_error(LORA_EINVAL, "%s: misaligned pointer (x, W, y: 16 B; ids, ranks, scale, page_table: 4 B; "
+                                          "workspace: 256 B)", fn);
+        const char *yb = (const char *)y[z];
+        if (xb < yb + xbytes && yb < xb + xbytes) return set_error(LORA_EINVAL, "%s: y overlaps x", fn);
+        for (int u = 0; u < z; ++u) {
+            const char *ub = (const char *)y[u];
+            if (ub < yb + xbytes && yb < ub + xbytes) return set_error(LORA_EINVAL, "%s: two outputs overlap", fn);
+        }
+    }
     Plan pl;
     make_plan(p, T, &pl);
-    if (ws_bytes < pl.total)
-        return set_error(LORA_EINVAL, "lora_project: workspace %zu bytes < %zu needed", ws_bytes, pl.total);
+    if (ws_bytes < pl.total * (size_t)n)
+        return set_error(LORA_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, pl.total * (size_t)n);
     DeviceGuard g(p->device);
-    if (!g.ok) return set_error(LORA_EHIP, "lora_project: cannot select the pool's device");
+    if (!g.ok) return set_error(LORA_EHIP, "%s: cannot select the pool's device", fn);
     hipStream_t s = (hipStream_t)stream;
-    Ws w = carve(ws, pl);
+    SlotPtrs sp{};
+    for (int z = 0; z < MAX_CALL_SLOTS; ++z) {
+        const int k = z < n ? z : 0;
+        const Ws wz = carve((char *)ws + (size_t)k * pl.total, pl);
+        sp.W[z] = W[k];
+        sp.y[z] = y[k];
+        sp.pt[z] = pt[k];
+        sp.v[z] = wz.v;
+        sp.v16[z] = wz.v16;
+        sp.ypart[z] = wz.ypart;
+        sp.sorted_tok[z] = wz.sorted_tok;
+        sp.spages[z] = wz.spages;
+    }
+    const Ws w0 = carve(ws, pl);
     hipEvent_t *ev = nullptr;
     if (p->prof_max > 0) {
         const int32_t slot = p->prof_next.fetch_add(1);
@@ -150,20 +177,62 @@ extern "C" int lora_project(lora_pool *p, const void *x, const void *W, const in
     if (ev) LP_HIP(hipEventRecord(ev[0], s));
     hipError_t e = hipSuccess;
     if (pl.path != PATH_DECODE) {   // the decode path groups tokens inside its first kernel
-        e = launch_segments(p, pl, w, ids, ranks, pt, s);
+        e = launch_segments(p, pl, w0, ids, ranks, sp, n, s);
         if (e != hipSuccess) return hip_error(e, "segment kernel launch");
     }
     if (ev) LP_HIP(hipEventRecord(ev[1], s));
     switch (pl.path) {
-        case PATH_DECODE:
-            e = launch_decode(p, pl, w, x, W, ids, ranks, pt, scale, y, s, ev ? ev[2] : nullptr);
-            break;
-        case PATH_PREFILL: e = launch_prefill(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
-        case PATH_F32: e = launch_f32(p, pl, w, x, W, pt, scale, y, s, ev ? ev[2] : nullptr); break;
+        case PATH_DECODE: e = launch_decode(p, pl, x, ids, ranks, scale, sp, n, s, ev ? ev[2] : nullptr); break;
+        case PATH_PREFILL: e = launch_prefill(p, pl, w0, x, scale, sp, n, s, ev ? ev[2] : nullptr); break;
+        case PATH_F32: e = launch_f32(p, pl, w0, x, W[0], pt[0], scale, y[0], s, ev ? ev[2] : nullptr); break;
     }
     if (e != hipSuccess) return hip_error(e, "projection kernel launch");
     if (ev) LP_HIP(hipEventRecord(ev[3], s));
     return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" int lora_project(lora_pool *p, const void *x, const void *W, const int32_t *pt, const int32_t *ids,
+                            const int32_t *ranks, const float *scale, int64_t T, void *y, void *ws,
+                            size_t ws_bytes, void *stream) {
+    return project_impl(p, "lora_project", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream);
+}
+
+extern "C" size_t lora_project_slots_workspace_size(const lora_pool *p, int32_t n, int64_t T) {
+    if (n < 1 || n > MAX_CALL_SLOTS) return 0;
+    Plan pl;
+    if (!make_plan(p, T, &pl)) return 0;
+    return pl.total * (size_t)n;
+}
+
+extern "C" int lora_project_slots(lora_pool *p, int32_t n, const int32_t *slots, const void *x,
+                                  const void *const *W, const int32_t *ids, const int32_t *ranks, const float *scale,
+                                  int64_t T, void *const *y, void *ws, size_t ws_bytes, void *stream) {
+    if (!p) return set_error(LORA_EINVAL, "lora_project_slots: pool is NULL");
+    if (n < 1 || n > MAX_CALL_SLOTS)
+        return set_error(LORA_EINVAL, "lora_project_slots: n = %d not in [1, %d]", n, MAX_CALL_SLOTS);
+    if (!slots || !W || !y) return set_error(LORA_EINVAL, "lora_project_slots: NULL pointer argument");
+    const int32_t *pts[MAX_CALL_SLOTS];
+    for (int z = 0; z < n; ++z) {
+        if (slots[z] < 0 || slots[z] >= p->n_slots)
+            return set_error(LORA_EINVAL, "lora_project_slots: slot %d not in [0, %d)", slots[z], p->n_slots);
+        pts[z] = p->page_table ? p->page_table + (size_t)slots[z] * p->max_adapters * 2 * p->max_rank : nullptr;
+    }
+    if (p->dtype == LORA_F32) {   // the float32 path (parity only) runs the slots one after another
+        Plan pl;
+        if (T > 0 && !make_plan(p, T, &pl)) return set_error(LORA_EINVAL, "lora_project_slots: bad T");
+        if (T > 0 && ws_bytes < pl.total * (size_t)n)
+            return set_error(LORA_EINVAL, "lora_project_slots: workspace %zu bytes < %zu needed", ws_bytes,
+                             pl.total * (size_t)n);
+        for (int z = 0; z < n; ++z) {
+            const int rc = project_impl(p, "lora_project_slots", 1, x, &W[z], &pts[z], ids, ranks, scale, T, &y[z],
+                                        T > 0 ? (char *)ws + (size_t)z * pl.total : ws, ws_bytes, stream);
+            if (rc) return rc;
+        }
+        return LORA_OK;
+    }
+    return project_impl(p, "lora_project_slots", n, x, W, pts, ids, ranks, scale, T, y, ws, ws_bytes, stream);
 }
 
 extern "C" int lora_profile_start(lora_pool *p, int32_t max_calls) {

@@ -1,0 +1,70 @@
+"""One call for several slots that share the tokens (the q, k and v projections of a layer): the
+outputs must equal, bit for bit, what one lora_project call per slot gives, on each path (decode
+T <= 64, decode 64 < T <= 256, prefill), and match the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import rank_gemm_unified_amd as rg
+from gpu_helpers import device_pool, errors, ids_ranks_scale, oracle_y, say
+from workloads import custom
+
+pytestmark = pytest.mark.gpu
+
+BF16_REL, BF16_ABS = 1e-2, 5e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("T,slots", [(48, [0, 1, 2]), (200, [0, 1, 2]), (700, [0, 1, 2]), (64, [2, 0]),
+                                     (300, [1, 1, 3, 0])])
+def test_slots_call_equals_one_call_per_slot(T, slots):
+    rng = np.random.default_rng(T * 31 + len(slots))
+    ranks = [8, 16, 32, 64, 0, 16, 8]
+    if T > 256:   # prefill-shaped: runs of one adapter, a few single rows
+        ids = np.repeat(rng.integers(-1, len(ranks), T // 50 + 1), 50)[:T].astype(np.int32)
+        ids[rng.integers(0, T, 10)] = rng.integers(-1, len(ranks), 10)
+    else:
+        ids = rng.integers(-1, len(ranks), T).astype(np.int32)
+    w = custom(1024, ranks, ids, n_slots=4, device="cuda", seed=900 + T)
+    say(f"case slots T={T} slots={slots}")
+    pool = device_pool(w)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    x = w.x(0)
+    ys = pool.project_slots(slots, x, [w.W(s) for s in slots], d_ids, d_ranks, d_scale)
+    singles = []
+    for s in slots:
+        y = torch.empty_like(x)
+        pool.project(s, x, w.W(s), d_ids, d_ranks, d_scale, y=y)
+        singles.append(y)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    for s, y, y1 in zip(slots, ys, singles):
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), s
+        rel, mx = errors(y, oracle_y(w, s, x=x))
+        say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
+        assert rel <= BF16_REL and mx <= BF16_ABS
+    pool.close()
+
+
+def test_slots_call_rejects_bad_arguments():
+    w = custom(256, [8, 16], np.array([0, 1, -1, 0], np.int32), n_slots=2, device="cuda", seed=3)
+    pool = device_pool(w)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    x = w.x(0)
+    ws = torch.empty(rg.lora_project_slots_workspace_size(pool.handle, 2, w.T), dtype=torch.uint8, device="cuda")
+    y0, y1 = torch.full_like(x, 7.0), torch.full_like(x, 7.0)
+    args = (x, [w.W(0), w.W(1)], d_ids, d_ranks, d_scale, w.T)
+    assert rg.lora_project_slots(pool.handle, [0, 2], *args, [y0, y1], ws, check=False) == rg.LORA_EINVAL
+    assert rg.lora_project_slots(pool.handle, [0, 1], *args, [y0, y0], ws, check=False) == rg.LORA_EINVAL
+    assert rg.lora_project_slots(pool.handle, [0, 1], *args, [y0, y1], ws, workspace_bytes=ws.numel() - 256,
+                                 check=False) == rg.LORA_EINVAL
+    assert rg.lora_project_slots(pool.handle, [0] * 5, x, [w.W(0)] * 5, d_ids, d_ranks, d_scale, w.T, [y0] * 5,
+                                 ws, check=False) == rg.LORA_EINVAL
+    torch.cuda.synchronize()
+    assert bool((y0 == 7.0).all()) and bool((y1 == 7.0).all())   # nothing ran
+    pool.close()
