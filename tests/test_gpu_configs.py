@@ -8,7 +8,9 @@
   churn.  All 40 layers are 40 independent copies of this case; the test builds one.
 
 Every gather index is compared bit for bit; outputs against the fp64 oracle, on every row (many)
-or on all decode rows plus 64 seeded rows of each prefill request (stack)."""
+or on all decode rows plus 64 seeded rows of each prefill request (stack).  At both sizes the q, k
+and v projections made by one lora_project_slots call must equal, bit for bit, one lora_project
+call per slot."""
 import numpy as np
 import pytest
 import torch
@@ -88,6 +90,20 @@ def test_many_adapters_parity(many, slot):
     _delta_check(w, pool, slot, y, ref)
 
 
+def test_many_adapters_qkv_in_one_call(many):
+    w, pool = many
+    say("case many: q/k/v in one call")
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    ys = pool.project_slots([0, 1, 2], w.x_for_slot(0), [w.W(s) for s in (0, 1, 2)], d_ids, d_ranks, d_scale)
+    for s, y in zip((0, 1, 2), ys):
+        assert torch.equal(y.view(torch.int16), run(pool, w, s).view(torch.int16)), s
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    rel, mx = errors(ys[1], oracle_y(w, 1))
+    say(f"many q/k/v in one call, slot 1: relL2={rel:.3e} maxabs={mx:.3e}")
+    assert rel <= BF16_REL and mx <= BF16_ABS
+
+
 # ---------------------------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def stack_layer():
@@ -140,3 +156,18 @@ def test_stack13b_layer_parity(stack_layer, slot):
     say(f"stack13b slot {slot}: {rows.size} rows, relL2={rel:.3e} maxabs={mx:.3e}")
     assert rel <= BF16_REL and mx <= BF16_ABS
     _delta_check(w, pool, slot, y, ref, rows=rows)
+
+
+def test_stack13b_qkv_in_one_call(stack_layer):
+    w, pool = stack_layer
+    say("case stack13b: q/k/v in one call")
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    ys = pool.project_slots([0, 1, 2], w.x_for_slot(0), [w.W(s) for s in (0, 1, 2)], d_ids, d_ranks, d_scale)
+    for s, y in zip((0, 1, 2), ys):
+        assert torch.equal(y.view(torch.int16), run(pool, w, s).view(torch.int16)), s
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    rows = _stack_rows(w)
+    rel, mx = errors(ys[1][torch.as_tensor(rows, device="cuda")], oracle_y(w, 1, rows=rows))
+    say(f"stack13b q/k/v in one call, slot 1: {rows.size} rows, relL2={rel:.3e} maxabs={mx:.3e}")
+    assert rel <= BF16_REL and mx <= BF16_ABS
