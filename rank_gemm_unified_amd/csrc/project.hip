@@ -220,14 +220,23 @@ extern "C" int lora_project_slots(lora_pool *p, int32_t n, const int32_t *slots,
         pts[z] = p->page_table ? p->page_table + (size_t)slots[z] * p->max_adapters * 2 * p->max_rank : nullptr;
     }
     if (p->dtype == LORA_F32) {   // the float32 path (parity only) runs the slots one after another
+        if (T <= 0 || T > MAX_TOKENS) return project_impl(p, "lora_project_slots", n, x, W, pts, ids, ranks, scale, T,
+                                                           y, ws, ws_bytes, stream);   // T = 0: nothing; else the error
         Plan pl;
-        if (T > 0 && !make_plan(p, T, &pl)) return set_error(LORA_EINVAL, "lora_project_slots: bad T");
-        if (T > 0 && ws_bytes < pl.total * (size_t)n)
+        if (!make_plan(p, T, &pl)) return set_error(LORA_EINVAL, "lora_project_slots: bad T");
+        if (ws_bytes < pl.total * (size_t)n)
             return set_error(LORA_EINVAL, "lora_project_slots: workspace %zu bytes < %zu needed", ws_bytes,
                              pl.total * (size_t)n);
+        const size_t ybytes = (size_t)T * p->hidden * p->elem;
+        for (int z = 0; z < n; ++z)   // all checks before the first launch: outputs must not overlap
+            for (int u = 0; u < z; ++u) {
+                const char *a = (const char *)y[z], *b = (const char *)y[u];
+                if (a && b && a < b + ybytes && b < a + ybytes)
+                    return set_error(LORA_EINVAL, "lora_project_slots: two outputs overlap");
+            }
         for (int z = 0; z < n; ++z) {
             const int rc = project_impl(p, "lora_project_slots", 1, x, &W[z], &pts[z], ids, ranks, scale, T, &y[z],
-                                        T > 0 ? (char *)ws + (size_t)z * pl.total : ws, ws_bytes, stream);
+                                        (char *)ws + (size_t)z * pl.total, ws_bytes - (size_t)z * pl.total, stream);
             if (rc) return rc;
         }
         return LORA_OK;

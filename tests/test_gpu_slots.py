@@ -68,3 +68,31 @@ def test_slots_call_rejects_bad_arguments():
     torch.cuda.synchronize()
     assert bool((y0 == 7.0).all()) and bool((y1 == 7.0).all())   # nothing ran
     pool.close()
+
+
+def test_slots_call_float32_pool():
+    """The float32 pool runs the slots one after another: same bits as one call per slot, every
+    output within the float32 bound of the oracle, and overlapping outputs refused before any work."""
+    rng = np.random.default_rng(77)
+    ranks = [8, 16, 4, 0]
+    ids = rng.integers(-1, len(ranks), 40).astype(np.int32)
+    w = custom(256, ranks, ids, dtype="f32", n_slots=3, device="cuda", seed=78)
+    say("case slots float32 T=40 slots=[2, 0, 1]")
+    pool = device_pool(w)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    x = w.x(0)
+    slots = [2, 0, 1]
+    ys = pool.project_slots(slots, x, [w.W(s) for s in slots], d_ids, d_ranks, d_scale)
+    for s, y in zip(slots, ys):
+        y1 = pool.project(s, x, w.W(s), d_ids, d_ranks, d_scale)
+        assert torch.equal(y, y1), s
+        rel, mx = errors(y, oracle_y(w, s, x=x))
+        assert rel <= 1e-4, (s, rel)
+    ws = torch.empty(rg.lora_project_slots_workspace_size(pool.handle, 2, w.T), dtype=torch.uint8, device="cuda")
+    y0 = torch.full_like(x, 7.0)
+    assert rg.lora_project_slots(pool.handle, [0, 1], x, [w.W(0), w.W(1)], d_ids, d_ranks, d_scale, w.T,
+                                 [y0, y0[1:]], ws, check=False) == rg.LORA_EINVAL
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    assert bool((y0 == 7.0).all())
+    pool.close()
