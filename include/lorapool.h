@@ -264,9 +264,13 @@ size_t lora_project_slots_workspace_size(const lora_pool *pool, int32_t n, int64
  *   slots        host int32 [n], distinct or not, each in [0, n_slots); page tables are the pool's
  *   W, y         host arrays of n device pointers, as lora_project's W and y; no two outputs may
  *                overlap each other or x
- *   workspace    >= lora_project_slots_workspace_size(pool, n, T) bytes, 256-byte aligned
+ *   workspace    >= lora_project_slots_workspace_size(pool, n, T) bytes, 256-byte aligned: n regions
+ *                of lora_project_workspace_size(pool, T) bytes, region z for the z-th slot
  * The rest as lora_project.  Float32 pools run the slots one after another.
- * Errors (host-side, before any device work): LORA_EINVAL, LORA_EHIP.
+ * Errors (host-side, before any device work): LORA_EINVAL, LORA_EHIP.  Device checks as
+ * lora_project, with one difference for T > 256 (the prefill path, whose grouping serves every
+ * slot): an adapter whose page-table row is bad in any slot of the call gets the base product
+ * only, in every slot of the call.
  */
 int lora_project_slots(lora_pool *pool, int32_t n, const int32_t *slots, const void *x,
                        const void *const *W, const int32_t *adapter_ids, const int32_t *ranks,

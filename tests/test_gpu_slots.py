@@ -96,3 +96,29 @@ def test_slots_call_float32_pool():
     assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
     assert bool((y0 == 7.0).all())
     pool.close()
+
+
+@pytest.mark.parametrize("T", [48, 300])   # decode path (grouping per slot) and prefill path (shared)
+def test_slots_call_bad_row_in_one_slot(T):
+    """A page id out of range in slot 1's row of adapter 1 is reported as a device error, and that
+    adapter's tokens get the base product only: in slot 1 on the decode path, in every slot of the
+    call on the prefill path (whose one grouping serves all slots)."""
+    rng = np.random.default_rng(5 + T)
+    ranks = [8, 16, 32]
+    ids = rng.integers(0, len(ranks), T).astype(np.int32)
+    w = custom(512, ranks, ids, n_slots=2, device="cuda", seed=40 + T)
+    say(f"case slots bad row T={T}")
+    pool = device_pool(w)
+    pool.table[1][1, 0] = w.num_pages + 5
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    x = w.x(0)
+    ys = pool.project_slots([0, 1], x, [w.W(0), w.W(1)], d_ids, d_ranks, d_scale)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == rg.LORA_EDEVICE
+    off = np.where(ids == 1, -1, ids).astype(np.int32)
+    for s, y in zip((0, 1), ys):
+        want_ids = off if (s == 1 or T > 256) else ids
+        rel, mx = errors(y, oracle_y(w, s, x=x, ids=want_ids))
+        say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
+        assert rel <= BF16_REL and mx <= BF16_ABS
+    pool.close()
