@@ -21,7 +21,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("T,slots", [(48, [0, 1, 2]), (200, [0, 1, 2]), (700, [0, 1, 2]), (64, [2, 0]),
-                                     (300, [1, 1, 3, 0])])
+                                     (300, [1, 1, 3, 0]), (1, [3, 1]), (65, [0, 2]), (256, [1, 2, 3]),
+                                     (257, [2, 1, 0])])
 def test_slots_call_equals_one_call_per_slot(T, slots):
     rng = np.random.default_rng(T * 31 + len(slots))
     ranks = [8, 16, 32, 64, 0, 16, 8]
@@ -121,4 +122,19 @@ def test_slots_call_bad_row_in_one_slot(T):
         rel, mx = errors(y, oracle_y(w, s, x=x, ids=want_ids))
         say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
         assert rel <= BF16_REL and mx <= BF16_ABS
+    pool.close()
+
+
+def test_slots_call_with_no_tokens():
+    """T = 0: the call succeeds and writes nothing."""
+    w = custom(256, [8, 16], np.array([0, 1, -1, 0], np.int32), n_slots=2, device="cuda", seed=4)
+    pool = device_pool(w)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    x = w.x(0)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    y0, y1 = torch.full_like(x, 7.0), torch.full_like(x, 7.0)
+    assert rg.lora_project_slots(pool.handle, [0, 1], x, [w.W(0), w.W(1)], d_ids, d_ranks, d_scale, 0, [y0, y1],
+                                 ws, check=False) == rg.LORA_OK
+    torch.cuda.synchronize()
+    assert bool((y0 == 7.0).all()) and bool((y1 == 7.0).all())
     pool.close()
