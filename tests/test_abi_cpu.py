@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every declared symbol, and its host-side pool
 bookkeeping matches the oracle's pool model bit for bit.  No device work is done here (pools are
 bookkeeping-only: no pages, no page table)."""
+import ctypes
 import json
 import os
 import re
@@ -253,6 +254,16 @@ def test_error_codes():
         # a projection on a bookkeeping-only pool is refused before any device work
         assert rg._lib.lora_project(pool, 16, 16, 16, 16, 16, 16, 4, 16, 256, 1 << 20, None) == rg.LORA_EINVAL
         assert rg._lib.lora_project(None, 16, 16, 16, 16, 16, 16, 4, 16, 256, 1 << 20, None) == rg.LORA_EINVAL
+        # ... and so is a several-slot projection, with the slot count and slot range checked first
+        ptrs = (ctypes.c_void_p * 5)(*([256] * 5))
+        for n, slots, msg in ((0, [0], "n = 0"), (5, [0] * 5, "n = 5"), (1, [1], "slot 1"), (1, [-1], "slot -1"),
+                              (1, [0], "bookkeeping-only")):
+            sl = (ctypes.c_int32 * len(slots))(*slots)
+            assert rg._lib.lora_project_slots(pool, n, sl, 256, ptrs, 16, 16, 16, 4, ptrs, 256, 1 << 20,
+                                              None) == rg.LORA_EINVAL
+            assert msg in rg.lora_last_error(), (msg, rg.lora_last_error())
+        assert rg.lora_project_slots_workspace_size(pool, 0, 16) == 0
+        assert rg.lora_project_slots_workspace_size(pool, rg.LORA_MAX_CALL_SLOTS + 1, 16) == 0
         st = rg.lora_pool_stats(pool)
         assert st["adapter_pages"] == 16 and st["kv_pages"] == 4 and st["free_pages"] == 0
         assert st["loads"] == 1 and st["resident_adapters"] == 1
