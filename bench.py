@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the unmerged multi-LoRA projection on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|many|tiny|stack13b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decode|prefill|many|tiny|stack13b|prefetch|adapters] [--fuse-slots]
 
 A step is one pass of the whole projection (token grouping, shrink, base GEMM + expand) over one
 batch of the workload, with every input already resident in HBM.  The default workload is the
@@ -14,7 +15,9 @@ timed loop rotates through enough independent replicas (pool, page table, W, x, 
 
 Prints one JSON line: the throughput, the dominant kernel's roofline fraction (its algorithmic
 bytes or flops over its average device time, from HIP events recorded on its launch stream), and
-the fp64 CPU oracle timed on this host as a baseline.
+the fp64 CPU oracle timed on this host as a baseline.  With --fuse-slots the slots that read the
+same x (a layer's q, k and v) are projected by one lora_project_slots call; the per-launch figures
+then cover every slot of the launch.
 """
 from __future__ import annotations
 
