@@ -2,7 +2,8 @@
 
 The functions below carry the C-ABI's names and only marshal arguments (torch tensors become their
 device addresses, streams their hipStream_t handles); every step of the projection runs in the
-library's HIP kernels.  Importing this package fails loudly when the library has not been built.
+library's HIP kernels.  Importing this package fails loudly when the library has not been built or
+was built from sources other than the ones beside it.
 
 ``Pool`` is a convenience owner of the device buffers a pool needs (pages and page table),
 allocated with torch; torch is used for device memory and streams only.
@@ -89,6 +90,16 @@ for _name, (_res, _args) in _SIGS.items():
     _f.restype, _f.argtypes = _res, _args
 
 EXPORTED = tuple(_SIGS)
+
+# The library carries the hash of the sources it was built from; refuse one built from other sources
+# (a stale build whose exports happen to match would otherwise load silently).
+from ._srchash import source_hash as _source_hash  # noqa: E402
+
+SOURCE_HASH = _source_hash()
+_built = _lib.lora_version().decode()
+if SOURCE_HASH is not None and not _built.endswith(" src " + SOURCE_HASH):
+    raise ImportError(f"{LIB_PATH} ({_built}) was not built from the sources beside it (hash {SOURCE_HASH}): "
+                      "it is stale, rebuild it (python rank_gemm_unified_amd/build.py)")
 
 
 class LoraError(RuntimeError):

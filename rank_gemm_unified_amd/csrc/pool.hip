@@ -37,7 +37,10 @@ static void clear_error() { g_last_error.clear(); }
 
 extern "C" const char *lora_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" const char *lora_version(void) { return "lorapool 0.1 (gfx950)"; }
+#ifndef LORAPOOL_SRC_HASH
+#define LORAPOOL_SRC_HASH "unknown"
+#endif
+extern "C" const char *lora_version(void) { return "lorapool 0.2 (gfx950) src " LORAPOOL_SRC_HASH; }
 
 extern "C" int64_t lora_pool_pages_for(int32_t rank, int32_t projections, int32_t layers) {
     if (rank < 0 || projections < 0 || layers < 0) return -1;

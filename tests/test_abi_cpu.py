@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import rank_gemm_unified_amd as rg
-from oracle import UnifiedPoolModel, kv_pages_per_token, pages_for_adapter
+from oracle import PagePoolModel, kv_pages_per_token, adapter_page_count
 from workloads import build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -38,9 +38,27 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_constants():
     assert "gfx950" in rg.lora_version()
+    assert rg.SOURCE_HASH and rg.lora_version().endswith(" src " + rg.SOURCE_HASH)
     text = open(HEADER).read()
     assert f"#define LORA_MAX_RANK {rg.LORA_MAX_RANK}" in text
     assert re.search(rf"#define LORA_MAX_ADAPTERS {rg.LORA_MAX_ADAPTERS}\b", text)
+
+
+def test_library_built_from_other_sources_is_refused(tmp_path):
+    """A copy of the package whose sources no longer match its library: importing it fails."""
+    import shutil
+    import sys
+    pkg = os.path.dirname(os.path.abspath(rg.__file__))
+    shutil.copytree(pkg, tmp_path / "rank_gemm_unified_amd", ignore=shutil.ignore_patterns("_build", "__pycache__"))
+    (tmp_path / "include").mkdir()
+    shutil.copy(HEADER, tmp_path / "include" / "lorapool.h")
+    probe = "import rank_gemm_unified_amd as r; print(r.SOURCE_HASH)"
+    ok = subprocess.run([sys.executable, "-c", probe], cwd=tmp_path, capture_output=True, text=True)
+    assert ok.returncode == 0, ok.stderr[-2000:]
+    with open(tmp_path / "rank_gemm_unified_amd" / "csrc" / "k_pool.hip", "a") as f:
+        f.write("\n// an edit after the build\n")
+    bad = subprocess.run([sys.executable, "-c", probe], cwd=tmp_path, capture_output=True, text=True)
+    assert bad.returncode != 0 and "stale" in bad.stderr, bad.stderr[-2000:]
 
 
 def test_page_arithmetic_matches_worked_example(golden_dir):
@@ -52,7 +70,7 @@ def test_page_arithmetic_matches_worked_example(golden_dir):
     for r in (0, 1, 8, 64, 128):
         for p in (1, 4):
             for L in (1, 32, 40):
-                assert rg.lora_pool_pages_for(r, p, L) == pages_for_adapter(r, L, p)
+                assert rg.lora_pool_pages_for(r, p, L) == adapter_page_count(r, L, p)
     assert rg.lora_pool_pages_for(-1, 4, 32) == -1 and rg.lora_kv_pages_per_token(-2) == -1
     assert rg.lora_kv_pages_per_token(40) == kv_pages_per_token(40)
 
@@ -113,7 +131,7 @@ def test_random_ops_match_model():
         n = int(rng.integers(8, 300))
         n_slots = int(rng.integers(1, 4))
         order = rng.permutation(n) if trial % 2 else None
-        model = UnifiedPoolModel(n, order)
+        model = PagePoolModel(n, order)
         pool = _bk_pool(n, n_slots, max_adapters=10, max_rank=8, free_order=order)
         try:
             for _ in range(300):
@@ -121,15 +139,15 @@ def test_random_ops_match_model():
                 aid, rid = int(rng.integers(0, 10)), int(rng.integers(0, 6))
                 if k == 0:
                     rank = int(rng.integers(0, 9))
-                    want = _model_status(model.ensure_adapter(aid, rank, n_slots))
+                    want = _model_status(model.admit(aid, rank, n_slots))
                     got = rg.lora_pool_load_adapter(pool, aid, rank, None, None, stream=0, check=False)
                 elif k == 1:
                     layers = int(rng.integers(1, 4))
-                    want = _model_status(model.grow_kv(rid, layers))
+                    want = _model_status(model.add_kv_token(rid, layers))
                     r = rg.lora_pool_grow_kv(pool, rid, layers, check=False)
                     got = r if isinstance(r, int) else 0
                 elif k == 2:
-                    want = _model_status(model.free_kv(rid))
+                    want = _model_status(model.end_request(rid))
                     got = rg.lora_pool_free_kv(pool, rid, check=False)
                 elif k == 3:
                     want = _model_status(model.release(aid))
@@ -138,11 +156,11 @@ def test_random_ops_match_model():
                     want = _model_status(model.evict(aid))
                     got = rg.lora_pool_evict_adapter(pool, aid, stream=0, check=False)
                 assert got == want, (trial, k, rg.lora_last_error())
-                assert rg.lora_pool_free_list(pool) == model.free
-            assert rg.lora_pool_resident(pool) == list(model.adapter_pages)
-            for a, pages in model.adapter_pages.items():
+                assert rg.lora_pool_free_list(pool) == model.free_list
+            assert rg.lora_pool_resident(pool) == model.resident_ids()
+            for a, res in model.residents.items():
                 got_pages, rank, users = rg.lora_pool_adapter_pages(pool, a)
-                assert got_pages == pages and rank == model.adapter_rank[a] and users == model.adapter_refs[a]
+                assert got_pages == res.pages and rank == res.rank and users == res.users
             st = rg.lora_pool_stats(pool)
             ms = model.stats()
             for key in ("num_pages", "free_pages", "kv_pages", "adapter_pages", "resident_adapters"):
@@ -162,7 +180,7 @@ def test_victim_rules_match_model(victim):
     for trial in range(20):
         n_slots = int(rng.integers(1, 3))
         n = int(rng.integers(40, 160))
-        model = UnifiedPoolModel(n, victim=victim)
+        model = PagePoolModel(n, victim=victim)
         pool = _bk_pool(n, n_slots, max_adapters=12, max_rank=8, free_order=None)
         try:
             assert rg.lora_pool_set_victim_rule(pool, _RULES[victim]) == 0
@@ -178,13 +196,13 @@ def test_victim_rules_match_model(victim):
                     want, got = model.release(a), rg.lora_pool_release_adapter(pool, a, check=False)
                 else:
                     a = int(rng.integers(0, 12))
-                    want = model.ensure_adapter(a, int(ranks[a]), n_slots)
+                    want = model.admit(a, int(ranks[a]), n_slots)
                     got = rg.lora_pool_load_adapter(pool, a, int(ranks[a]), None, None, stream=0, check=False)
                     if want == "ok":
                         held.append(a)
                 assert got == _model_status(want), (trial, step, rg.lora_last_error())
-                assert rg.lora_pool_free_list(pool) == model.free
-            assert rg.lora_pool_resident(pool) == list(model.adapter_pages)
+                assert rg.lora_pool_free_list(pool) == model.free_list
+            assert rg.lora_pool_resident(pool) == model.resident_ids()
         finally:
             rg.lora_pool_free(pool)
 
@@ -204,15 +222,16 @@ def test_victim_rule_arguments():
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "many"])
 def test_workload_plans_match_model(name):
     w = build(name)
-    model = UnifiedPoolModel(w.num_pages, w.free_order)
+    model = PagePoolModel(w.num_pages, w.free_order)
     want = model.run(w.ops, w.ranks, w.n_slots)
     pool = _bk_pool(w.num_pages, w.n_slots, w.max_adapters, 64, w.free_order)
     try:
         got = rg.run_pool_ops(pool, w.ops, w.ranks, lambda a: (None, None), stream=0)
         assert [_STATUS[s] for s in want] == got
-        assert rg.lora_pool_free_list(pool) == model.free
-        for a in list(model.adapter_pages)[:: max(1, len(model.adapter_pages) // 50)]:
-            assert rg.lora_pool_adapter_pages(pool, a)[0] == model.adapter_pages[a]
+        assert rg.lora_pool_free_list(pool) == model.free_list
+        ids = model.resident_ids()
+        for a in ids[:: max(1, len(ids) // 50)]:
+            assert rg.lora_pool_adapter_pages(pool, a)[0] == model.pages_of(a)
     finally:
         rg.lora_pool_free(pool)
 
