@@ -18,8 +18,8 @@
  * pool"): a pool of pages, each one vector of H elements, shared by KV cache and adapters through
  * one free list.  An adapter of rank r on one projection takes 2r pages: the r columns of A and
  * the r rows of B.  Pages need not be contiguous or in order; a per-projection page table maps
- * (adapter, j) to a page, and the projection's gather reads each token's pages wherever they sit
- * (same page, section "The architecture").
+ * (adapter, j) to a page, and the projection's gather fetches each token's pages from wherever the
+ * pool placed them (same page, section "The architecture").
  *
  * Conventions for every function returning int:
  *   0 = LORA_OK, negative = error (below).  No C++ exception crosses this boundary.  On error,
@@ -176,7 +176,8 @@ int lora_pool_evict_adapter(lora_pool *pool, int32_t adapter_id, void *stream);
 
 /* Grow request `request_id`'s KV cache by one token: 2 * layers pages (K and V per layer), as the
  * sketch's grow_kv.  If page_ids_out is not NULL it receives the 2*layers page ids (host int64).
- * Errors: LORA_ENOMEM (caller must preempt or abort a request), LORA_EINVAL. */
+ * Errors: LORA_ENOMEM (no room: the caller has to stop or cut short some request to make room),
+ * LORA_EINVAL. */
 int lora_pool_grow_kv(lora_pool *pool, int64_t request_id, int32_t layers, int64_t *page_ids_out);
 
 /* Request finished: its KV pages return to the end of the free list.  Errors: LORA_ENOENT. */

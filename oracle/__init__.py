@@ -9,8 +9,8 @@ Sources (the pages this follows):
   * "S-LoRA, in depth" (aicassindra.com), section "Merge or keep adapters separate": the layer
     output for activation x is xW + (xA)B; merging gives W' = W + AB; unmerged serving batches xW
     over every request whatever its adapter.
-  * same page, section "The architecture": a gather step reads each request's A and B pages
-    wherever they sit in memory.
+  * same page, section "The architecture": a gather step fetches each request's A and B pages
+    from whatever places in memory hold them.
   * same page, section "Unified paging: adapters and KV cache in one pool" (with its worked
     example and its pool sketch): one page = one H-vector; a rank-R LoRA tensor takes R pages;
     KV and adapters share one free list.
@@ -30,12 +30,13 @@ from .projection import (  # noqa: F401
     project_loops,
 )
 from .pool import (  # noqa: F401
-    UnifiedPoolModel,
+    PagePoolModel,
+    Resident,
     adapter_bytes,
+    adapter_page_count,
     h2d_seconds,
     kv_bytes_per_token,
     kv_pages_per_token,
-    pages_for_adapter,
     tp_comm_lora,
     tp_comm_base,
 )

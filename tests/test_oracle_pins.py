@@ -232,4 +232,4 @@ def test_loops_and_numpy_agree_all_small_shapes():
 
 
 def test_exports():
-    assert callable(oracle.project) and callable(oracle.UnifiedPoolModel)
+    assert callable(oracle.project) and callable(oracle.PagePoolModel)

@@ -6,8 +6,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (UnifiedPoolModel, adapter_bytes, gather_page_ids, expected_page_rows,
-                    h2d_seconds, kv_bytes_per_token, kv_pages_per_token, pages_for_adapter,
+from oracle import (PagePoolModel, adapter_bytes, gather_page_ids, expected_page_rows,
+                    h2d_seconds, kv_bytes_per_token, kv_pages_per_token, adapter_page_count,
                     tp_comm_base, tp_comm_lora)
 
 KiB, MiB, GiB = 1024, 1024 ** 2, 1024 ** 3
@@ -34,8 +34,8 @@ def test_worked_example_kv(worked):
 
 def test_worked_example_adapter(worked):
     m, a = worked["model"], worked["adapter"]
-    assert pages_for_adapter(a["rank"], 1, a["projections"]) == worked["adapter_vectors_per_layer"]
-    assert pages_for_adapter(a["rank"], m["layers"], a["projections"]) == worked["adapter_vectors_total"]
+    assert adapter_page_count(a["rank"], 1, a["projections"]) == worked["adapter_vectors_per_layer"]
+    assert adapter_page_count(a["rank"], m["layers"], a["projections"]) == worked["adapter_vectors_total"]
     nbytes = adapter_bytes(a["rank"], m["layers"], a["projections"], m["hidden"], m["elem_bytes"])
     assert nbytes == worked["adapter_bytes"] == 32 * MiB
     kv = kv_bytes_per_token(m["layers"], m["hidden"], m["elem_bytes"])
@@ -64,23 +64,23 @@ def test_tensor_parallel_ratio(worked):
 
 def test_rank_slot_ratio(worked):
     r = worked["rank_slot_ratio"]
-    assert pages_for_adapter(r["big_rank"], 32, 4) == r["ratio"] * pages_for_adapter(r["small_rank"], 32, 4)
+    assert adapter_page_count(r["big_rank"], 32, 4) == r["ratio"] * adapter_page_count(r["small_rank"], 32, 4)
 
 
 def _apply(pool, step, n_slots):
     op = step["op"]
     if op == "load":
-        before = list(pool.free)
-        st = pool.ensure_adapter(step["aid"], step["rank"], n_slots)
-        taken = [] if st != "ok" or step["aid"] in pool.adapter_pages and pool.adapter_refs[step["aid"]] > 1 \
-            else pool.adapter_pages[step["aid"]]
+        before = list(pool.free_list)
+        st = pool.admit(step["aid"], step["rank"], n_slots)
+        res = pool.residents.get(step["aid"])
+        taken = [] if st != "ok" or res.users > 1 else res.pages
         return st, taken, before
     if op == "kv":
-        n0 = len(pool.kv_pages.get(step["rid"], []))
-        st = pool.grow_kv(step["rid"], step["layers"])
-        return st, pool.kv_pages.get(step["rid"], [])[n0:], None
+        n0 = len(pool.requests.get(step["rid"], []))
+        st = pool.add_kv_token(step["rid"], step["layers"])
+        return st, pool.requests.get(step["rid"], [])[n0:], None
     if op == "free_kv":
-        return pool.free_kv(step["rid"]), None, None
+        return pool.end_request(step["rid"]), None, None
     if op == "release":
         return pool.release(step["aid"]), None, None
     if op == "evict":
@@ -90,16 +90,16 @@ def _apply(pool, step, n_slots):
 
 def test_hand_derived_traces(traces):
     for tr in traces:
-        pool = UnifiedPoolModel(tr["num_pages"])
+        pool = PagePoolModel(tr["num_pages"])
         for step in tr["steps"]:
             st, taken, _ = _apply(pool, step, tr["n_slots"])
             assert st == step["status"], step
             if "pages" in step:
                 assert list(taken or []) == step["pages"], step
         fin = tr["final"]
-        assert pool.free == fin["free"]
-        assert list(pool.adapter_pages) == fin["resident_in_load_order"]
-        assert {str(k): v for k, v in pool.kv_pages.items()} == fin["kv"]
+        assert pool.free_list == fin["free"]
+        assert pool.resident_ids() == fin["resident_in_load_order"]
+        assert {str(k): v for k, v in pool.requests.items()} == fin["kv"]
         for key in [k for k in fin if k.startswith("page_table_slot")]:
             slot = int(key[len("page_table_slot"):])
             pt = pool.page_table(slot, tr["max_adapters"], tr["max_rank"])
@@ -111,26 +111,26 @@ def test_random_ops_invariants():
     rng = np.random.default_rng(0)
     for trial in range(20):
         n = int(rng.integers(10, 200))
-        pool = UnifiedPoolModel(n, rng.permutation(n))
+        pool = PagePoolModel(n, rng.permutation(n))
         n_slots = int(rng.integers(1, 4))
         for _ in range(200):
             k = rng.integers(0, 5)
             if k == 0:
-                pool.ensure_adapter(int(rng.integers(0, 8)), int(rng.integers(0, 5)), n_slots)
+                pool.admit(int(rng.integers(0, 8)), int(rng.integers(0, 5)), n_slots)
             elif k == 1:
-                pool.grow_kv(int(rng.integers(0, 6)), int(rng.integers(1, 3)))
+                pool.add_kv_token(int(rng.integers(0, 6)), int(rng.integers(1, 3)))
             elif k == 2:
-                pool.free_kv(int(rng.integers(0, 6)))
+                pool.end_request(int(rng.integers(0, 6)))
             elif k == 3:
                 pool.release(int(rng.integers(0, 8)))
             else:
                 pool.evict(int(rng.integers(0, 8)))
-            used = [p for v in pool.adapter_pages.values() for p in v] + [p for v in pool.kv_pages.values() for p in v]
-            every = used + pool.free
+            used = [p for r in pool.residents.values() for p in r.pages] + [p for v in pool.requests.values() for p in v]
+            every = used + pool.free_list
             assert sorted(every) == list(range(n))          # conserved and pairwise distinct
-            for aid, pages in pool.adapter_pages.items():
-                assert len(pages) == 2 * pool.adapter_rank[aid] * n_slots
-                assert pool.adapter_refs[aid] >= 0
+            for aid, res in pool.residents.items():
+                assert len(res.pages) == 2 * res.rank * n_slots
+                assert res.users >= 0
 
 
 def test_gather_ids_hand_table():
@@ -163,14 +163,14 @@ def test_expected_page_rows():
     ("load_order", [], 0), ("lru", [], 1), ("farthest", [1, 0, 2], 2), ("farthest", [1], 2),
     ("farthest", [2], 1), ("farthest", [], 1)])
 def test_victim_rules_hand_trace(victim, lookahead, evicted):
-    m = UnifiedPoolModel(12, victim=victim)
+    m = PagePoolModel(12, victim=victim)
     for a in (0, 1, 2, 0):
-        assert m.ensure_adapter(a, 2, 1) == "ok"
+        assert m.admit(a, 2, 1) == "ok"
         assert m.release(a) == "ok"
     m.set_lookahead(lookahead)
-    assert m.ensure_adapter(3, 2, 1) == "ok"
-    assert sorted(m.adapter_pages) == sorted({0, 1, 2, 3} - {evicted})
-    assert len(m.free) == 0
+    assert m.admit(3, 2, 1) == "ok"
+    assert sorted(m.resident_ids()) == sorted({0, 1, 2, 3} - {evicted})
+    assert len(m.free_list) == 0
 
 
 def _min_loads(seq, cap):
@@ -194,13 +194,13 @@ def _min_loads(seq, cap):
 def _loads(seq, cap, victim, foresight=None):
     """Loads the pool model makes serving `seq` (admit, then release, each request), adapters of
     rank 1 on one slot (2 pages each), `cap` of them fitting."""
-    m = UnifiedPoolModel(2 * cap, victim=victim)
+    m = PagePoolModel(2 * cap, victim=victim)
     n = 0
     for i, a in enumerate(seq):
         rest = seq[i + 1:]
         m.set_lookahead(rest if foresight is None else rest[:foresight])
-        n += a not in m.adapter_pages
-        assert m.ensure_adapter(a, 1, 1) == "ok"
+        n += a not in m.residents
+        assert m.admit(a, 1, 1) == "ok"
         assert m.release(a) == "ok"
     return n
 

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import UnifiedPoolModel
+from oracle import PagePoolModel
 from workloads import build, custom, round_to_bf16
 
 
@@ -64,7 +64,7 @@ def test_stack_rows():
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "many"])
 def test_pool_plans_fit(name):
     w = build(name)
-    pool = UnifiedPoolModel(w.num_pages, w.free_order)
+    pool = PagePoolModel(w.num_pages, w.free_order)
     assert all(s == "ok" for s in pool.run(w.ops, w.ranks, w.n_slots))
     st = pool.stats()
     assert 0.5 <= st["kv_pages"] / st["num_pages"] <= 0.61
@@ -75,7 +75,7 @@ def test_pool_plans_fit(name):
 def test_stack_plan_churn_and_fragmentation():
     t0 = time.time()
     w = build("stack13b")
-    pool = UnifiedPoolModel(w.num_pages, w.free_order)
+    pool = PagePoolModel(w.num_pages, w.free_order)
     st = pool.run(w.ops, w.ranks, w.n_slots)
     assert all(s == "ok" for s in st)
     assert sum(1 for o in w.ops if o[0] == "evict") > 100
