@@ -90,15 +90,23 @@ def traffic_from_profiles(kernel_key, src_file, launches_bytes_ok=True):
 
 
 def cpu_baseline(w, seconds, slots):
-    """The fp64 oracle, as it stands, on this host's cores: full batch of one projection, repeated."""
+    """The fp64 oracle, as it stands, on this host's cores: full batch of one projection, repeated.
+
+    BLAS threads: the cores this process may run on (sched_getaffinity), capped by OMP_NUM_THREADS
+    when the host sets it (the GPU hosts give each GPU a share of their cores and set it to that share);
+    `cores` is the thread count the BLAS pool then reports."""
     import numpy as np
     import oracle
     from workloads import storage_to_f64
+    affinity = len(os.sched_getaffinity(0))
+    want = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity))
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=want, user_api="blas")
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [want])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        cores = want
     slot = 0
     x64 = storage_to_f64(w.x_for_slot(slot))
     W64 = storage_to_f64(w.W(slot)).T
@@ -115,7 +123,10 @@ def cpu_baseline(w, seconds, slots):
         if el >= seconds:
             break
     tokens_per_s = n * w.T / el / slots      # a step pushes T tokens through `slots` projections
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(cores), "affinity_cores": affinity,
+            "kind": "oracle",
             "sample": f"full {w.T}-token batch of one projection (slot 0), {n} repeats in {el:.1f} s, "
                       f"scaled to {slots} projection(s) per step"}
 
