@@ -279,10 +279,33 @@ int lora_project_slots(lora_pool *pool, int32_t n, const int32_t *slots, const v
                        size_t workspace_bytes, void *stream);
 
 /*
- * Debug view of the gather: for every token t (input order) writes the pages its projection reads
- * into page_ids_out[t][0..2*max_rank) (device int32): entries 0..r-1 its A columns, r..2r-1 its B
- * rows, -1 elsewhere and for tokens with no adapter or rank 0.  Same inputs and device checks as
- * lora_project (an invalid token gets all -1).  Enqueued on `stream`.
+ * The projection with its own indices exposed ("S-LoRA, in depth", section "The architecture": the
+ * gather fetches each request's A and B pages from wherever the pool placed them).  Runs exactly the
+ * kernels lora_project runs for these arguments -- in instantiations that also record the indices
+ * they use -- and writes y bit for bit as lora_project does.  In addition (device int32, caller-owned,
+ * 4-byte aligned, filled with -1 by the call first):
+ *   gather_out   [T][2*max_rank], input token order: entry j < r is the page whose A column the
+ *                shrink multiplied into token t's v[j]; entry r + j the page whose B row the expand
+ *                multiplied into token t's y; -1 elsewhere (no adapter, rank 0, past the rank).  An
+ *                entry that two workgroups or kernels filled with different pages reads -2.
+ *   order_out    [T][2], per sorted position q (the grouping the kernels consumed): the token at q
+ *                and the adapter of its segment.  T <= 256 (bfloat16): every token, the ones with a
+ *                low-rank term first, grouped by adapter in order of first token, then the others
+ *                with adapter -1.  Otherwise: positions [0, n) hold the n tokens with a low-rank term,
+ *                grouped by adapter in adapter order; the rest stay (-1, -1).
+ * Other arguments, checks and errors as lora_project.  For tests and debugging; not a fast path.
+ */
+int lora_debug_project(lora_pool *pool, const void *x, const void *W, const int32_t *page_table,
+                       const int32_t *adapter_ids, const int32_t *ranks, const float *scale, int64_t T,
+                       void *y, void *workspace, size_t workspace_bytes, int32_t *gather_out,
+                       int32_t *order_out, void *stream);
+
+/*
+ * Page-table view of the gather (no projection): for every token t (input order) writes the table
+ * entries its adapter owns into page_ids_out[t][0..2*max_rank) (device int32): entries 0..r-1 its A
+ * columns, r..2r-1 its B rows, -1 elsewhere and for tokens with no adapter or rank 0.  Same inputs
+ * and device checks as lora_project (an invalid token gets all -1).  Enqueued on `stream`.  The
+ * pages the projection's kernels themselves read come from lora_debug_project.
  */
 int lora_debug_gather(lora_pool *pool, const int32_t *page_table, const int32_t *adapter_ids,
                       const int32_t *ranks, int64_t T, int32_t *page_ids_out, void *stream);

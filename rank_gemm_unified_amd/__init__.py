@@ -75,6 +75,7 @@ _SIGS = {
     "lora_project_slots": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_debug_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "lora_debug_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp]),
     "lora_check_device_errors": (ctypes.c_int, [_vp]),
     "lora_profile_start": (ctypes.c_int, [_vp, _i32]),
     "lora_profile_stop": (ctypes.c_int, [_vp, ctypes.POINTER(lora_profile_t)]),
@@ -288,6 +289,16 @@ def lora_debug_gather(pool, page_table, adapter_ids, ranks, T, out, stream=None,
     rc = _lib.lora_debug_gather(pool, _ptr(page_table), _ptr(adapter_ids), _ptr(ranks), T, _ptr(out),
                                 _stream(stream))
     return _check(rc, "lora_debug_gather") if check else rc
+
+
+def lora_debug_project(pool, x, W, page_table, adapter_ids, ranks, scale, T, y, workspace, gather_out, order_out,
+                       workspace_bytes=None, stream=None, check=True):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.lora_debug_project(pool, _ptr(x), _ptr(W), _ptr(page_table), _ptr(adapter_ids), _ptr(ranks),
+                                 _ptr(scale), T, _ptr(y), _ptr(workspace), workspace_bytes, _ptr(gather_out),
+                                 _ptr(order_out), _stream(stream))
+    return _check(rc, "lora_debug_project") if check else rc
 
 
 def lora_check_device_errors(pool, check=True):

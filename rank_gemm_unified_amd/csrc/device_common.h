@@ -84,6 +84,14 @@ __device__ __forceinline__ int wave_sum_int(int v) {
     return v;
 }
 
+// Debug instantiations record each page id where a kernel uses it.  The first writer of an entry
+// sets it; a writer that finds a different value marks the entry -2, so two workgroups (or two
+// kernels) that used different pages for the same token and j cannot hide one another.
+__device__ __forceinline__ void dbg_put(int32_t *p, int32_t v) {
+    const int32_t old = atomicCAS(p, -1, v);
+    if (old != -1 && old != v) atomicExch(p, -2);
+}
+
 // Check adapter a's page-table row against rank r: entries [0, 2r) must be page ids in
 // [0, num_pages) and, when 2r < stride, entry 2r must be -1 (so r is the loaded rank).
 // `j` is this thread's entry (threads of a group cover the row together); returns error bits.

@@ -140,6 +140,14 @@ struct SlotRows {   // the page tables alone (the grouping kernel checks every s
     const int32_t *pt[MAX_CALL_SLOTS];
 };
 
+// Outputs of the debug instantiations of the kernels (lora_debug_project): every kernel that reads a
+// page for a token records the page id where it uses it, and the kernels that consume the token
+// grouping record it.  Both buffers are filled with -1 before the launches.
+struct DebugOut {
+    int32_t *gather;   // [T][2 max_rank], token order: A pages 0..r-1, B pages r..2r-1
+    int32_t *order;    // [T][2]: per sorted position, the token and its segment's adapter (-1: none)
+};
+
 // ctrl[] slots written by the segment kernel
 enum : int { CTRL_NSEG = 0, CTRL_NITEMS = 1, CTRL_NVALID = 2, CTRL_WORDS = 64 };
 
@@ -160,15 +168,17 @@ hipError_t launch_debug_gather(const lora_pool *p, const int32_t *pt, const int3
                                const int32_t *ranks, int64_t T, int32_t *out, hipStream_t s);
 hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
                               const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n,
-                              hipStream_t s);
+                              hipStream_t s, const DebugOut *dbg = nullptr);
 hipError_t launch_decode(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
                          const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
-                         hipEvent_t mid);
+                         hipEvent_t mid, const DebugOut *dbg = nullptr);
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
-                          const float *scale, const SlotPtrs &sp, int n, hipStream_t s, hipEvent_t mid);
+                          const float *scale, const SlotPtrs &sp, int n, hipStream_t s, hipEvent_t mid,
+                          const DebugOut *dbg = nullptr);
 hipError_t launch_f32(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x,
                       const void *W, const int32_t *pt, const float *scale, void *y,
-                      hipStream_t s, hipEvent_t mid);
+                      hipStream_t s, hipEvent_t mid, const DebugOut *dbg = nullptr);
+hipError_t launch_fill_i32(int32_t *dst, int64_t n, int32_t value, hipStream_t s);
 
 struct DeviceGuard {
     int prev = -1;

@@ -17,6 +17,8 @@
 //
 // The float32 path (parity-only, small shapes) keeps the grouping kernel, a gathered shrink and a
 // plain VALU kernel.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -148,14 +150,14 @@ struct StreamShape {
     static constexpr size_t LDS = 4 * REGION + PBYTES + GBYTES;
 };
 
-template <int MB, int KQ>
+template <int MB, int KQ, bool DBG>
 __device__ __forceinline__ void decode_stream_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
     int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
     float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
-    int *__restrict__ err_word) {
+    int *__restrict__ err_word, int32_t *__restrict__ dbg_gather) {
     using SH = StreamShape<MB, KQ>;
     constexpr int TP = SH::TP, P = SH::P, RS = SH::RS, PS = SH::PS;
     constexpr int SWZ = P < 16 ? P - 1 : 15;          // piece c of row r sits in slot c ^ (r & SWZ)
@@ -362,7 +364,7 @@ __device__ __forceinline__ void decode_stream_body(
     // thread -> column lrow (its own lane's page), rows lane/16 + 4 (wave + 4 u); the partial of wave
     // w, row t sits at part(w) + t * pstride
     auto page_store = [&](const float *part0, size_t wstride, int pstride, bool live_col, int32_t a_col,
-                          int32_t j_col) {
+                          int32_t j_col, int32_t pid_col) {
         float v[MB];
 #pragma unroll
         for (int u = 0; u < MB; ++u) {
@@ -374,7 +376,10 @@ __device__ __forceinline__ void decode_stream_body(
         for (int u = 0; u < MB; ++u) {
             const int t = lq + 4 * (wave + 4 * u);
             const int32_t key_t = __shfl(key, t & 63, 64);
-            if (live_col && t < T && key_t == a_col) vpart[((int64_t)t * RP + j_col) * S + split] = v[u];
+            if (live_col && t < T && key_t == a_col) {
+                vpart[((int64_t)t * RP + j_col) * S + split] = v[u];
+                if constexpr (DBG) dbg_put(dbg_gather + (int64_t)t * stride + j_col, pid_col);
+            }
         }
     };
     f32x4_t pacc0[MB];
@@ -405,7 +410,7 @@ __device__ __forceinline__ void decode_stream_body(
 #pragma unroll
             for (int i = 0; i < 4; ++i) pred[((size_t)wave * TP + m * 16 + lq * 4 + i) * PS + lrow] = pacc[m][i];
         __syncthreads();
-        page_store(pred, (size_t)TP * PS, PS, live, a2, j2);
+        page_store(pred, (size_t)TP * PS, PS, live, a2, j2, pg);
         __syncthreads();
     }
 
@@ -444,7 +449,7 @@ __device__ __forceinline__ void decode_stream_body(
             const int e = threadIdx.x + 256 * u, t = e >> 4;
             if (t < T) __builtin_nontemporal_store(v[u], reinterpret_cast<f32x4_t *>(ypart + ((int64_t)split * T + t) * H + n0 + 4 * (e & 15)));
         }
-        page_store(red + TP * RS, WS, PS, plive, pa, pj);
+        page_store(red + TP * RS, WS, PS, plive, pa, pj, pid);
     }
 
     // ---- publish (wave 0): segments s = blockIdx.x + k gridDim.x -- check the page-table row, then
@@ -501,8 +506,21 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream(
     int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
     float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
     int *__restrict__ err_word) {
-    decode_stream_body<MB, KQ>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T, H, S,
-                               n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word);
+    decode_stream_body<MB, KQ, false>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T,
+                                      H, S, n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word, nullptr);
+}
+
+// The debug instantiation (lora_debug_project): the same body, recording the A pages it reads per token.
+template <int MB, int KQ>
+__global__ __launch_bounds__(256, 1) void k_decode_stream_dbg(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
+    int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
+    float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
+    int *__restrict__ err_word, int32_t *__restrict__ dbg_gather) {
+    decode_stream_body<MB, KQ, true>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T,
+                                     H, S, n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word, dbg_gather);
 }
 
 template <int MB, int KQ>
@@ -512,9 +530,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream_slots(
     int32_t max_adapters, int32_t max_rank, int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP,
     int *__restrict__ err_word) {
     const int z = blockIdx.z;
-    decode_stream_body<MB, KQ>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks, scale,
-                               max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
-                               (int4 *)sp.sorted_tok[z], sp.spages[z], err_word);
+    decode_stream_body<MB, KQ, false>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks,
+                                      scale, max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
+                                      (int4 *)sp.sorted_tok[z], sp.spages[z], err_word, nullptr);
 }
 
 // ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
@@ -525,11 +543,12 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream_slots(
 //     partials of two j's (summed in split order into LDS).
 // The four quarter threads of a token then add their x W partials and expand terms by two lane
 // shuffles (a fixed order), and one of them rounds and stores.
-template <int SY, int SV>
+template <int SY, int SV, bool DBG>
 __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sorted_tok, const int32_t *__restrict__ spages,
                                                    const float *__restrict__ ypart, const float *__restrict__ vpart,
                                                    int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
-                                                   int32_t H, int32_t T, uint16_t *__restrict__ y) {
+                                                   int32_t H, int32_t T, uint16_t *__restrict__ y,
+                                                   const DebugOut dbg = DebugOut{}, int32_t stride = 0) {
     constexpr int SQ = (SY + 3) / 4;   // x W splits per quarter thread
     __shared__ float s_v[8][64];
     const int n0 = blockIdx.x * 64;
@@ -558,6 +577,17 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
     const int r = has ? st.z : 0;
     const int j0 = 16 * q;
     const bool qlive = has && j0 < r;
+    if constexpr (DBG) {   // the B pages this thread multiplies into the token's output, and the grouping it used
+        if (live_tok) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (qlive && j0 + u < r) dbg_put(dbg.gather + (int64_t)t * stride + r + j0 + u, pid[u]);
+            if (q == 0 && c == 0) {
+                dbg_put(dbg.order + 2 * sp, t);
+                dbg_put(dbg.order + 2 * sp + 1, a);
+            }
+        }
+    }
     // ---- round trip 2 (every load unconditional, stand-in addresses for dead entries)
     u32x4_t bv[16];
     uint32_t okm = 0;   // rows whose page id is in range
@@ -633,7 +663,17 @@ __global__ __launch_bounds__(256) void k_decode_finish(const int4 *__restrict__ 
                                                        const float *__restrict__ ypart, const float *__restrict__ vpart,
                                                        int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
                                                        int32_t H, int32_t T, uint16_t *__restrict__ y) {
-    decode_finish_body<SY, SV>(sorted_tok, spages, ypart, vpart, RP, pages, num_pages, H, T, y);
+    decode_finish_body<SY, SV, false>(sorted_tok, spages, ypart, vpart, RP, pages, num_pages, H, T, y);
+}
+
+template <int SY, int SV>
+__global__ __launch_bounds__(256) void k_decode_finish_dbg(const int4 *__restrict__ sorted_tok,
+                                                           const int32_t *__restrict__ spages,
+                                                           const float *__restrict__ ypart, const float *__restrict__ vpart,
+                                                           int32_t RP, const uint16_t *__restrict__ pages,
+                                                           int64_t num_pages, int32_t H, int32_t T,
+                                                           uint16_t *__restrict__ y, const DebugOut dbg, int32_t stride) {
+    decode_finish_body<SY, SV, true>(sorted_tok, spages, ypart, vpart, RP, pages, num_pages, H, T, y, dbg, stride);
 }
 
 template <int SY, int SV>
@@ -641,17 +681,18 @@ __global__ __launch_bounds__(256) void k_decode_finish_slots(const SlotPtrs sl, 
                                                              const uint16_t *__restrict__ pages, int64_t num_pages,
                                                              int32_t H, int32_t T) {
     const int z = blockIdx.z;
-    decode_finish_body<SY, SV>((const int4 *)sl.sorted_tok[z], sl.spages[z], sl.ypart[z], sl.v[z], RP, pages,
-                               num_pages, H, T, (uint16_t *)sl.y[z]);
+    decode_finish_body<SY, SV, false>((const int4 *)sl.sorted_tok[z], sl.spages[z], sl.ypart[z], sl.v[z], RP, pages,
+                                      num_pages, H, T, (uint16_t *)sl.y[z]);
 }
 
 // ---- float32 pools: grouping kernel + gathered shrink + plain VALU kernel ---------------------------
+template <bool DBG>
 __global__ __launch_bounds__(256) void k_shrink_items_f32(
     const char *__restrict__ x, const char *__restrict__ pages, int32_t H, const int32_t *__restrict__ pt,
     int32_t stride, const float *__restrict__ scale, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ seg_a, const int32_t *__restrict__ seg_start, const int32_t *__restrict__ item_seg,
     const int32_t *__restrict__ item_row, const int32_t *__restrict__ ctrl, const int32_t *__restrict__ tok_r,
-    float *__restrict__ v, int32_t R) {
+    float *__restrict__ v, int32_t R, const DebugOut dbg) {
     const int item = blockIdx.x;
     if (item >= ctrl[CTRL_NITEMS]) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -665,16 +706,25 @@ __global__ __launch_bounds__(256) void k_shrink_items_f32(
 #pragma unroll
     for (int i = 0; i < CHUNK; ++i) tok[i] = i < n ? perm[row0 + i] : 0;
     const int64_t row_bytes = (int64_t)H * 4;
-    shrink_page_wave<4>(x, pages + (int64_t)pt[(int64_t)a * stride + j] * row_bytes, row_bytes, tok, n, scale[a], j,
-                        v, R, lane);
+    const int32_t pg = pt[(int64_t)a * stride + j];
+    if constexpr (DBG) {   // the A page this wave multiplies into its tokens' v[j], and the grouping
+        if (lane < n) {
+            dbg_put(dbg.gather + (int64_t)tok[lane] * stride + j, pg);
+            dbg_put(dbg.order + 2 * (row0 + lane), tok[lane]);
+            dbg_put(dbg.order + 2 * (row0 + lane) + 1, a);
+        }
+    }
+    shrink_page_wave<4>(x, pages + (int64_t)pg * row_bytes, row_bytes, tok, n, scale[a], j, v, R, lane);
 }
 
 // Grid (H/64 column tiles, ceil(T/16) token blocks); thread -> one token, 4 columns.
+template <bool DBG>
 __global__ __launch_bounds__(256) void k_project_f32(const float *__restrict__ x, const float *__restrict__ W,
                                                      const float *__restrict__ pages, const int32_t *__restrict__ pt,
                                                      int32_t stride, const int32_t *__restrict__ tok_a,
                                                      const int32_t *__restrict__ tok_r, const float *__restrict__ v,
-                                                     int32_t R, int32_t T, int32_t H, float *__restrict__ y) {
+                                                     int32_t R, int32_t T, int32_t H, float *__restrict__ y,
+                                                     const DebugOut dbg) {
     const int t = blockIdx.y * 16 + (threadIdx.x >> 4);
     const int n = blockIdx.x * 64 + (threadIdx.x & 15) * 4;
     if (t >= T) return;
@@ -694,6 +744,7 @@ __global__ __launch_bounds__(256) void k_project_f32(const float *__restrict__ x
         const int32_t r = tok_r[t];
         const int32_t *prow = pt + (int64_t)a * stride + r;
         for (int32_t j = 0; j < r; ++j) {
+            if constexpr (DBG) dbg_put(dbg.gather + (int64_t)t * stride + r + j, prow[j]);
             const f32x4_t b = *reinterpret_cast<const f32x4_t *>(pages + (int64_t)prow[j] * H + n);
             const float vj = v[(int64_t)t * R + j];
 #pragma unroll
@@ -706,7 +757,8 @@ __global__ __launch_bounds__(256) void k_project_f32(const float *__restrict__ x
 // ---- launchers -----------------------------------------------------------------------------------------
 template <int MB, int KQ>
 static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
-                                const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s) {
+                                const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
+                                const DebugOut *dbg) {
     constexpr size_t lds = StreamShape<MB, KQ>::LDS;
     static_assert(lds <= 160 * 1024, "stream kernel LDS");
     static bool attr_set = false;
@@ -716,10 +768,19 @@ static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const void
         if (e == hipSuccess)
             e = hipFuncSetAttribute((const void *)k_decode_stream_slots<MB, KQ>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)k_decode_stream_dbg<MB, KQ>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    if (n == 1)
+    if (dbg)
+        hipLaunchKernelGGL((k_decode_stream_dbg<MB, KQ>), dim3(plan.n_tiles * plan.ysplit), dim3(256), lds, s,
+                           (const uint16_t *)x, (const uint16_t *)sp.W[0], (const uint16_t *)p->pages, p->num_pages,
+                           sp.pt[0], 2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank,
+                           (int32_t)plan.T, p->hidden, plan.ysplit, plan.n_tiles, plan.rp, sp.ypart[0], sp.v[0],
+                           (int4 *)sp.sorted_tok[0], sp.spages[0], p->dev_err, dbg->gather);
+    else if (n == 1)
         hipLaunchKernelGGL((k_decode_stream<MB, KQ>), dim3(plan.n_tiles * plan.ysplit), dim3(256), lds, s,
                            (const uint16_t *)x, (const uint16_t *)sp.W[0], (const uint16_t *)p->pages, p->num_pages,
                            sp.pt[0], 2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank,
@@ -734,9 +795,14 @@ static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const void
 }
 
 template <int SY, int SV>
-static void launch_finish_t(const lora_pool *p, const Plan &plan, const SlotPtrs &sp, int n, hipStream_t s) {
+static void launch_finish_t(const lora_pool *p, const Plan &plan, const SlotPtrs &sp, int n, hipStream_t s,
+                            const DebugOut *dbg) {
     dim3 grid(p->hidden / 64, (unsigned)((plan.T + 7) / 8), n);
-    if (n == 1)
+    if (dbg)
+        hipLaunchKernelGGL((k_decode_finish_dbg<SY, SV>), grid, dim3(256), 0, s, (const int4 *)sp.sorted_tok[0],
+                           sp.spages[0], sp.ypart[0], sp.v[0], plan.rp, (const uint16_t *)p->pages, p->num_pages,
+                           p->hidden, (int32_t)plan.T, (uint16_t *)sp.y[0], *dbg, 2 * p->max_rank);
+    else if (n == 1)
         hipLaunchKernelGGL((k_decode_finish<SY, SV>), grid, dim3(256), 0, s, (const int4 *)sp.sorted_tok[0],
                            sp.spages[0], sp.ypart[0], sp.v[0], plan.rp, (const uint16_t *)p->pages, p->num_pages,
                            p->hidden, (int32_t)plan.T, (uint16_t *)sp.y[0]);
@@ -745,10 +811,11 @@ static void launch_finish_t(const lora_pool *p, const Plan &plan, const SlotPtrs
                            (const uint16_t *)p->pages, p->num_pages, p->hidden, (int32_t)plan.T);
 }
 
-static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const SlotPtrs &sp, int n, hipStream_t s) {
+static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const SlotPtrs &sp, int n, hipStream_t s,
+                                const DebugOut *dbg) {
     const int sy = plan.ysplit, sv = plan.ysplit;   // both decode kernels write S v partials
     switch (sy * 16 + sv) {
-#define LP_CASE(A, B) case A * 16 + B: launch_finish_t<A, B>(p, plan, sp, n, s); break;
+#define LP_CASE(A, B) case A * 16 + B: launch_finish_t<A, B>(p, plan, sp, n, s, dbg); break;
         LP_CASE(1, 1) LP_CASE(2, 1) LP_CASE(4, 1) LP_CASE(8, 1)
         LP_CASE(2, 2) LP_CASE(3, 3) LP_CASE(4, 4) LP_CASE(5, 5) LP_CASE(6, 6) LP_CASE(7, 7) LP_CASE(8, 8)
 #undef LP_CASE
@@ -759,11 +826,11 @@ static hipError_t launch_finish(const lora_pool *p, const Plan &plan, const Slot
 
 hipError_t launch_decode(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
                          const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
-                         hipEvent_t mid) {
+                         hipEvent_t mid, const DebugOut *dbg) {
     hipError_t e;
     if (plan.stream) {
         switch (plan.mb * 64 + plan.ks) {
-#define LP_CASE(M, K) case M * 64 + K: e = launch_stream<M, K>(p, plan, x, ids, ranks, scale, sp, n, s); break;
+#define LP_CASE(M, K) case M * 64 + K: e = launch_stream<M, K>(p, plan, x, ids, ranks, scale, sp, n, s, dbg); break;
             LP_CASE(1, 1) LP_CASE(1, 2) LP_CASE(1, 4) LP_CASE(1, 8)
             LP_CASE(2, 1) LP_CASE(2, 2) LP_CASE(2, 4) LP_CASE(2, 8)
             LP_CASE(3, 1) LP_CASE(3, 2) LP_CASE(3, 4) LP_CASE(3, 8)
@@ -772,26 +839,40 @@ hipError_t launch_decode(const lora_pool *p, const Plan &plan, const void *x, co
             default: return hipErrorInvalidValue;
         }
     } else {
-        e = launch_decode_wide(p, plan, x, ids, ranks, scale, sp, n, s);
+        e = launch_decode_wide(p, plan, x, ids, ranks, scale, sp, n, s, dbg);
     }
     if (e != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
-    return launch_finish(p, plan, sp, n, s);
+    return launch_finish(p, plan, sp, n, s, dbg);
 }
 
 hipError_t launch_f32(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const void *W,
-                      const int32_t *pt, const float *scale, void *y, hipStream_t s, hipEvent_t mid) {
+                      const int32_t *pt, const float *scale, void *y, hipStream_t s, hipEvent_t mid,
+                      const DebugOut *dbg) {
+    const DebugOut d = dbg ? *dbg : DebugOut{};
     dim3 g1(plan.n_items_max, (p->max_rank + 3) / 4);
-    hipLaunchKernelGGL(k_shrink_items_f32, g1, dim3(256), 0, s, (const char *)x, (const char *)p->pages, p->hidden,
-                       pt, 2 * p->max_rank, scale, ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.ctrl,
-                       ws.tok_r, ws.v, p->max_rank);
+    hipLaunchKernelGGL(dbg ? k_shrink_items_f32<true> : k_shrink_items_f32<false>, g1, dim3(256), 0, s,
+                       (const char *)x, (const char *)p->pages, p->hidden, pt, 2 * p->max_rank, scale, ws.perm,
+                       ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.ctrl, ws.tok_r, ws.v, p->max_rank, d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
     dim3 grid(p->hidden / 64, (unsigned)((plan.T + 15) / 16));
-    hipLaunchKernelGGL(k_project_f32, grid, dim3(256), 0, s, (const float *)x, (const float *)W,
-                       (const float *)p->pages, pt, 2 * p->max_rank, ws.tok_a, ws.tok_r, ws.v, p->max_rank,
-                       (int32_t)plan.T, p->hidden, (float *)y);
+    hipLaunchKernelGGL(dbg ? k_project_f32<true> : k_project_f32<false>, grid, dim3(256), 0, s, (const float *)x,
+                       (const float *)W, (const float *)p->pages, pt, 2 * p->max_rank, ws.tok_a, ws.tok_r, ws.v,
+                       p->max_rank, (int32_t)plan.T, p->hidden, (float *)y, d);
+    return hipGetLastError();
+}
+
+// Fill n int32 entries with `value` (the debug outputs start at -1).
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ dst, int64_t n, int32_t value) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = value;
+}
+
+hipError_t launch_fill_i32(int32_t *dst, int64_t n, int32_t value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)blocks), dim3(256), 0, s, dst, n, value);
     return hipGetLastError();
 }
 

@@ -74,14 +74,14 @@ __device__ __forceinline__ int last_leq(const int32_t *off, int n, int32_t i) {
 }  // namespace wide
 using namespace wide;
 
-template <int MB16>
+template <int MB16, bool DBG>
 __device__ __forceinline__ void decode_wide_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
     int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
     float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
-    int *__restrict__ err_word) {
+    int *__restrict__ err_word, int32_t *__restrict__ dbg_gather) {
     constexpr int TP = MB16 * 16;           // padded token rows
     constexpr int MBW = MB16 / NW;          // 16-row blocks per wave
     constexpr int XSTAGE = TP * KC;         // elements per x stage
@@ -293,6 +293,7 @@ __device__ __forceinline__ void decode_wide_body(
         int32_t u_seg[UPW], u_pb[UPW], u_tc[UPW];
         bool u_live[UPW];
         const uint16_t *upr[UPW];
+        int32_t u_pid[UPW];
         int u_row[UPW];
         float u_sc[UPW];
 #pragma unroll
@@ -308,6 +309,7 @@ __device__ __forceinline__ void decode_wide_body(
             const int j = u_pb[e] * 16 + lrow, it = u_tc[e] * 16 + lrow;
             u_row[e] = g.sorted[u_live[e] ? to + min(it, ns - 1) : 0];
             const int32_t pid = pt[u_live[e] && j < rs ? (int64_t)a * stride + j : 0];
+            u_pid[e] = pid;
             const bool pok = u_live[e] && j < rs && pid >= 0 && (int64_t)pid < num_pages;
             upr[e] = pok ? pages + (int64_t)pid * H + kb + lq * 8 : x + lq * 8;
             u_sc[e] = scale[u_live[e] ? a : 0];
@@ -407,6 +409,7 @@ __device__ __forceinline__ void decode_wide_body(
                 if (j < rs && it < ns) {
                     const int t = g.sorted[to + it];
                     vpart[((int64_t)t * RP + j) * S + split] = u_sc[e] * uacc[e][i];
+                    if constexpr (DBG) dbg_put(dbg_gather + (int64_t)t * stride + j, u_pid[e]);
                 }
             }
         }
@@ -474,8 +477,21 @@ __global__ __launch_bounds__(NTH, 1) void k_decode_wide(
     int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
     float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
     int *__restrict__ err_word) {
-    decode_wide_body<MB16>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T, H, S,
-                           n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word);
+    decode_wide_body<MB16, false>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T, H,
+                                  S, n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word, nullptr);
+}
+
+// The debug instantiation (lora_debug_project): the same body, recording the A pages it reads per token.
+template <int MB16>
+__global__ __launch_bounds__(NTH, 1) void k_decode_wide_dbg(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    int64_t num_pages, const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, const float *__restrict__ scale, int32_t max_adapters, int32_t max_rank,
+    int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP, float *__restrict__ ypart,
+    float *__restrict__ vpart, int4 *__restrict__ sorted_tok, int32_t *__restrict__ spages,
+    int *__restrict__ err_word, int32_t *__restrict__ dbg_gather) {
+    decode_wide_body<MB16, true>(x, W, pages, num_pages, pt, stride, ids, ranks, scale, max_adapters, max_rank, T, H,
+                                 S, n_tiles, RP, ypart, vpart, sorted_tok, spages, err_word, dbg_gather);
 }
 
 template <int MB16>
@@ -485,16 +501,17 @@ __global__ __launch_bounds__(NTH, 1) void k_decode_wide_slots(
     int32_t max_adapters, int32_t max_rank, int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP,
     int *__restrict__ err_word) {
     const int z = blockIdx.z;
-    decode_wide_body<MB16>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks, scale,
-                           max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
-                           (int4 *)sp.sorted_tok[z], sp.spages[z], err_word);
+    decode_wide_body<MB16, false>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks, scale,
+                                  max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
+                                  (int4 *)sp.sorted_tok[z], sp.spages[z], err_word, nullptr);
 }
 
 size_t decode_wide_lds(int mb16) { return (size_t)(NSTAGE * mb16 * 16 + NWS * 64) * KC * 2 + sizeof(WideGroup); }
 
 template <int MB16>
 static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
-                                const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s) {
+                                const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
+                                const DebugOut *dbg) {
     static bool attr_set = false;
     const size_t lds = decode_wide_lds(MB16);
     if (!attr_set) {
@@ -503,11 +520,20 @@ static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const void
         if (e == hipSuccess)
             e = hipFuncSetAttribute((const void *)k_decode_wide_slots<MB16>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)k_decode_wide_dbg<MB16>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     dim3 grid((unsigned)(plan.n_tiles * plan.ysplit), 1, n);
-    if (n == 1)
+    if (dbg)
+        hipLaunchKernelGGL((k_decode_wide_dbg<MB16>), dim3(grid.x), dim3(NTH), lds, s, (const uint16_t *)x,
+                           (const uint16_t *)sp.W[0], (const uint16_t *)p->pages, p->num_pages, sp.pt[0],
+                           2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T,
+                           p->hidden, plan.ysplit, plan.n_tiles, plan.rp, sp.ypart[0], sp.v[0],
+                           (int4 *)sp.sorted_tok[0], sp.spages[0], p->dev_err, dbg->gather);
+    else if (n == 1)
         hipLaunchKernelGGL((k_decode_wide<MB16>), grid, dim3(NTH), lds, s, (const uint16_t *)x,
                            (const uint16_t *)sp.W[0], (const uint16_t *)p->pages, p->num_pages, sp.pt[0],
                            2 * p->max_rank, ids, ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T,
@@ -522,10 +548,11 @@ static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const void
 }
 
 hipError_t launch_decode_wide(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
-                              const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s) {
+                              const int32_t *ranks, const float *scale, const SlotPtrs &sp, int n, hipStream_t s,
+                              const DebugOut *dbg) {
     switch (plan.mb) {
-        case 8: return launch_wide_t<8>(p, plan, x, ids, ranks, scale, sp, n, s);
-        case 16: return launch_wide_t<16>(p, plan, x, ids, ranks, scale, sp, n, s);
+        case 8: return launch_wide_t<8>(p, plan, x, ids, ranks, scale, sp, n, s, dbg);
+        case 16: return launch_wide_t<16>(p, plan, x, ids, ranks, scale, sp, n, s, dbg);
         default: return hipErrorInvalidValue;
     }
 }

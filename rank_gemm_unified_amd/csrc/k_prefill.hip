@@ -38,15 +38,17 @@ constexpr int SK = 64;                                  // K tile
 constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements (16 KiB)
 __device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ ((r >> 1) & 7)) << 3); }   // as swz
 
-template <int SNS>
+template <int SNS, bool DBG>
 __device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H,
                                               const int32_t *__restrict__ pt, int32_t stride,
                                               const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
-                                              float *__restrict__ vpart, int32_t T, int32_t R) {
+                                              float *__restrict__ vpart, int32_t T, int32_t R,
+                                              const DebugOut dbg = DebugOut{}) {
     const int4 rec = item_rec[blockIdx.x];
     if (rec.x < 0) return;   // past the last work item
     extern __shared__ __align__(16) uint16_t st[];   // SNS stages
     __shared__ int32_t s_perm[SH_ROWS];
+    __shared__ int32_t s_pid[DBG ? SH_ROWS : 1];     // debug: the page of each column of v
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int32_t a = rec.x, r = rec.y, row0 = rec.z, n = rec.w;   // 1 <= r, 1 <= n <= 64
     const int split = blockIdx.y;
@@ -65,6 +67,8 @@ __device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, cons
         src[i] = x + (int64_t)tk * H + p * 8;
         const int32_t pid = pt[(int64_t)a * stride + min(row, r - 1)];   // checked by the grouping kernel
         src[2 + i] = pages + (int64_t)pid * H + p * 8;
+        if constexpr (DBG)
+            if ((lane & 7) == 0) s_pid[row] = pid;
     }
     auto dma = [&](int kt, uint16_t *stg) {
 #pragma unroll
@@ -104,7 +108,16 @@ __device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, cons
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int rr = wm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
-        if (rr < n && j < r) vout[(int64_t)s_perm[rr] * R + j] = acc[e];
+        if (rr < n && j < r) {
+            vout[(int64_t)s_perm[rr] * R + j] = acc[e];
+            if constexpr (DBG) dbg_put(dbg.gather + (int64_t)s_perm[rr] * stride + j, s_pid[j]);
+        }
+    }
+    if constexpr (DBG) {   // the item's sorted rows: token and adapter
+        if (tid < n) {
+            dbg_put(dbg.order + 2 * (row0 + tid), s_perm[tid]);
+            dbg_put(dbg.order + 2 * (row0 + tid) + 1, a);
+        }
     }
 }
 
@@ -115,7 +128,17 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict_
                                                      const int32_t *__restrict__ pt, int32_t stride,
                                                      const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
                                                      float *__restrict__ vpart, int32_t T, int32_t R) {
-    shrink_body<SNS>(x, pages, H, pt, stride, perm, item_rec, vpart, T, R);
+    shrink_body<SNS, false>(x, pages, H, pt, stride, perm, item_rec, vpart, T, R);
+}
+
+template <int SNS>
+__global__ __launch_bounds__(256) void k_shrink_mfma_dbg(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ pages, int32_t H,
+                                                         const int32_t *__restrict__ pt, int32_t stride,
+                                                         const int32_t *__restrict__ perm,
+                                                         const int4 *__restrict__ item_rec, float *__restrict__ vpart,
+                                                         int32_t T, int32_t R, const DebugOut dbg) {
+    shrink_body<SNS, true>(x, pages, H, pt, stride, perm, item_rec, vpart, T, R, dbg);
 }
 
 template <int SNS>
@@ -124,7 +147,7 @@ __global__ __launch_bounds__(256) void k_shrink_mfma_slots(const uint16_t *__res
                                                            const SlotPtrs sp, int32_t stride,
                                                            const int32_t *__restrict__ perm,
                                                            const int4 *__restrict__ item_rec, int32_t T, int32_t R) {
-    shrink_body<SNS>(x, pages, H, sp.pt[blockIdx.z], stride, perm, item_rec, sp.v[blockIdx.z], T, R);
+    shrink_body<SNS, false>(x, pages, H, sp.pt[blockIdx.z], stride, perm, item_rec, sp.v[blockIdx.z], T, R);
 }
 
 // v16[t][j] = bf16(s_a * sum_split vpart[split][t][j]) for tokens with an adapter; zero for
@@ -187,13 +210,15 @@ constexpr int DPW = (BM * BK * 2 / 1024) / PF_WAVES;   // 1 KiB tile chunks per 
 constexpr int LR_K = 64 * (BN / 8) / PF_THREADS;         // B-row pieces per thread of the low-rank term
 constexpr int LR_V = BM * (64 / 8) / PF_THREADS;         // v-row pieces per thread of the low-rank term
 
+template <bool DBG>
 __device__ __forceinline__ void prefill_main_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
-    int32_t n_tiles_n, uint16_t *__restrict__ y) {
+    int32_t n_tiles_n, uint16_t *__restrict__ y, const DebugOut dbg = DebugOut{}) {
     extern __shared__ __align__(16) uint16_t sm[];
     __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
+    __shared__ int32_t s_bpg[DBG ? 64 : 1];   // debug: the B pages of the adapter being added
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
     // Tile order.  The first P0 = roundup(n_tiles_n, 8) workgroups take the last row of tiles, one
@@ -416,6 +441,26 @@ __device__ __forceinline__ void prefill_main_body(
                                                                           acc[mi][ni], 0, 0, 0);
         }
     };
+    // debug: the B pages the K-extension of adapter li used (its thread-held page ids), recorded for
+    // every row of the tile that belongs to the adapter
+    auto dbg_b = [&](int li, const int32_t *pg) {
+        if constexpr (DBG) {
+            const int32_t a = s_list[li], r = s_lr[li];
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < LR_K; ++k) {
+                const int idx = tid + PF_THREADS * k, j = idx >> 5;
+                if ((idx & 31) == 0 && j < r) s_bpg[j] = pg[k];
+            }
+            __syncthreads();
+            for (int e = tid; e < BM * 64; e += PF_THREADS) {
+                const int row = e >> 6, j = e & 63;
+                if (j < r && m0 + row < T && s_key[row] == a)
+                    dbg_put(dbg.gather + (int64_t)(m0 + row) * stride + r + j, s_bpg[j]);
+            }
+            __syncthreads();
+        }
+    };
     // the same operands through registers (the caller has made the stage free with a barrier)
     auto lr_regs = [&](uint16_t *stg, int li, const int32_t *pg) {
         u32x4_t bv[LR_K], vv[LR_V];
@@ -488,12 +533,14 @@ __device__ __forceinline__ void prefill_main_body(
         lr_mask(stg, 0);
         __syncthreads();
         lr_mfma(stg, 0);
+        dbg_b(0, pg0);
     }
     __syncthreads();
     for (int li = 1; li < nlist; ++li) {
         int32_t pg[LR_K];
         lr_pages(li, pg);
         lr_regs(sm, li, pg);
+        dbg_b(li, pg);
     }
 
     // ---- one rounding, and each lane stores its own elements with 2-byte streaming stores (the 32
@@ -522,7 +569,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
     int32_t n_tiles_n, uint16_t *__restrict__ y) {
-    prefill_main_body(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y);
+    prefill_main_body<false>(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y);
+}
+
+__global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_dbg(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
+    const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
+    const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
+    int32_t n_tiles_n, uint16_t *__restrict__ y, const DebugOut dbg) {
+    prefill_main_body<true>(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y, dbg);
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_slots(
@@ -530,17 +585,20 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_slots(
     const int32_t *__restrict__ tok_a, const int32_t *__restrict__ tok_r, int32_t R, int32_t T, int32_t H,
     int32_t n_tiles_n) {
     const int z = blockIdx.z;
-    prefill_main_body(x, (const uint16_t *)sp.W[z], pages, sp.pt[z], stride, tok_a, tok_r,
-                      (const uint16_t *)sp.v16[z], R, T, H, n_tiles_n, (uint16_t *)sp.y[z]);
+    prefill_main_body<false>(x, (const uint16_t *)sp.W[z], pages, sp.pt[z], stride, tok_a, tok_r,
+                             (const uint16_t *)sp.v16[z], R, T, H, n_tiles_n, (uint16_t *)sp.y[z]);
 }
 
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const float *scale,
-                          const SlotPtrs &sp, int n, hipStream_t s, hipEvent_t mid) {
+                          const SlotPtrs &sp, int n, hipStream_t s, hipEvent_t mid, const DebugOut *dbg) {
     static bool attr_set = false;
     if (!attr_set) {
         const struct { const void *f; int lds; } attrs[] = {
             {(const void *)k_prefill_main, (int)MAIN_LDS},
             {(const void *)k_prefill_main_slots, (int)MAIN_LDS},
+            {(const void *)k_prefill_main_dbg, (int)MAIN_LDS},
+            {(const void *)k_shrink_mfma_dbg<6>, (int)(6 * SH_STAGE * 2)},
+            {(const void *)k_shrink_mfma_dbg<4>, (int)(4 * SH_STAGE * 2)},
             {(const void *)k_shrink_mfma<6>, (int)(6 * SH_STAGE * 2)},
             {(const void *)k_shrink_mfma_slots<6>, (int)(6 * SH_STAGE * 2)},
             {(const void *)k_shrink_mfma<4>, (int)(4 * SH_STAGE * 2)},
@@ -558,7 +616,14 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
     dim3 g1(plan.n_items_max, VSPLIT, n);
     const int sns = plan.T <= 4096 ? 6 : 4;
     const size_t sh_lds = (size_t)sns * SH_STAGE * 2;
-    if (n == 1) {
+    if (dbg) {
+        if (sns == 6)
+            hipLaunchKernelGGL(k_shrink_mfma_dbg<6>, dim3(g1.x, g1.y), dim3(256), sh_lds, s, xh, pages, p->hidden,
+                               sp.pt[0], stride, ws.perm, ws.item_rec, sp.v[0], T, plan.rp, *dbg);
+        else
+            hipLaunchKernelGGL(k_shrink_mfma_dbg<4>, dim3(g1.x, g1.y), dim3(256), sh_lds, s, xh, pages, p->hidden,
+                               sp.pt[0], stride, ws.perm, ws.item_rec, sp.v[0], T, plan.rp, *dbg);
+    } else if (n == 1) {
         if (sns == 6)
             hipLaunchKernelGGL(k_shrink_mfma<6>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
                                ws.perm, ws.item_rec, sp.v[0], T, plan.rp);
@@ -586,7 +651,11 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
     if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
     const int tn = (p->hidden + BN - 1) / BN, tm = (int)((plan.T + BM - 1) / BM);
     const int grid = (tn + 7) / 8 * 8 + ((tm - 1) * tn + 7) / 8 * 8;   // the last row of tiles, then the rest
-    if (n == 1)
+    if (dbg)
+        hipLaunchKernelGGL(k_prefill_main_dbg, dim3(grid), dim3(PF_THREADS), MAIN_LDS, s, xh, (const uint16_t *)sp.W[0],
+                           pages, sp.pt[0], stride, ws.tok_a, ws.tok_r, (const uint16_t *)sp.v16[0], plan.rp, T,
+                           p->hidden, tn, (uint16_t *)sp.y[0], *dbg);
+    else if (n == 1)
         hipLaunchKernelGGL(k_prefill_main, dim3(grid), dim3(PF_THREADS), MAIN_LDS, s, xh, (const uint16_t *)sp.W[0],
                            pages, sp.pt[0], stride, ws.tok_a, ws.tok_r, (const uint16_t *)sp.v16[0], plan.rp, T,
                            p->hidden, tn, (uint16_t *)sp.y[0]);

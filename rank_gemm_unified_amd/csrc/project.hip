@@ -124,7 +124,7 @@ namespace {
 // serves every slot.  Every argument is checked before any device work.
 int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void *const *W,
                  const int32_t *const *pt, const int32_t *ids, const int32_t *ranks, const float *scale, int64_t T,
-                 void *const *y, void *ws, size_t ws_bytes, void *stream) {
+                 void *const *y, void *ws, size_t ws_bytes, void *stream, const DebugOut *dbg = nullptr) {
     if (!p) return set_error(LORA_EINVAL, "%s: pool is NULL", fn);
     if (p->bookkeeping_only) return set_error(LORA_EINVAL, "%s: bookkeeping-only pool", fn);
     if (T < 0 || T > MAX_TOKENS)
@@ -169,6 +169,11 @@ int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void 
         sp.spages[z] = wz.spages;
     }
     const Ws w0 = carve(ws, pl);
+    if (dbg) {   // the debug outputs start at -1: kernels record only what they use
+        hipError_t e = launch_fill_i32(dbg->gather, T * 2 * p->max_rank, -1, s);
+        if (e == hipSuccess) e = launch_fill_i32(dbg->order, 2 * T, -1, s);
+        if (e != hipSuccess) return hip_error(e, "debug output fill");
+    }
     hipEvent_t *ev = nullptr;
     if (p->prof_max > 0) {
         const int32_t slot = p->prof_next.fetch_add(1);
@@ -182,9 +187,9 @@ int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void 
     }
     if (ev) LP_HIP(hipEventRecord(ev[1], s));
     switch (pl.path) {
-        case PATH_DECODE: e = launch_decode(p, pl, x, ids, ranks, scale, sp, n, s, ev ? ev[2] : nullptr); break;
-        case PATH_PREFILL: e = launch_prefill(p, pl, w0, x, scale, sp, n, s, ev ? ev[2] : nullptr); break;
-        case PATH_F32: e = launch_f32(p, pl, w0, x, W[0], pt[0], scale, y[0], s, ev ? ev[2] : nullptr); break;
+        case PATH_DECODE: e = launch_decode(p, pl, x, ids, ranks, scale, sp, n, s, ev ? ev[2] : nullptr, dbg); break;
+        case PATH_PREFILL: e = launch_prefill(p, pl, w0, x, scale, sp, n, s, ev ? ev[2] : nullptr, dbg); break;
+        case PATH_F32: e = launch_f32(p, pl, w0, x, W[0], pt[0], scale, y[0], s, ev ? ev[2] : nullptr, dbg); break;
     }
     if (e != hipSuccess) return hip_error(e, "projection kernel launch");
     if (ev) LP_HIP(hipEventRecord(ev[3], s));
@@ -277,6 +282,17 @@ extern "C" int lora_profile_stop(lora_pool *p, lora_profile_t *out) {
     for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
     p->prof_events.clear();
     return LORA_OK;
+}
+
+extern "C" int lora_debug_project(lora_pool *p, const void *x, const void *W, const int32_t *pt, const int32_t *ids,
+                                  const int32_t *ranks, const float *scale, int64_t T, void *y, void *ws,
+                                  size_t ws_bytes, int32_t *gather_out, int32_t *order_out, void *stream) {
+    if (T > 0 && (!gather_out || !order_out))
+        return set_error(LORA_EINVAL, "lora_debug_project: NULL pointer argument");
+    if (!aligned(gather_out, 4) || !aligned(order_out, 4))
+        return set_error(LORA_EINVAL, "lora_debug_project: misaligned debug output");
+    const DebugOut dbg{gather_out, order_out};
+    return project_impl(p, "lora_debug_project", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream, &dbg);
 }
 
 extern "C" int lora_debug_gather(lora_pool *p, const int32_t *pt, const int32_t *ids, const int32_t *ranks,

@@ -72,3 +72,59 @@ def errors(y_gpu: torch.Tensor, y_ref: np.ndarray):
 def bf16_round_f64(y: np.ndarray) -> torch.Tensor:
     """Round exactly-representable-in-f32 values to bfloat16 (single rounding)."""
     return torch.as_tensor(y.astype(np.float32)).to(torch.bfloat16)
+
+
+def check_grouping(order: np.ndarray, ids: np.ndarray, ranks: np.ndarray, decode: bool) -> None:
+    """The token grouping the kernels consumed (lora_debug_project's order_out) is valid: its first n
+    positions hold exactly the n tokens with a low-rank term, each once and with its own adapter, and
+    each adapter's tokens form one contiguous run.  Decode path: runs in order of first token, then
+    every other token with adapter -1.  Prefill path: runs in adapter order, the rest untouched (-1)."""
+    ids = np.asarray(ids)
+    live = np.array([a >= 0 and int(ranks[a]) > 0 for a in ids], bool)
+    n = int(live.sum())
+    toks, ads = order[:, 0], order[:, 1]
+    assert np.array_equal(np.sort(toks[:n]), np.nonzero(live)[0]), "grouped tokens are not the adapter tokens"
+    assert np.array_equal(ads[:n], ids[toks[:n]]), "a token sits in another adapter's segment"
+    runs = [int(a) for i, a in enumerate(ads[:n]) if i == 0 or a != ads[i - 1]]
+    assert len(runs) == len(set(runs)), "an adapter's tokens are split over several runs"
+    if decode:
+        first = {}
+        for t, a in enumerate(ids):
+            if live[t]:
+                first.setdefault(int(a), t)
+        assert runs == sorted(first, key=first.get), "segments not in order of first token"
+        assert np.array_equal(np.sort(toks[n:]), np.nonzero(~live)[0]) and (ads[n:] == -1).all()
+    else:
+        assert runs == sorted(runs), "segments not in adapter order"
+        assert (order[n:] == -1).all()
+
+
+def check_indices(pool: rg.Pool, w: Workload, slot: int, ids=None, x=None) -> dict:
+    """Bit-exact check of the projection's own indices: lora_debug_project runs the production kernels
+    (their debug instantiations) and reports, per token, the pages they multiplied in and the grouping
+    they consumed.  Checks: y equals lora_project's bit for bit; the pages equal the oracle's table
+    lookup (oracle.gather_page_ids) bit for bit; the grouping is valid (check_grouping)."""
+    ids = np.asarray(w.ids if ids is None else ids, np.int32)
+    x = w.x_for_slot(slot) if x is None else x
+    T = int(ids.size)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w, ids)
+    y_ref = torch.empty_like(x)
+    pool.project(slot, x, w.W(slot), d_ids, d_ranks, d_scale, y=y_ref)
+    y = torch.empty_like(x)
+    R2 = 2 * w.max_rank
+    g = torch.empty((T, R2), dtype=torch.int32, device=x.device)
+    o = torch.empty((T, 2), dtype=torch.int32, device=x.device)
+    rg.lora_debug_project(pool.handle, x, w.W(slot), pool.table[slot], d_ids, d_ranks, d_scale, T, y,
+                          pool.workspace(T), g, o)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    bits = (lambda t: t.view(torch.int16)) if y.dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    assert torch.equal(bits(y), bits(y_ref)), "debug instantiation changed y"
+    want = oracle.gather_page_ids(pool.table[slot].cpu().numpy(), ids, w.ranks, w.max_rank)
+    got = g.cpu().numpy()
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, {"tokens": bad[:8].tolist(), "ids": ids[bad[:8]].tolist(),
+                           "got": got[bad[0]].tolist(), "want": want[bad[0]].tolist()}
+    check_grouping(o.cpu().numpy(), ids, w.ranks, decode=(w.dtype == "bf16" and T <= 256))
+    live = sum(1 for a in ids if a >= 0 and int(w.ranks[a]) > 0)
+    return {"tokens": T, "with_adapter": live, "pages_checked": int((want >= 0).sum())}

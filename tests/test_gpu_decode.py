@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import rank_gemm_unified_amd as rg
-from gpu_helpers import bf16_round_f64, device_pool, errors, ids_ranks_scale, oracle_y, run, say
+from gpu_helpers import bf16_round_f64, check_indices, device_pool, errors, ids_ranks_scale, oracle_y, run, say
 from workloads import build, custom, storage_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -62,9 +62,10 @@ def test_decode_parity_and_gather():
     _pool_contents_exact(pool, w)
     ids, ranks, _ = ids_ranks_scale(w)
     out = torch.empty((w.T, 2 * w.max_rank), dtype=torch.int32, device="cuda")
-    rg.lora_debug_gather(pool.handle, pool.table[0], ids, ranks, w.T, out)
+    rg.lora_debug_gather(pool.handle, pool.table[0], ids, ranks, w.T, out)   # the table view
     want = oracle.gather_page_ids(pool.table[0].cpu().numpy(), w.ids, w.ranks, w.max_rank)
     assert np.array_equal(out.cpu().numpy(), want)
+    check_indices(pool, w, 0)                                                  # the kernels' own indices
     y = run(pool, w, 0)
     torch.cuda.synchronize()
     assert rg.lora_check_device_errors(pool.handle, check=False) == 0
