@@ -310,6 +310,22 @@ int lora_debug_project(lora_pool *pool, const void *x, const void *W, const int3
 int lora_debug_gather(lora_pool *pool, const int32_t *page_table, const int32_t *adapter_ids,
                       const int32_t *ranks, int64_t T, int32_t *page_ids_out, void *stream);
 
+/*
+ * lora_project for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  No workspace argument: the call uses a scratch
+ * array of LORA_NOALLOC_SCRATCH_MB MiB that the library holds on each GPU it runs on until the
+ * process ends (its address is taken at pool creation).  It allocates nothing and writes y exactly as
+ * lora_project does.  Calls that need more scratch than that (lora_project_workspace_size) are refused
+ * with LORA_EINVAL before any device work: at H = 4096 every decode batch (T <= 256) and prefill
+ * batches up to about 25k tokens fit.  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (several streams or threads without ordering between them) race and may produce wrong
+ * results; order them.  Other arguments, checks and errors as lora_project.
+ */
+#define LORA_NOALLOC_SCRATCH_MB 32
+int lora_project_noalloc(lora_pool *pool, const void *x, const void *W, const int32_t *page_table,
+                         const int32_t *adapter_ids, const int32_t *ranks, const float *scale, int64_t T,
+                         void *y, void *stream);
+
 /* Wait for all device work, then report and clear the pool's device error word:
  * LORA_OK, or LORA_EDEVICE with a message naming the kinds of fault seen. */
 int lora_check_device_errors(lora_pool *pool);

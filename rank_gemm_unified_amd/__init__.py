@@ -23,6 +23,7 @@ LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_RANK, LORA_MAX_ADAPTERS = 64, 8192
 LORA_VICTIM_LOAD_ORDER, LORA_VICTIM_LRU, LORA_VICTIM_FARTHEST = 0, 1, 2
 LORA_MAX_CALL_SLOTS = 4
+LORA_NOALLOC_SCRATCH_MB = 32
 STATUS_NAMES = {0: "ok", -1: "einval", -2: "enomem", -3: "enoent", -4: "erank", -5: "ebusy",
                 -6: "eexist", -7: "ehip", -8: "edevice"}
 
@@ -76,6 +77,7 @@ _SIGS = {
     "lora_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_debug_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp]),
     "lora_debug_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "lora_project_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
     "lora_check_device_errors": (ctypes.c_int, [_vp]),
     "lora_profile_start": (ctypes.c_int, [_vp, _i32]),
     "lora_profile_stop": (ctypes.c_int, [_vp, ctypes.POINTER(lora_profile_t)]),
@@ -299,6 +301,12 @@ def lora_debug_project(pool, x, W, page_table, adapter_ids, ranks, scale, T, y, 
                                  _ptr(scale), T, _ptr(y), _ptr(workspace), workspace_bytes, _ptr(gather_out),
                                  _ptr(order_out), _stream(stream))
     return _check(rc, "lora_debug_project") if check else rc
+
+
+def lora_project_noalloc(pool, x, W, page_table, adapter_ids, ranks, scale, T, y, stream=None, check=True):
+    rc = _lib.lora_project_noalloc(pool, _ptr(x), _ptr(W), _ptr(page_table), _ptr(adapter_ids), _ptr(ranks),
+                                   _ptr(scale), T, _ptr(y), _stream(stream))
+    return _check(rc, "lora_project_noalloc") if check else rc
 
 
 def lora_check_device_errors(pool, check=True):

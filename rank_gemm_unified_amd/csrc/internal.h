@@ -180,6 +180,10 @@ hipError_t launch_f32(const lora_pool *p, const Plan &plan, const Ws &ws, const 
                       hipStream_t s, hipEvent_t mid, const DebugOut *dbg = nullptr);
 hipError_t launch_fill_i32(int32_t *dst, int64_t n, int32_t value, hipStream_t s);
 
+// Address of the allocation-free entry point's scratch array on device `dev`, taken once per device
+// (at pool creation).  Returns a lora_status.
+int scratch_setup(int dev);
+
 struct DeviceGuard {
     int prev = -1;
     bool ok = true;

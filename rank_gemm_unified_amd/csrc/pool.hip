@@ -129,6 +129,9 @@ extern "C" int lora_pool_create(void *pages, int64_t num_pages, int32_t hidden, 
     if (!bk) {
         hipError_t e = hipGetDevice(&p->device);
         if (e != hipSuccess) { destroy(p); return hip_error(e, "hipGetDevice"); }
+        // lora_project_noalloc's scratch address on this device; a failure here only disables that
+        // entry point (it retries and reports the error), so it does not fail the pool
+        if (scratch_setup(p->device) != LORA_OK) clear_error();
         const size_t slot_bytes = 2ull * max_rank * hidden * p->elem;          // A and B of one slot
         const size_t want = slot_bytes * (size_t)n_slots;
         p->staging_bytes = std::max(slot_bytes, std::min(want, (size_t)64 << 20));

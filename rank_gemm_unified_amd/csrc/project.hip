@@ -7,6 +7,7 @@
 // use the tiled MFMA GEMM.  The choice depends only on T and the dtype, both known on the host.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -293,6 +294,58 @@ extern "C" int lora_debug_project(lora_pool *p, const void *x, const void *W, co
         return set_error(LORA_EINVAL, "lora_debug_project: misaligned debug output");
     const DebugOut dbg{gather_out, order_out};
     return project_impl(p, "lora_debug_project", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream, &dbg);
+}
+
+// ---- the projection for callers that cannot allocate -------------------------------------------
+// The workspace of lora_project_noalloc is this file-scope device array, one copy per GPU, held until
+// the process ends.  Host code never passes its name to a kernel (on the host it is a stand-in, not a
+// device address): its address on each device comes from hipGetSymbolAddress, taken once per device
+// at pool creation with that device current.
+namespace {
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(LORA_NOALLOC_SCRATCH_MB) << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+namespace lorapool {
+int scratch_setup(int dev) {
+    if (dev < 0 || dev >= MAX_DEVICES) return set_error(LORA_EINVAL, "device %d beyond %d", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return LORA_OK;
+    DeviceGuard g(dev);
+    if (!g.ok) return set_error(LORA_EHIP, "cannot select device %d", dev);
+    void *ptr = nullptr;
+    LP_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[dev] = ptr;
+    return LORA_OK;
+}
+}  // namespace lorapool
+
+extern "C" int lora_project_noalloc(lora_pool *p, const void *x, const void *W, const int32_t *pt, const int32_t *ids,
+                                    const int32_t *ranks, const float *scale, int64_t T, void *y, void *stream) {
+    if (!p) return set_error(LORA_EINVAL, "lora_project_noalloc: pool is NULL");
+    if (p->bookkeeping_only) return set_error(LORA_EINVAL, "lora_project_noalloc: bookkeeping-only pool");
+    Plan pl;
+    if (!make_plan(p, T, &pl)) return set_error(LORA_EINVAL, "lora_project_noalloc: T = %lld out of range", (long long)T);
+    if (pl.total > NOALLOC_SCRATCH_BYTES)
+        return set_error(LORA_EINVAL, "lora_project_noalloc: %lld tokens at H = %d need %zu bytes of scratch, beyond the "
+                                      "%d MiB this entry point has; use lora_project with a workspace",
+                         (long long)T, p->hidden, pl.total, LORA_NOALLOC_SCRATCH_MB);
+    void *ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        if (p->device >= 0 && p->device < MAX_DEVICES) ws = g_scratch_ptr[p->device];
+    }
+    if (!ws) {   // pool creation could not take the address: try once more, and report why not
+        const int rc = scratch_setup(p->device);
+        if (rc != LORA_OK) return rc;
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        ws = g_scratch_ptr[p->device];
+    }
+    return project_impl(p, "lora_project_noalloc", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, NOALLOC_SCRATCH_BYTES,
+                        stream);
 }
 
 extern "C" int lora_debug_gather(lora_pool *p, const int32_t *pt, const int32_t *ids, const int32_t *ranks,
