@@ -14,10 +14,13 @@ timed loop rotates through enough independent replicas (pool, page table, W, x, 
 >= 1 GiB between reuses.
 
 Prints one JSON line: the throughput, the dominant kernel's roofline fraction (its algorithmic
-bytes or flops over its average device time, from HIP events recorded on its launch stream), and
-the fp64 CPU oracle timed on this host as a baseline.  With --fuse-slots the slots that read the
-same x (a layer's q, k and v) are projected by one lora_project_slots call; the per-launch figures
-then cover every slot of the launch.
+bytes or flops over its average device time, from HIP events recorded on its launch stream) with
+the whole call's fraction beside it (roofline.call), and the fp64 CPU oracle timed on this host as a
+baseline.  The default run also times the prefill batch (MFMA-bound) and the 2000-adapter batch
+(HBM-bound) and adds their lines' figures under "more_workloads".  With --fuse-slots the slots that
+read the same x (a layer's q, k and v) are projected by one lora_project_slots call; the per-launch
+figures then cover every slot of the launch.  --workload stack13b runs the whole 40-layer stack
+(160 slots, a 115 GiB pool, one replica: a step moves 42 GiB, far beyond the Infinity Cache).
 """
 from __future__ import annotations
 
@@ -297,89 +300,61 @@ def adapter_sweep_bench(args, rg, torch):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny", "stack13b", "prefetch", "adapters"],
-                    help="stack13b runs one layer (its q/k/v/o slots) of the 40-layer stack; prefetch measures "
-                         "adapter loads from pinned host memory beside the decode projection; adapters runs the "
-                         "1/10/100/1000-adapter load test")
-    ap.add_argument("--fuse-slots", action="store_true",
-                    help="project the slots that read the same x (a layer's q, k, v) in one lora_project_slots "
-                         "call (up to 4 slots per call) instead of one lora_project call per slot")
-    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
-    ap.add_argument("--profile-calls", type=int, default=400)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB 20 times (HBM counter calibration) and exit")
-    args = ap.parse_args()
+DESCRIPTIONS = {
+    "decode": "Llama-7B-shaped q_proj decode: H=4096 bf16, 32 adapters ranks U{8,16,32,64}, 64 tokens "
+              "(1 per request), pool 60% KV pages",
+    "prefill": "prefill grouped GEMM: H=4096 bf16, 8 requests x 512 tokens, ranks {8,8,16,16,32,32,64,64}",
+    "many": "2000 adapters, q/k/v/o of one layer, H=4096 bf16, 256 decode tokens Zipf(1.0), 10% identity",
+    "tiny": "tiny: H=256 fp32, 4 adapters, 16 tokens",
+    "stack13b": "Llama-13B-shaped stack: H=5120 bf16, 40 layers x q/k/v/o (160 slots), 1000 adapters, "
+                "4x2048 prefill + 256 decode rows Zipf(1.2), churned pool of 115 GiB",
+}
 
-    rank = int(os.environ.get("RANK", "0"))
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        if rank == 0:
-            print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the projection is "
-                  "data-parallel over tokens and its multi-GPU sharding is a design note, not a run", flush=True)
-        sys.exit(2)
 
-    import numpy as np
-    import torch
-    import rank_gemm_unified_amd as rg
-    from workloads import build
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.calibrate_copy:
-        n = args.calibrate_copy * 2**20
-        src_t = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst_t = torch.empty_like(src_t)
-        for _ in range(20):
-            dst_t.copy_(src_t)
+def load_pool(rg, torch, w):
+    """A device pool holding the workload's adapters and KV pages (ops run in chunks; adapters drawn
+    without keeping them, so the largest pool does not hold its weights twice)."""
+    pool = rg.Pool(w.num_pages, w.hidden, rg.LORA_F32 if w.dtype == "f32" else rg.LORA_BF16, n_slots=w.n_slots,
+                   max_adapters=w.max_adapters, free_order=w.free_order)
+    for i in range(0, len(w.ops), 20000):
+        st = pool.run_ops(w.ops[i:i + 20000], w.ranks, w.adapter_uncached)
+        assert all(s == 0 for s in st), rg.lora_last_error()
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 20}), flush=True)
-        return
-    if args.workload == "prefetch":
-        prefetch_bench(args, rg, torch)
-        return
-    if args.workload == "adapters":
-        adapter_sweep_bench(args, rg, torch)
-        return
-    w = build(args.workload, device="cuda", layers=1 if args.workload == "stack13b" else None)
+        if len(w.ops) > 20000:
+            log(f"  pool ops {min(i + 20000, len(w.ops))}/{len(w.ops)}")
+    return pool
+
+
+def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=0):
+    """Time `steps` steps of one workload (after `warmup`), then the per-kernel device times from HIP
+    events on the launch stream.  Returns the JSON fields of the workload's line."""
+    from workloads import build
+    dev = torch.device("cuda:0")
+    w = build(name, device="cuda")
     slots = list(range(w.n_slots))
     info = algorithmic(w, w.ids, len(slots))
     log(f"workload {w.name}: H={w.hidden} T={w.T} slots={len(slots)} adapters={w.max_adapters} "
         f"distinct={info['distinct_adapters']} step bytes={info['bytes'] / 2**20:.1f} MiB "
         f"flops={info['flops'] / 1e9:.2f} G")
-
-    if args.replicas:
-        R = args.replicas
-    else:
-        R = max(2, math.ceil(2 ** 30 / max(info["bytes"], 1)))
-    R = min(R, 64)
-    dcode = rg.LORA_F32 if w.dtype == "f32" else rg.LORA_BF16
+    # cold HBM: rotate replicas so that >= 1 GiB is touched between reuses (one replica when a step
+    # alone moves more than that)
+    R = replicas or max(1, math.ceil(2 ** 30 / max(info["bytes"], 1)))
+    R = 1 if info["bytes"] >= 2 ** 30 else max(2, min(R, 64))
     d_ids = torch.as_tensor(w.ids, device=dev)
     d_ranks = torch.as_tensor(w.ranks, device=dev)
     d_scale = torch.as_tensor(w.scales, device=dev)
     reps = []
     for i in range(R):
-        pool = rg.Pool(w.num_pages, w.hidden, dcode, n_slots=w.n_slots, max_adapters=w.max_adapters,
-                       free_order=w.free_order)
-        st = pool.run_ops(w.ops, w.ranks, w.adapter)
-        assert all(s == 0 for s in st), rg.lora_last_error()
-        Ws = [w.W(s).clone() for s in slots]
-        xs = [w.x(i2).clone() for i2 in range(w.n_x)]
+        pool = load_pool(rg, torch, w)
+        Ws = [w.W(s) if R == 1 else w.W(s).clone() for s in slots]
+        xs = [w.x(i2) if R == 1 else w.x(i2).clone() for i2 in range(w.n_x)]
         ys = [torch.empty_like(xs[0]) for _ in slots]
         reps.append((pool, Ws, xs, ys))
-        if w.name in ("many", "stack13b"):
-            w.drop_cache("AB")
-    # the calls of one step: one per slot, or (--fuse-slots) one per run of up to LORA_MAX_CALL_SLOTS
+    # the calls of one step: one per slot, or (fuse_slots) one per run of up to LORA_MAX_CALL_SLOTS
     # slots that read the same x
     groups = []
     for s in slots:
-        if (args.fuse_slots and groups and w.slot_x[groups[-1][0]] == w.slot_x[s]
+        if (fuse_slots and groups and w.slot_x[groups[-1][0]] == w.slot_x[s]
                 and len(groups[-1]) < rg.LORA_MAX_CALL_SLOTS):
             groups[-1].append(s)
         else:
@@ -388,11 +363,11 @@ def main():
     ws = torch.empty(max(rg.lora_project_slots_workspace_size(p.handle, len(g), w.T) for p, *_ in reps
                          for g in groups), dtype=torch.uint8, device=dev)
     wsb = ws.numel()
-    log(f"replicas: {R}; calls per step: {[list(g) for g in groups]}")
+    log(f"replicas: {R}; calls per step: {len(groups)}")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    if args.fuse_slots:   # argument arrays built once per replica, outside the timed loop
-        fused = []
+    fused = []
+    if fuse_slots:   # argument arrays built once per replica, outside the timed loop
         for pool, Ws, xs, ys in reps:
             calls = []
             for g in groups:
@@ -404,7 +379,7 @@ def main():
 
     def step(i):
         pool, Ws, xs, ys = reps[i % R]
-        if args.fuse_slots:
+        if fuse_slots:
             for n, sl, xp, wp, yp in fused[i % R]:
                 rg._lib.lora_project_slots(pool.handle, n, sl, xp, wp, d_ids.data_ptr(), d_ranks.data_ptr(),
                                            d_scale.data_ptr(), w.T, yp, ws.data_ptr(), wsb, sh)
@@ -414,24 +389,25 @@ def main():
                                  d_ids.data_ptr(), d_ranks.data_ptr(), d_scale.data_ptr(), w.T, ys[s].data_ptr(),
                                  ws.data_ptr(), wsb, sh)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     assert rg.lora_check_device_errors(reps[0][0].handle, check=False) == 0, rg.lora_last_error()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / steps
     tokens_per_s = w.T / (ms_per_step / 1e3)
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
-        f"step algorithmic {info['bytes'] / (ms_per_step / 1e3) / 1e9:.0f} GB/s")
+    log(f"timed {steps} steps: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
+        f"step algorithmic {info['bytes'] / (ms_per_step / 1e3) / 1e9:.0f} GB/s, "
+        f"{info['flops'] / (ms_per_step / 1e3) / 1e12:.0f} TFLOP/s")
 
     # per-kernel device time from HIP events on the launch stream (separate loop: events add gaps)
-    calls_per_rep = max(1, args.profile_calls // R)
+    calls_per_rep = max(1, profile_calls // (R * len(groups)))
     for pool, *_ in reps:
         rg.lora_profile_start(pool.handle, calls_per_rep * len(groups))
     for i in range(calls_per_rep * R):
@@ -457,9 +433,12 @@ def main():
     src = os.path.join(ROOT, "rank_gemm_unified_amd", "csrc")
     first_us = avg["first_us"] - event_gap_us
     second_us = avg["second_us"] - event_gap_us
+    timing = ("HIP events around each launch on its stream, minus the per-interval event cost "
+              f"({event_gap_us:.2f} us, from the event-free timed loop)")
     if decode_like:
         stream_kernel = w.T <= 64 and w.hidden <= 8192
         achieved = info["decode_first_bytes"] * per_call / (first_us / 1e6) / 1e9
+        call_gbs = info["bytes"] / (ms_per_step / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "kernel": ("k_decode_stream (W stream + MFMA partials, gathered-A shrink)" if stream_kernel else
@@ -467,54 +446,123 @@ def main():
                 "algorithmic_bytes_per_launch": info["decode_first_bytes"] * per_call, "avg_launch_us": first_us,
                 "traffic": (traffic_from_profiles("decode_stream", os.path.join(src, "k_decode.hip")) if stream_kernel
                             else traffic_from_profiles("decode_wide", os.path.join(src, "k_decode_wide.hip"))),
-                "timing": "HIP events around each launch on its stream, minus the per-interval event cost "
-                          f"({event_gap_us:.2f} us, from the event-free timed loop)",
+                "timing": timing,
                 "second_kernel": {"kernel": "k_decode_finish (partials + gathered-B expand + rounding)",
                                   "avg_launch_us": second_us,
-                                  "achieved_GBps": info["decode_second_bytes"] * per_call / (second_us / 1e6) / 1e9}}
+                                  "achieved_GBps": info["decode_second_bytes"] * per_call / (second_us / 1e6) / 1e9},
+                "call": {"what": "the whole step (every launch of every call), event-free loop",
+                         "algorithmic_bytes": info["bytes"], "us": ms_per_step * 1e3, "achieved": call_gbs,
+                         "frac": call_gbs / HBM_PEAK_GBS}}
     else:
         achieved = info["prefill_second_flops"] * per_call / (second_us / 1e6) / 1e12
+        call_tf = info["flops"] / (ms_per_step / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)",
+                "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)" + (" (q/k/v in one launch)" if fuse_slots else ""),
                 "algorithmic_flops_per_launch": info["prefill_second_flops"] * per_call, "avg_launch_us": second_us,
                 "traffic": traffic_from_profiles("prefill_main", os.path.join(src, "k_prefill.hip")),
-                "timing": "HIP events around each launch on its stream, minus the per-interval event cost "
-                          f"({event_gap_us:.2f} us, from the event-free timed loop)"}
-
-    cpu = None
-    if not args.no_cpu_baseline and rank == 0:
-        log("timing the fp64 oracle on the host ...")
-        cpu = cpu_baseline(w, args.cpu_seconds, len(slots))
-
-    desc = {
-        "decode": "Llama-7B-shaped q_proj decode: H=4096 bf16, 32 adapters ranks U{8,16,32,64}, 64 tokens "
-                  "(1 per request), pool 60% KV pages",
-        "prefill": "prefill grouped GEMM: H=4096 bf16, 8 requests x 512 tokens, ranks {8,8,16,16,32,32,64,64}",
-        "many": "2000 adapters, q/k/v/o of one layer, H=4096 bf16, 256 decode tokens Zipf(1.0), 10% identity",
-        "tiny": "tiny: H=256 fp32, 4 adapters, 16 tokens",
-        "stack13b": "Llama-13B-shaped stack, one layer (q/k/v/o) of 40: H=5120 bf16, 1000 adapters, "
-                    "4x2048 prefill + 256 decode rows Zipf(1.2), churned pool",
-    }[w.name]
+                "timing": timing,
+                "call": {"what": "the whole step (every launch of every call), event-free loop",
+                         "algorithmic_flops": info["flops"], "us": ms_per_step * 1e3, "achieved": call_tf,
+                         "frac": call_tf / MFMA_BF16_PEAK_TFLOPS,
+                         "hbm_GBps": info["bytes"] / (ms_per_step / 1e3) / 1e9}}
     out = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; inputs resident in HBM)",
-        "config": {"workload": desc, "hidden": w.hidden, "tokens": w.T, "projections_per_step": len(slots),
-                   "adapters": w.max_adapters, "distinct_adapters_in_batch": info["distinct_adapters"],
-                   "replicas_rotated": R, "parallelism": "single GPU",
-                   "calls_per_step": [list(g) for g in groups]},
+        "value": tokens_per_s, "unit": "tokens/s", "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step,
+        "dtype": w.dtype,
+        "config": {"workload": DESCRIPTIONS[w.name], "hidden": w.hidden, "tokens": w.T,
+                   "projections_per_step": len(slots), "adapters": w.max_adapters,
+                   "distinct_adapters_in_batch": info["distinct_adapters"], "replicas_rotated": R,
+                   "parallelism": "single GPU", "calls_per_step": len(groups),
+                   "slots_per_call": [len(g) for g in groups][:8]},
         "step_algorithmic_bytes": info["bytes"], "step_algorithmic_flops": info["flops"],
         "step_hbm_GBps": info["bytes"] / (ms_per_step / 1e3) / 1e9,
         "step_hbm_frac": info["bytes"] / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "kernel_event_intervals_us": avg, "event_cost_per_interval_us": event_gap_us,
         "roofline": roof,
-        "cpu_baseline": cpu,
     }
-    if w.name == "stack13b":
-        # the 40 layers are independent copies of this one (same shapes, draws and pool rules), so a
-        # step through the whole stack is 40 of these; labelled as an extrapolation, not measured
-        out["extrapolated_stack_step_ms"] = 40 * ms_per_step
+    for pool, *_ in reps:
+        pool.close()
+    return w, out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 20 for stack13b)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 200; 3 for stack13b)")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "tiny", "stack13b", "prefetch", "adapters"],
+                    help="stack13b runs the whole 40-layer stack (160 slots); prefetch measures adapter loads from "
+                         "pinned host memory beside the decode projection; adapters runs the 1/10/100/1000-adapter "
+                         "load test")
+    ap.add_argument("--fuse-slots", action="store_true",
+                    help="project the slots that read the same x (a layer's q, k, v) in one lora_project_slots "
+                         "call (up to 4 slots per call) instead of one lora_project call per slot")
+    ap.add_argument("--no-more", action="store_true",
+                    help="default workload only: skip the extra prefill and many-adapter blocks")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
+    ap.add_argument("--profile-calls", type=int, default=400)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB 20 times (HBM counter calibration) and exit")
+    args = ap.parse_args()
+
+    rank = int(os.environ.get("RANK", "0"))
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        if rank == 0:
+            print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the projection is "
+                  "data-parallel over tokens and its multi-GPU sharding is a design note, not a run", flush=True)
+        sys.exit(2)
+
+    import torch
+    import rank_gemm_unified_amd as rg
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2**20
+        src_t = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(20):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 20}), flush=True)
+        return
+    if args.workload == "prefetch":
+        prefetch_bench(args, rg, torch)
+        return
+    if args.workload == "adapters":
+        adapter_sweep_bench(args, rg, torch)
+        return
+    big = args.workload == "stack13b"
+    steps = args.steps if args.steps is not None else (20 if big else 2000)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 200)
+    w, res = measure(rg, torch, args.workload, steps, warmup, args.fuse_slots, args.profile_calls, args.replicas)
+
+    cpu = None
+    if not args.no_cpu_baseline and rank == 0:
+        log("timing the fp64 oracle on the host ...")
+        cpu = cpu_baseline(w, args.cpu_seconds, w.n_slots)
+    out = {"metric": METRIC, "value": res["value"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic (seeded; inputs resident in HBM)"}
+    out.update({k: v for k, v in res.items() if k not in out})
+    out["cpu_baseline"] = cpu
+    w.drop_cache()
+    del w
+    torch.cuda.empty_cache()
+    if args.workload == "decode" and not args.no_more:
+        # the prefill (MFMA-bound) and many-adapter (HBM-bound) workloads, timed in the same run
+        more = {}
+        for name, n_steps in (("prefill", 300), ("many", 300)):
+            w2, r2 = measure(rg, torch, name, n_steps, 30, False, args.profile_calls)
+            more[name] = {k: r2[k] for k in ("value", "unit", "ms_per_step", "steps", "config", "step_hbm_frac",
+                                             "roofline")}
+            w2.drop_cache()
+            del w2
+            torch.cuda.empty_cache()
+        out["more_workloads"] = more
     if rank == 0:
         print(json.dumps(out), flush=True)
 

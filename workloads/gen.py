@@ -138,16 +138,23 @@ class Workload:
                                      _seed(self.master, _K_W, slot), self.dtype, self.device, self.values)
         return self._cache[key]
 
+    def _draw_ab(self, aid: int):
+        r = int(self.ranks[aid])
+        shape = (self.n_slots, r, self.hidden)
+        return (_draw(shape, self.ab_std, _seed(self.master, _K_AB, aid, 0), self.dtype, self.device, self.values),
+                _draw(shape, self.ab_std, _seed(self.master, _K_AB, aid, 1), self.dtype, self.device, self.values))
+
     def adapter(self, aid: int):
         """(A_t, B), each [n_slots][r][H]; r = ranks[aid] (may be 0)."""
         key = ("AB", aid)
         if key not in self._cache:
-            r = int(self.ranks[aid])
-            shape = (self.n_slots, r, self.hidden)
-            a_t = _draw(shape, self.ab_std, _seed(self.master, _K_AB, aid, 0), self.dtype, self.device, self.values)
-            b = _draw(shape, self.ab_std, _seed(self.master, _K_AB, aid, 1), self.dtype, self.device, self.values)
-            self._cache[key] = (a_t, b)
+            self._cache[key] = self._draw_ab(aid)
         return self._cache[key]
+
+    def adapter_uncached(self, aid: int):
+        """The same (A_t, B) as ``adapter`` (same seeds, same values), drawn without keeping them: for
+        loading pools whose adapters would not fit twice in memory."""
+        return self._cache.get(("AB", aid)) or self._draw_ab(aid)
 
     def drop_cache(self, kind: str | None = None) -> None:
         for k in list(self._cache):
