@@ -375,9 +375,9 @@ __device__ __forceinline__ void decode_stream_body(
 #pragma unroll
         for (int u = 0; u < MB; ++u) {
             const int t = lq + 4 * (wave + 4 * u);
-            const int32_t key_t = __shfl(key, t & 63, 64);
+            const int32_t key_t = __shfl(key, t & 63, 64), pos_t = __shfl(my_pos, t & 63, 64);
             if (live_col && t < T && key_t == a_col) {
-                vpart[((int64_t)t * RP + j_col) * S + split] = v[u];
+                vpart[((int64_t)pos_t * RP + j_col) * S + split] = v[u];
                 if constexpr (DBG) dbg_put(dbg_gather + (int64_t)t * stride + j_col, pid_col);
             }
         }
@@ -445,9 +445,10 @@ __device__ __forceinline__ void decode_stream_body(
         // streaming stores: the finishing kernel reads each partial once (measured: 0.2 us less per call
         // than stores that keep the lines in this XCD's L2)
 #pragma unroll
-        for (int u = 0; u < MB; ++u) {
+        for (int u = 0; u < MB; ++u) {   // row of the token's sorted position, so the finish needs no record to find it
             const int e = threadIdx.x + 256 * u, t = e >> 4;
-            if (t < T) __builtin_nontemporal_store(v[u], reinterpret_cast<f32x4_t *>(ypart + ((int64_t)split * T + t) * H + n0 + 4 * (e & 15)));
+            const int pos_t = __shfl(my_pos, t & 63, 64);
+            if (t < T) __builtin_nontemporal_store(v[u], reinterpret_cast<f32x4_t *>(ypart + ((int64_t)split * T + pos_t) * H + n0 + 4 * (e & 15)));
         }
         page_store(red + TP * RS, WS, PS, plive, pa, pj, pid);
     }
@@ -538,9 +539,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream_slots(
 // ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
 // Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Thread -> (token i of the
 // group, 8 columns c, quarter q of j: j in [16 q, 16 q + 16)).  Two dependent round trips:
-//  1. by sorted position only: the token record and this quarter's B page ids;
-//  2. all at once: the quarter's 16 B-row slices, the x W partials of splits q, q + 4 and the v
-//     partials of two j's (summed in split order into LDS).
+//  1. by sorted position only: the token record, this quarter's B page ids, the x W partials of splits
+//     q, q + 4 and the v partials of two j's (both stored by sorted position);
+//  2. the quarter's 16 B-row slices.
 // The four quarter threads of a token then add their x W partials and expand terms by two lane
 // shuffles (a fixed order), and one of them rounds and stores.
 template <int SY, int SV, bool DBG>
@@ -555,7 +556,22 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
     const int i = threadIdx.x >> 5, c = ((threadIdx.x >> 2) & 7) * 8, q = threadIdx.x & 3;
     const int sp = min((int)blockIdx.y * 8 + i, T - 1);
     const bool live_tok = (int)blockIdx.y * 8 + i < T;
-    // ---- round trip 1
+    // ---- round trip 1: the record, the B page ids, and the x W and v partials (stored by sorted position,
+    // so they need nothing from the record)
+    f32x4_t part[SQ][2];
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const float *src = ypart + ((int64_t)min(q + 4 * k, SY - 1) * T + sp) * H + n0 + c;
+        part[k][0] = *reinterpret_cast<const f32x4_t *>(src);
+        part[k][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
+    }
+    const int jj = (threadIdx.x & 31) * 2;   // this thread's two j's of v
+    float pv[2 * SV];
+    {
+        const float *src = vpart + ((int64_t)sp * RP + min(jj, RP - 2)) * SV;
+#pragma unroll
+        for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
+    }
     const int4 st = sorted_tok[sp];
     int32_t pid[16];
     {
@@ -597,20 +613,6 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
         const bool pok = pg >= 0 && (int64_t)pg < num_pages;
         okm |= pok ? 1u << u : 0u;
         bv[u] = load16(pages + (int64_t)(qlive && pok ? pg : 0) * H + n0 + c);
-    }
-    f32x4_t part[SQ][2];
-#pragma unroll
-    for (int k = 0; k < SQ; ++k) {
-        const float *src = ypart + ((int64_t)min(q + 4 * k, SY - 1) * T + t) * H + n0 + c;
-        part[k][0] = *reinterpret_cast<const f32x4_t *>(src);
-        part[k][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
-    }
-    const int jj = (threadIdx.x & 31) * 2;   // this thread's two j's of v
-    float pv[2 * SV];
-    {
-        const float *src = vpart + ((int64_t)t * RP + min(jj, RP - 2)) * SV;
-#pragma unroll
-        for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
     }
     // ---- v[t][j] summed over the splits in order; entries past the rank (never written) are dropped
     {

@@ -19,7 +19,7 @@
 // The grouping of tokens by adapter (segments in order of first token, tokens in order within a
 // segment) is worked out by every workgroup from the ids, deterministically, so all agree.
 // Outputs as the T <= 64 kernel: float32 partials of x W (ypart[split]) and of s x A
-// (vpart[t][j][split]); the workgroups that own a segment check its page-table row and publish its
+// (vpart[pos][j][split]), rows in sorted-position order; the workgroups that own a segment check its page-table row and publish its
 // sorted-token records and B page ids for the finishing kernel.
 #include "device_common.h"
 #include "internal.h"
@@ -47,6 +47,7 @@ struct WideGroup {
     int32_t slot_seg[HSLOTS];
     int32_t seg_a[WT], seg_r[WT], seg_n[WT], seg_toff[WT + 1], seg_uoff[WT + 1];
     int32_t sorted[WT];                     // sorted position -> token
+    int32_t pos[WT];                        // token -> sorted position
     int32_t pub_ent[2 * 64 + 1];           // page-table row of the segment being published
     int32_t wsum[3][NW];
     int32_t pub_bad, nseg, nvalid, nunits;
@@ -263,7 +264,11 @@ __device__ __forceinline__ void decode_wide_body(
             g.nunits = t1;
         }
         lds_sync();
-        if (tokt && tid < T) g.sorted[key >= 0 ? g.seg_toff[my_seg] + rank_in : t0 + b2 + i2 - ungrouped] = tid;
+        if (tokt && tid < T) {
+            const int q = key >= 0 ? g.seg_toff[my_seg] + rank_in : t0 + b2 + i2 - ungrouped;
+            g.sorted[q] = tid;
+            g.pos[tid] = q;
+        }
         lds_sync();
     }
     const int nvalid = g.nvalid, nunits = g.nunits;
@@ -408,23 +413,26 @@ __device__ __forceinline__ void decode_wide_body(
                 const int it = u_tc[e] * 16 + 4 * lq + i;
                 if (j < rs && it < ns) {
                     const int t = g.sorted[to + it];
-                    vpart[((int64_t)t * RP + j) * S + split] = u_sc[e] * uacc[e][i];
+                    vpart[((int64_t)(to + it) * RP + j) * S + split] = u_sc[e] * uacc[e][i];   // by sorted position
                     if constexpr (DBG) dbg_put(dbg_gather + (int64_t)t * stride + j, u_pid[e]);
                 }
             }
         }
     }
 
-    // ---- x W partial of this split: lane holds column 16 nb + lrow, rows 16 (wave MBW + m) + 4 lq + i
+    // ---- x W partial of this split: lane holds column 16 nb + lrow, rows 16 (wave MBW + m) + 4 lq + i; each
+    // token's row goes to its sorted position, so the finish needs no record to find it
 #pragma unroll
     for (int m = 0; m < MBW; ++m)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int i = 0; i < 4; ++i) {
+            const int t = (wave * MBW + m) * 16 + 4 * lq + i;
+            if (t < T) {
+                const int q = g.pos[t];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = (wave * MBW + m) * 16 + 4 * lq + i;
-                if (t < T) ypart[((int64_t)split * T + t) * H + n0 + 16 * nb + lrow] = acc[m][nb][i];
+                for (int nb = 0; nb < 4; ++nb) ypart[((int64_t)split * T + q) * H + n0 + 16 * nb + lrow] = acc[m][nb][i];
             }
+        }
 
     // ---- publish: segments s = blockIdx.x + k gridDim.x -- check the page-table row (exactly 2r pages
     // in range, -1 after), then write the segment's sorted-token records and B page ids; workgroup 0
