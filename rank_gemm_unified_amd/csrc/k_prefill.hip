@@ -218,7 +218,6 @@ __device__ __forceinline__ void prefill_main_body(
     int32_t n_tiles_n, uint16_t *__restrict__ y, const DebugOut dbg = DebugOut{}) {
     extern __shared__ __align__(16) uint16_t sm[];
     __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
-    __shared__ int32_t s_bpg[DBG ? 64 : 1];   // debug: the B pages of the adapter being added
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
     // Tile order.  The first P0 = roundup(n_tiles_n, 8) workgroups take the last row of tiles, one
@@ -386,43 +385,29 @@ __device__ __forceinline__ void prefill_main_body(
         for (int k = 0; k < LR_V; ++k)
             lds_gload16(vsrc(k), (lds_void *)(stg + 64 * BN + (PF_THREADS * k + 64 * wave) * 8));
     };
-    // each thread clears, in its own pieces, B rows in [r, roundup(r, 16)) and v entries of other
-    // adapters' rows or past r (the pages may hold any bits, NaN included, and 0 * NaN is NaN)
-    auto lr_mask = [&](uint16_t *stg, int li) {
+    // The K-extension of adapter li: rp / 16 substeps of 32x32x16 MFMAs on the accumulators.  The v
+    // operand (the tile's v rows, all adapters, in Vs) is masked in registers: rows of other adapters and
+    // entries past the rank are zero (v16 entries past the rank may hold any bits, NaN included, and
+    // 0 * NaN is NaN).  B rows past the rank are stand-ins (row r - 1: finite adapter values) and meet
+    // those zeros.  The B operand (8 consecutive j of one column) is gathered with 2-byte reads, lane ->
+    // column.
+    int32_t rkey[WMI];   // the adapter of each row this lane's v fragments cover
+#pragma unroll
+    for (int mi = 0; mi < WMI; ++mi) rkey[mi] = s_key[wm * WTM + mi * 32 + frow];
+    auto lr_mfma = [&](const uint16_t *Bn, const uint16_t *Vs, int li) {
         const int32_t a = s_list[li], r = s_lr[li], rp = (r + 15) & ~15;
-        const u32x4_t zero = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < LR_K; ++k) {
-            const int idx = tid + PF_THREADS * k, j = idx >> 5;
-            if (j >= r && j < rp) store16(stg + idx * 8, zero);
-        }
-#pragma unroll
-        for (int k = 0; k < LR_V; ++k) {
-            const int idx = tid + PF_THREADS * k, row = idx >> 3, j0 = 8 * ((idx & 7) ^ ((row >> 1) & 7));
-            uint16_t *q = stg + 64 * BN + idx * 8;
-            if (j0 >= rp) continue;   // never read
-            if (s_key[row] != a || j0 >= r) {
-                store16(q, zero);
-            } else if (j0 + 8 > r) {
-                u32x4_t v = load16(q);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = j0 + 2 * e < r ? 0xffffu : 0u, hi = j0 + 2 * e + 1 < r ? 0xffff0000u : 0u;
-                    v[e] &= lo | hi;
-                }
-                store16(q, v);
-            }
-        }
-    };
-    // the K-extension: rp / 16 substeps of 32x32x16 MFMAs on the accumulators; the B operand (8
-    // consecutive j of one column) is gathered with 2-byte reads, lane -> column
-    auto lr_mfma = [&](const uint16_t *stg, int li) {
-        const int32_t rp = (s_lr[li] + 15) & ~15;
-        const uint16_t *Bn = stg, *Vs = stg + 64 * BN;
         for (int ks = 0; ks < rp / 16; ++ks) {
             u32x4_t la[WMI], lb[WNI];
+            const int jb = ks * 16 + fk;   // this lane's first j
 #pragma unroll
-            for (int mi = 0; mi < WMI; ++mi) la[mi] = load16(Vs + swz(wm * WTM + mi * 32 + frow, ks * 2 + (fk >> 3)));
+            for (int mi = 0; mi < WMI; ++mi) {
+                u32x4_t v = load16(Vs + swz(wm * WTM + mi * 32 + frow, ks * 2 + (fk >> 3)));
+                const int nv = rkey[mi] == a ? min(max(r - jb, 0), 8) : 0;   // entries kept
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] &= (2 * e < nv ? 0xffffu : 0u) | (2 * e + 1 < nv ? 0xffff0000u : 0u);
+                la[mi] = v;
+            }
 #pragma unroll
             for (int ni = 0; ni < WNI; ++ni) {
                 const int col = wn * WTN + ni * 32 + frow, cp = col >> 3, ce = col & 7;
@@ -441,41 +426,27 @@ __device__ __forceinline__ void prefill_main_body(
                                                                           acc[mi][ni], 0, 0, 0);
         }
     };
-    // debug: the B pages the K-extension of adapter li used (its thread-held page ids), recorded for
-    // every row of the tile that belongs to the adapter
+    // B rows of an adapter straight into a buffer of [64][BN] (LR_K loads per thread, rows past the rank
+    // are stand-ins, so the count is fixed)
+    auto lr_issue_b = [&](uint16_t *buf, const int32_t *pg) {
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k)
+            lds_gload16(bsrc(pg, k), (lds_void *)(buf + (PF_THREADS * k + 64 * wave) * 8));
+    };
+    // debug: the B page each B row of adapter li was loaded from (as the loads above used it), recorded
+    // for every row of the tile that belongs to the adapter (one thread per B row)
     auto dbg_b = [&](int li, const int32_t *pg) {
         if constexpr (DBG) {
             const int32_t a = s_list[li], r = s_lr[li];
-            __syncthreads();
 #pragma unroll
             for (int k = 0; k < LR_K; ++k) {
                 const int idx = tid + PF_THREADS * k, j = idx >> 5;
-                if ((idx & 31) == 0 && j < r) s_bpg[j] = pg[k];
+                if ((idx & 31) == 0 && j < r)
+                    for (int row = 0; row < BM; ++row)
+                        if (m0 + row < T && s_key[row] == a)
+                            dbg_put(dbg.gather + (int64_t)(m0 + row) * stride + r + j, pg[k]);
             }
-            __syncthreads();
-            for (int e = tid; e < BM * 64; e += PF_THREADS) {
-                const int row = e >> 6, j = e & 63;
-                if (j < r && m0 + row < T && s_key[row] == a)
-                    dbg_put(dbg.gather + (int64_t)(m0 + row) * stride + r + j, s_bpg[j]);
-            }
-            __syncthreads();
         }
-    };
-    // the same operands through registers (the caller has made the stage free with a barrier)
-    auto lr_regs = [&](uint16_t *stg, int li, const int32_t *pg) {
-        u32x4_t bv[LR_K], vv[LR_V];
-#pragma unroll
-        for (int k = 0; k < LR_K; ++k) bv[k] = load16(bsrc(pg, k));
-#pragma unroll
-        for (int k = 0; k < LR_V; ++k) vv[k] = load16(vsrc(k));
-#pragma unroll
-        for (int k = 0; k < LR_K; ++k) store16(stg + (tid + PF_THREADS * k) * 8, bv[k]);
-#pragma unroll
-        for (int k = 0; k < LR_V; ++k) store16(stg + 64 * BN + (tid + PF_THREADS * k) * 8, vv[k]);
-        lr_mask(stg, li);   // this thread's own pieces: its LDS accesses are in order
-        __syncthreads();
-        lr_mfma(stg, li);
-        __syncthreads();
     };
 
     if (nk > 1) dma(1, sm + STAGE);
@@ -527,20 +498,65 @@ __device__ __forceinline__ void prefill_main_body(
     step(nk - 1, std::integral_constant<int, 2>());
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every load, the low-rank operands' included, has landed
 
-    // ---- low-rank term: one K-extension per adapter owning rows of this tile
+    // ---- low-rank term: one K-extension per adapter owning rows of this tile.  Adapter 0's B rows and
+    // the tile's v rows came into stage X during the K loop's second-to-last step.  The B rows of
+    // adapter li rotate through three buffers -- X's B part and the two halves of stage Y, free since
+    // the last K step -- and go out two adapters ahead of their MFMAs; their page ids two further ahead,
+    // in two register sets taken in turn.  Each adapter waits for its own loads only (the count of
+    // younger loads is exact: every load group has a fixed size), then for one barrier, after which the
+    // buffer of adapter li - 1 is free for adapter li + 2.
     if (nlist > 0) {
-        uint16_t *stg = sm + (nk & 1) * STAGE;   // the stage step nk - 2 (or, for one step, the prologue) filled
-        lr_mask(stg, 0);
-        __syncthreads();
-        lr_mfma(stg, 0);
+        uint16_t *const X = sm + (nk & 1) * STAGE, *const Y = sm + ((nk + 1) & 1) * STAGE;
+        const uint16_t *const Vs = X + 64 * BN;
+        auto buf = [&](int li) { const int m = li % 3; return m == 0 ? X : m == 1 ? Y : Y + 64 * BN; };
+        auto lds_barrier = [] {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        int32_t pg1[LR_K] = {}, pgA[LR_K] = {}, pgB[LR_K] = {};
+        if (nlist > 1) lr_pages(1, pg1);
+        if (nlist > 2) lr_pages(2, pgA);
+        if (nlist > 3) lr_pages(3, pgB);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nlist > 1) {
+            lr_issue_b(buf(1), pg1);
+            dbg_b(1, pg1);
+        }
         dbg_b(0, pg0);
-    }
-    __syncthreads();
-    for (int li = 1; li < nlist; ++li) {
-        int32_t pg[LR_K];
-        lr_pages(li, pg);
-        lr_regs(sm, li, pg);
-        dbg_b(li, pg);
+        __builtin_amdgcn_sched_barrier(0);
+        // iteration li: wait for adapter li's B rows (v and adapter 0's rows were waited for after the K
+        // loop), barrier, issue adapter li + 2's rows (ids in `use`) and adapter li + 4's ids (into `use`),
+        // then adapter li's MFMAs
+        auto iter = [&](int li, int32_t *use) {
+            if (li >= 1) {
+                // loads younger than adapter li's B rows: li = 1: [B(2), ids(4)]; li >= 2: [ids(li + 2),
+                // B(li + 1), ids(li + 3)] -- those that were issued
+                const int n = li == 1 ? (nlist > 2) + (nlist > 4)
+                                      : (li + 2 < nlist) + (li + 1 < nlist) + (li + 3 < nlist);
+                static_assert(LR_K == 4, "wait counts");
+                // (the debug instantiation's atomics count as memory operations too: it waits for all)
+                if (n == 0 || DBG) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            }
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (li + 2 < nlist) {
+                lr_issue_b(buf(li + 2), use);
+                dbg_b(li + 2, use);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (li + 4 < nlist) lr_pages(li + 4, use);
+            __builtin_amdgcn_sched_barrier(0);
+            lr_mfma(buf(li), Vs, li);
+        };
+        for (int li = 0; li < nlist; li += 2) {
+            iter(li, pgA);
+            if (li + 1 < nlist) iter(li + 1, pgB);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stand-in loads past the end have landed
     }
 
     // ---- one rounding, and each lane stores its own elements with 2-byte streaming stores (the 32
