@@ -17,9 +17,9 @@ Prints one JSON line: the throughput, the dominant kernel's roofline fraction (i
 bytes or flops over its average device time, from HIP events recorded on its launch stream) with
 the whole call's fraction beside it (roofline.call), and the fp64 CPU oracle timed on this host as a
 baseline.  The default run also times the prefill batch (MFMA-bound) and the 2000-adapter batch
-(HBM-bound) and adds their lines' figures under "more_workloads".  With --fuse-slots the slots that
-read the same x (a layer's q, k and v) are projected by one lora_project_slots call; the per-launch
-figures then cover every slot of the launch.  --workload stack13b runs the whole 40-layer stack
+(HBM-bound) and adds their lines' figures under "more_workloads".  With --fuse-slots a layer's q, k, v
+and o (each with its own x) are projected by one lora_project_slots_x call; the per-launch figures then
+cover every slot of the launch.  --workload stack13b runs the whole 40-layer stack
 (160 slots, a 115 GiB pool, one replica: a step moves 42 GiB, far beyond the Infinity Cache).
 """
 from __future__ import annotations
@@ -351,11 +351,10 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
         ys = [torch.empty_like(xs[0]) for _ in slots]
         reps.append((pool, Ws, xs, ys))
     # the calls of one step: one per slot, or (fuse_slots) one per run of up to LORA_MAX_CALL_SLOTS
-    # slots that read the same x
+    # consecutive slots (a layer's q, k, v and o: lora_project_slots_x, each slot with its own x)
     groups = []
     for s in slots:
-        if (fuse_slots and groups and w.slot_x[groups[-1][0]] == w.slot_x[s]
-                and len(groups[-1]) < rg.LORA_MAX_CALL_SLOTS):
+        if fuse_slots and groups and len(groups[-1]) < rg.LORA_MAX_CALL_SLOTS:
             groups[-1].append(s)
         else:
             groups.append([s])
@@ -372,7 +371,7 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
             calls = []
             for g in groups:
                 n = len(g)
-                calls.append((n, (ctypes.c_int32 * n)(*g), xs[w.slot_x[g[0]]].data_ptr(),
+                calls.append((n, (ctypes.c_int32 * n)(*g), (ctypes.c_void_p * n)(*[xs[w.slot_x[s]].data_ptr() for s in g]),
                               (ctypes.c_void_p * n)(*[Ws[s].data_ptr() for s in g]),
                               (ctypes.c_void_p * n)(*[ys[s].data_ptr() for s in g])))
             fused.append(calls)
@@ -381,8 +380,8 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
         pool, Ws, xs, ys = reps[i % R]
         if fuse_slots:
             for n, sl, xp, wp, yp in fused[i % R]:
-                rg._lib.lora_project_slots(pool.handle, n, sl, xp, wp, d_ids.data_ptr(), d_ranks.data_ptr(),
-                                           d_scale.data_ptr(), w.T, yp, ws.data_ptr(), wsb, sh)
+                rg._lib.lora_project_slots_x(pool.handle, n, sl, xp, wp, d_ids.data_ptr(), d_ranks.data_ptr(),
+                                             d_scale.data_ptr(), w.T, yp, ws.data_ptr(), wsb, sh)
             return
         for s in slots:
             rg._lib.lora_project(pool.handle, xs[w.slot_x[s]].data_ptr(), Ws[s].data_ptr(), pool.table[s].data_ptr(),
@@ -495,8 +494,8 @@ def main():
                          "pinned host memory beside the decode projection; adapters runs the 1/10/100/1000-adapter "
                          "load test")
     ap.add_argument("--fuse-slots", action="store_true",
-                    help="project the slots that read the same x (a layer's q, k, v) in one lora_project_slots "
-                         "call (up to 4 slots per call) instead of one lora_project call per slot")
+                    help="project up to 4 consecutive slots (a layer's q, k, v and o, each with its own x) in one "
+                         "lora_project_slots_x call instead of one lora_project call per slot")
     ap.add_argument("--no-more", action="store_true",
                     help="default workload only: skip the extra prefill and many-adapter blocks")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")

@@ -279,6 +279,21 @@ int lora_project_slots(lora_pool *pool, int32_t n, const int32_t *slots, const v
                        size_t workspace_bytes, void *stream);
 
 /*
+ * lora_project_slots where each slot reads its own input rows: x is a host array of n device
+ * pointers (each as lora_project's x; slots may share one).  The q, k, v and o projections of a layer
+ * act on the same tokens but o reads the attention output, not the layer input ("S-LoRA, in depth":
+ * an adapter has A and B for each of the projections of each layer); with this call all four go in
+ * one launch per stage, so their tiles share the chip.  For each z < n,
+ *     y[z][t] = x[z][t] W[z] + s[a] * (x[z][t] A_{slots[z],a}) B_{slots[z],a},   a = adapter_ids[t],
+ * bit for bit what lora_project gives for that slot.  No output may overlap any input or another
+ * output.  Workspace, errors and device checks as lora_project_slots.
+ */
+int lora_project_slots_x(lora_pool *pool, int32_t n, const int32_t *slots, const void *const *x,
+                         const void *const *W, const int32_t *adapter_ids, const int32_t *ranks,
+                         const float *scale, int64_t T, void *const *y, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
  * The projection with its own indices exposed ("S-LoRA, in depth", section "The architecture": the
  * gather fetches each request's A and B pages from wherever the pool placed them).  Runs exactly the
  * kernels lora_project runs for these arguments -- in instantiations that also record the indices

@@ -74,6 +74,7 @@ _SIGS = {
     "lora_project_workspace_size": (_sz, [_vp, _i64]),
     "lora_project_slots_workspace_size": (_sz, [_vp, _i32, _i64]),
     "lora_project_slots": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "lora_project_slots_x": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_debug_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp]),
     "lora_debug_project": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp]),
@@ -293,6 +294,22 @@ def lora_debug_gather(pool, page_table, adapter_ids, ranks, T, out, stream=None,
     return _check(rc, "lora_debug_gather") if check else rc
 
 
+def lora_project_slots_x(pool, slots, xs, Ws, adapter_ids, ranks, scale, T, ys, workspace, workspace_bytes=None,
+                         stream=None, check=True):
+    """slots: sequence of slot indices; xs, Ws, ys: sequences of tensors (or addresses), one per slot."""
+    n = len(slots)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    xp = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in xs])
+    wp = (ctypes.c_void_p * max(n, 1))(*[_ptr(w) for w in Ws])
+    yp = (ctypes.c_void_p * max(n, 1))(*[_ptr(y) for y in ys])
+    rc = _lib.lora_project_slots_x(pool, n, sl.ctypes.data, ctypes.cast(xp, ctypes.c_void_p),
+                                   ctypes.cast(wp, ctypes.c_void_p), _ptr(adapter_ids), _ptr(ranks), _ptr(scale), T,
+                                   ctypes.cast(yp, ctypes.c_void_p), _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(rc, "lora_project_slots_x") if check else rc
+
+
 def lora_debug_project(pool, x, W, page_table, adapter_ids, ranks, scale, T, y, workspace, gather_out, order_out,
                        workspace_bytes=None, stream=None, check=True):
     if workspace_bytes is None:
@@ -406,13 +423,20 @@ class Pool:
         return run_pool_ops(self.handle, ops, ranks, adapter_weights, stream)
 
     def project_slots(self, slots, x, Ws, adapter_ids, ranks, scale, ys=None, stream=None):
-        T = x.shape[0]
+        """x: one tensor every slot reads (lora_project_slots), or a list with one per slot
+        (lora_project_slots_x)."""
+        per_slot = isinstance(x, (list, tuple))
+        x0 = x[0] if per_slot else x
+        T = x0.shape[0]
         if ys is None:
-            ys = [self.torch.empty_like(x) for _ in slots]
+            ys = [self.torch.empty_like(x0) for _ in slots]
         need = lora_project_slots_workspace_size(self.handle, len(slots), T)
         if self._ws is None or self._ws.numel() < need:
             self._ws = self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=self.pages.device)
-        lora_project_slots(self.handle, slots, x, Ws, adapter_ids, ranks, scale, T, ys, self._ws, stream=stream)
+        if per_slot:
+            lora_project_slots_x(self.handle, slots, x, Ws, adapter_ids, ranks, scale, T, ys, self._ws, stream=stream)
+        else:
+            lora_project_slots(self.handle, slots, x, Ws, adapter_ids, ranks, scale, T, ys, self._ws, stream=stream)
         return ys
 
     def project(self, slot, x, W, adapter_ids, ranks, scale, y=None, stream=None):

@@ -120,13 +120,14 @@ struct Ws {
 };
 Ws carve(void *base, const Plan &plan);
 
-// Per-slot pointers of one call: up to MAX_CALL_SLOTS slots that share x and the tokens' adapter
-// ids (the q, k and v projections of a layer).  The argument of the several-slot kernels, indexed
+// Per-slot pointers of one call: up to MAX_CALL_SLOTS slots that share the tokens and their adapter
+// ids (the q, k, v and o projections of a layer; q, k and v also share x).  The argument of the several-slot kernels, indexed
 // by blockIdx.z (a one-slot call launches the one-slot kernels, whose arguments are the slot's
 // pointers themselves); the token grouping of the prefill path lives in slot 0's workspace region
 // and serves every slot.
 constexpr int MAX_CALL_SLOTS = 4;
 struct SlotPtrs {
+    const void *x[MAX_CALL_SLOTS];       // the slot's input rows (slots may share one)
     const void *W[MAX_CALL_SLOTS];
     void *y[MAX_CALL_SLOTS];
     const int32_t *pt[MAX_CALL_SLOTS];   // the slot's page table [max_adapters][2 max_rank]

@@ -526,12 +526,13 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream_dbg(
 
 template <int MB, int KQ>
 __global__ __launch_bounds__(256, 1) void k_decode_stream_slots(
-    const uint16_t *__restrict__ x, const SlotPtrs sp, const uint16_t *__restrict__ pages, int64_t num_pages,
+    const SlotPtrs sp, const uint16_t *__restrict__ pages, int64_t num_pages,
     int32_t stride, const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const float *__restrict__ scale,
     int32_t max_adapters, int32_t max_rank, int32_t T, int32_t H, int32_t S, int32_t n_tiles, int32_t RP,
     int *__restrict__ err_word) {
     const int z = blockIdx.z;
-    decode_stream_body<MB, KQ, false>(x, (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z], stride, ids, ranks,
+    decode_stream_body<MB, KQ, false>((const uint16_t *)sp.x[z], (const uint16_t *)sp.W[z], pages, num_pages, sp.pt[z],
+                                      stride, ids, ranks,
                                       scale, max_adapters, max_rank, T, H, S, n_tiles, RP, sp.ypart[z], sp.v[z],
                                       (int4 *)sp.sorted_tok[z], sp.spages[z], err_word, nullptr);
 }
@@ -790,7 +791,7 @@ static hipError_t launch_stream(const lora_pool *p, const Plan &plan, const void
                            (int4 *)sp.sorted_tok[0], sp.spages[0], p->dev_err);
     else
         hipLaunchKernelGGL((k_decode_stream_slots<MB, KQ>), dim3(plan.n_tiles * plan.ysplit, 1, n), dim3(256), lds,
-                           s, (const uint16_t *)x, sp, (const uint16_t *)p->pages, p->num_pages, 2 * p->max_rank, ids,
+                           s, sp, (const uint16_t *)p->pages, p->num_pages, 2 * p->max_rank, ids,
                            ranks, scale, p->max_adapters, p->max_rank, (int32_t)plan.T, p->hidden, plan.ysplit,
                            plan.n_tiles, plan.rp, p->dev_err);
     return hipGetLastError();

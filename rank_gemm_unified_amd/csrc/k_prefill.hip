@@ -142,12 +142,12 @@ __global__ __launch_bounds__(256) void k_shrink_mfma_dbg(const uint16_t *__restr
 }
 
 template <int SNS>
-__global__ __launch_bounds__(256) void k_shrink_mfma_slots(const uint16_t *__restrict__ x,
-                                                           const uint16_t *__restrict__ pages, int32_t H,
+__global__ __launch_bounds__(256) void k_shrink_mfma_slots(const uint16_t *__restrict__ pages, int32_t H,
                                                            const SlotPtrs sp, int32_t stride,
                                                            const int32_t *__restrict__ perm,
                                                            const int4 *__restrict__ item_rec, int32_t T, int32_t R) {
-    shrink_body<SNS, false>(x, pages, H, sp.pt[blockIdx.z], stride, perm, item_rec, sp.v[blockIdx.z], T, R);
+    shrink_body<SNS, false>((const uint16_t *)sp.x[blockIdx.z], pages, H, sp.pt[blockIdx.z], stride, perm, item_rec,
+                            sp.v[blockIdx.z], T, R);
 }
 
 // v16[t][j] = bf16(s_a * sum_split vpart[split][t][j]) for tokens with an adapter; zero for
@@ -597,11 +597,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_dbg(
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_slots(
-    const uint16_t *__restrict__ x, const SlotPtrs sp, const uint16_t *__restrict__ pages, int32_t stride,
+    const SlotPtrs sp, const uint16_t *__restrict__ pages, int32_t stride,
     const int32_t *__restrict__ tok_a, const int32_t *__restrict__ tok_r, int32_t R, int32_t T, int32_t H,
     int32_t n_tiles_n) {
     const int z = blockIdx.z;
-    prefill_main_body<false>(x, (const uint16_t *)sp.W[z], pages, sp.pt[z], stride, tok_a, tok_r,
+    prefill_main_body<false>((const uint16_t *)sp.x[z], (const uint16_t *)sp.W[z], pages, sp.pt[z], stride, tok_a, tok_r,
                              (const uint16_t *)sp.v16[z], R, T, H, n_tiles_n, (uint16_t *)sp.y[z]);
 }
 
@@ -648,10 +648,10 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
                                ws.perm, ws.item_rec, sp.v[0], T, plan.rp);
     } else {
         if (sns == 6)
-            hipLaunchKernelGGL(k_shrink_mfma_slots<6>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp, stride,
+            hipLaunchKernelGGL(k_shrink_mfma_slots<6>, g1, dim3(256), sh_lds, s, pages, p->hidden, sp, stride,
                                ws.perm, ws.item_rec, T, plan.rp);
         else
-            hipLaunchKernelGGL(k_shrink_mfma_slots<4>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp, stride,
+            hipLaunchKernelGGL(k_shrink_mfma_slots<4>, g1, dim3(256), sh_lds, s, pages, p->hidden, sp, stride,
                                ws.perm, ws.item_rec, T, plan.rp);
     }
     hipError_t e = hipGetLastError();
@@ -676,7 +676,7 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
                            pages, sp.pt[0], stride, ws.tok_a, ws.tok_r, (const uint16_t *)sp.v16[0], plan.rp, T,
                            p->hidden, tn, (uint16_t *)sp.y[0]);
     else
-        hipLaunchKernelGGL(k_prefill_main_slots, dim3(grid, 1, n), dim3(PF_THREADS), MAIN_LDS, s, xh, sp, pages,
+        hipLaunchKernelGGL(k_prefill_main_slots, dim3(grid, 1, n), dim3(PF_THREADS), MAIN_LDS, s, sp, pages,
                            stride, ws.tok_a, ws.tok_r, plan.rp, T, p->hidden, tn);
     return hipGetLastError();
 }

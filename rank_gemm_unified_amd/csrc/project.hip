@@ -120,10 +120,10 @@ extern "C" size_t lora_project_workspace_size(const lora_pool *p, int64_t T) {
 
 namespace {
 
-// One call for n slots that share x, ids, ranks and scale (n = 1: lora_project).  The workspace
-// holds n regions of one plan each; the prefill path's token grouping lives in region 0 and
-// serves every slot.  Every argument is checked before any device work.
-int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void *const *W,
+// One call for n slots that share the tokens (ids, ranks, scale), each with its own x, W and y
+// (n = 1: lora_project).  The workspace holds n regions of one plan each; the prefill path's token
+// grouping lives in region 0 and serves every slot.  Every argument is checked before any device work.
+int project_impl(lora_pool *p, const char *fn, int n, const void *const *X, const void *const *W,
                  const int32_t *const *pt, const int32_t *ids, const int32_t *ranks, const float *scale, int64_t T,
                  void *const *y, void *ws, size_t ws_bytes, void *stream, const DebugOut *dbg = nullptr) {
     if (!p) return set_error(LORA_EINVAL, "%s: pool is NULL", fn);
@@ -131,19 +131,23 @@ int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void 
     if (T < 0 || T > MAX_TOKENS)
         return set_error(LORA_EINVAL, "%s: T = %lld not in [0, %lld]", fn, (long long)T, (long long)MAX_TOKENS);
     if (T == 0) return LORA_OK;
-    if (!x || !ids || !ranks || !scale || !ws) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
-    if (!aligned(x, 16) || !aligned(ids, 4) || !aligned(ranks, 4) || !aligned(scale, 4) || !aligned(ws, 256))
+    if (!ids || !ranks || !scale || !ws) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
+    if (!aligned(ids, 4) || !aligned(ranks, 4) || !aligned(scale, 4) || !aligned(ws, 256))
         return set_error(LORA_EINVAL, "%s: misaligned pointer (x, W, y: 16 B; ids, ranks, scale, page_table: 4 B; "
                                       "workspace: 256 B)", fn);
     const size_t xbytes = (size_t)T * p->hidden * p->elem;
-    const char *xb = (const char *)x;
     for (int z = 0; z < n; ++z) {
-        if (!W[z] || !pt[z] || !y[z]) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
-        if (!aligned(W[z], 16) || !aligned(y[z], 16) || !aligned(pt[z], 4))
+        if (!X[z] || !W[z] || !pt[z] || !y[z]) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
+        if (!aligned(X[z], 16) || !aligned(W[z], 16) || !aligned(y[z], 16) || !aligned(pt[z], 4))
             return set_error(LORA_EINVAL, "%s: misaligned pointer (x, W, y: 16 B; ids, ranks, scale, page_table: 4 B; "
                                           "workspace: 256 B)", fn);
+    }
+    for (int z = 0; z < n; ++z) {   // no output may overlap an input or another output
         const char *yb = (const char *)y[z];
-        if (xb < yb + xbytes && yb < xb + xbytes) return set_error(LORA_EINVAL, "%s: y overlaps x", fn);
+        for (int u = 0; u < n; ++u) {
+            const char *xb = (const char *)X[u];
+            if (xb < yb + xbytes && yb < xb + xbytes) return set_error(LORA_EINVAL, "%s: y overlaps x", fn);
+        }
         for (int u = 0; u < z; ++u) {
             const char *ub = (const char *)y[u];
             if (ub < yb + xbytes && yb < ub + xbytes) return set_error(LORA_EINVAL, "%s: two outputs overlap", fn);
@@ -160,6 +164,7 @@ int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void 
     for (int z = 0; z < MAX_CALL_SLOTS; ++z) {
         const int k = z < n ? z : 0;
         const Ws wz = carve((char *)ws + (size_t)k * pl.total, pl);
+        sp.x[z] = X[k];
         sp.W[z] = W[k];
         sp.y[z] = y[k];
         sp.pt[z] = pt[k];
@@ -188,9 +193,9 @@ int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void 
     }
     if (ev) LP_HIP(hipEventRecord(ev[1], s));
     switch (pl.path) {
-        case PATH_DECODE: e = launch_decode(p, pl, x, ids, ranks, scale, sp, n, s, ev ? ev[2] : nullptr, dbg); break;
-        case PATH_PREFILL: e = launch_prefill(p, pl, w0, x, scale, sp, n, s, ev ? ev[2] : nullptr, dbg); break;
-        case PATH_F32: e = launch_f32(p, pl, w0, x, W[0], pt[0], scale, y[0], s, ev ? ev[2] : nullptr, dbg); break;
+        case PATH_DECODE: e = launch_decode(p, pl, X[0], ids, ranks, scale, sp, n, s, ev ? ev[2] : nullptr, dbg); break;
+        case PATH_PREFILL: e = launch_prefill(p, pl, w0, X[0], scale, sp, n, s, ev ? ev[2] : nullptr, dbg); break;
+        case PATH_F32: e = launch_f32(p, pl, w0, X[0], W[0], pt[0], scale, y[0], s, ev ? ev[2] : nullptr, dbg); break;
     }
     if (e != hipSuccess) return hip_error(e, "projection kernel launch");
     if (ev) LP_HIP(hipEventRecord(ev[3], s));
@@ -202,7 +207,7 @@ int project_impl(lora_pool *p, const char *fn, int n, const void *x, const void 
 extern "C" int lora_project(lora_pool *p, const void *x, const void *W, const int32_t *pt, const int32_t *ids,
                             const int32_t *ranks, const float *scale, int64_t T, void *y, void *ws,
                             size_t ws_bytes, void *stream) {
-    return project_impl(p, "lora_project", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream);
+    return project_impl(p, "lora_project", 1, &x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream);
 }
 
 extern "C" size_t lora_project_slots_workspace_size(const lora_pool *p, int32_t n, int64_t T) {
@@ -212,42 +217,58 @@ extern "C" size_t lora_project_slots_workspace_size(const lora_pool *p, int32_t 
     return pl.total * (size_t)n;
 }
 
-extern "C" int lora_project_slots(lora_pool *p, int32_t n, const int32_t *slots, const void *x,
-                                  const void *const *W, const int32_t *ids, const int32_t *ranks, const float *scale,
-                                  int64_t T, void *const *y, void *ws, size_t ws_bytes, void *stream) {
-    if (!p) return set_error(LORA_EINVAL, "lora_project_slots: pool is NULL");
-    if (n < 1 || n > MAX_CALL_SLOTS)
-        return set_error(LORA_EINVAL, "lora_project_slots: n = %d not in [1, %d]", n, MAX_CALL_SLOTS);
-    if (!slots || !W || !y) return set_error(LORA_EINVAL, "lora_project_slots: NULL pointer argument");
+namespace {
+int project_slots_impl(lora_pool *p, const char *fn, int32_t n, const int32_t *slots, const void *const *X,
+                       const void *const *W, const int32_t *ids, const int32_t *ranks, const float *scale, int64_t T,
+                       void *const *y, void *ws, size_t ws_bytes, void *stream) {
+    if (!p) return set_error(LORA_EINVAL, "%s: pool is NULL", fn);
+    if (n < 1 || n > MAX_CALL_SLOTS) return set_error(LORA_EINVAL, "%s: n = %d not in [1, %d]", fn, n, MAX_CALL_SLOTS);
+    if (!slots || !X || !W || !y) return set_error(LORA_EINVAL, "%s: NULL pointer argument", fn);
     const int32_t *pts[MAX_CALL_SLOTS];
     for (int z = 0; z < n; ++z) {
         if (slots[z] < 0 || slots[z] >= p->n_slots)
-            return set_error(LORA_EINVAL, "lora_project_slots: slot %d not in [0, %d)", slots[z], p->n_slots);
+            return set_error(LORA_EINVAL, "%s: slot %d not in [0, %d)", fn, slots[z], p->n_slots);
         pts[z] = p->page_table ? p->page_table + (size_t)slots[z] * p->max_adapters * 2 * p->max_rank : nullptr;
     }
     if (p->dtype == LORA_F32) {   // the float32 path (parity only) runs the slots one after another
-        if (T <= 0 || T > MAX_TOKENS) return project_impl(p, "lora_project_slots", n, x, W, pts, ids, ranks, scale, T,
-                                                           y, ws, ws_bytes, stream);   // T = 0: nothing; else the error
+        if (T <= 0 || T > MAX_TOKENS) return project_impl(p, fn, n, X, W, pts, ids, ranks, scale, T, y, ws, ws_bytes,
+                                                          stream);   // T = 0: nothing; else the error
         Plan pl;
-        if (!make_plan(p, T, &pl)) return set_error(LORA_EINVAL, "lora_project_slots: bad T");
+        if (!make_plan(p, T, &pl)) return set_error(LORA_EINVAL, "%s: bad T", fn);
         if (ws_bytes < pl.total * (size_t)n)
-            return set_error(LORA_EINVAL, "lora_project_slots: workspace %zu bytes < %zu needed", ws_bytes,
-                             pl.total * (size_t)n);
+            return set_error(LORA_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, pl.total * (size_t)n);
         const size_t ybytes = (size_t)T * p->hidden * p->elem;
-        for (int z = 0; z < n; ++z)   // all checks before the first launch: outputs must not overlap
-            for (int u = 0; u < z; ++u) {
-                const char *a = (const char *)y[z], *b = (const char *)y[u];
-                if (a && b && a < b + ybytes && b < a + ybytes)
-                    return set_error(LORA_EINVAL, "lora_project_slots: two outputs overlap");
+        for (int z = 0; z < n; ++z) {   // all checks before the first launch: no output overlaps an input or output
+            const char *a = (const char *)y[z];
+            for (int u = 0; u < n; ++u) {
+                const char *b = (const char *)X[u], *c = (const char *)y[u];
+                if (a && b && a < b + ybytes && b < a + ybytes) return set_error(LORA_EINVAL, "%s: y overlaps x", fn);
+                if (u < z && a && c && a < c + ybytes && c < a + ybytes)
+                    return set_error(LORA_EINVAL, "%s: two outputs overlap", fn);
             }
+        }
         for (int z = 0; z < n; ++z) {
-            const int rc = project_impl(p, "lora_project_slots", 1, x, &W[z], &pts[z], ids, ranks, scale, T, &y[z],
+            const int rc = project_impl(p, fn, 1, &X[z], &W[z], &pts[z], ids, ranks, scale, T, &y[z],
                                         (char *)ws + (size_t)z * pl.total, ws_bytes - (size_t)z * pl.total, stream);
             if (rc) return rc;
         }
         return LORA_OK;
     }
-    return project_impl(p, "lora_project_slots", n, x, W, pts, ids, ranks, scale, T, y, ws, ws_bytes, stream);
+    return project_impl(p, fn, n, X, W, pts, ids, ranks, scale, T, y, ws, ws_bytes, stream);
+}
+}  // namespace
+
+extern "C" int lora_project_slots_x(lora_pool *p, int32_t n, const int32_t *slots, const void *const *x,
+                                    const void *const *W, const int32_t *ids, const int32_t *ranks, const float *scale,
+                                    int64_t T, void *const *y, void *ws, size_t ws_bytes, void *stream) {
+    return project_slots_impl(p, "lora_project_slots_x", n, slots, x, W, ids, ranks, scale, T, y, ws, ws_bytes, stream);
+}
+
+extern "C" int lora_project_slots(lora_pool *p, int32_t n, const int32_t *slots, const void *x,
+                                  const void *const *W, const int32_t *ids, const int32_t *ranks, const float *scale,
+                                  int64_t T, void *const *y, void *ws, size_t ws_bytes, void *stream) {
+    const void *X[MAX_CALL_SLOTS] = {x, x, x, x};
+    return project_slots_impl(p, "lora_project_slots", n, slots, X, W, ids, ranks, scale, T, y, ws, ws_bytes, stream);
 }
 
 extern "C" int lora_profile_start(lora_pool *p, int32_t max_calls) {
@@ -293,7 +314,7 @@ extern "C" int lora_debug_project(lora_pool *p, const void *x, const void *W, co
     if (!aligned(gather_out, 4) || !aligned(order_out, 4))
         return set_error(LORA_EINVAL, "lora_debug_project: misaligned debug output");
     const DebugOut dbg{gather_out, order_out};
-    return project_impl(p, "lora_debug_project", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream, &dbg);
+    return project_impl(p, "lora_debug_project", 1, &x, &W, &pt, ids, ranks, scale, T, &y, ws, ws_bytes, stream, &dbg);
 }
 
 // ---- the projection for callers that cannot allocate -------------------------------------------
@@ -344,7 +365,7 @@ extern "C" int lora_project_noalloc(lora_pool *p, const void *x, const void *W, 
         std::lock_guard<std::mutex> lk(g_scratch_mu);
         ws = g_scratch_ptr[p->device];
     }
-    return project_impl(p, "lora_project_noalloc", 1, x, &W, &pt, ids, ranks, scale, T, &y, ws, NOALLOC_SCRATCH_BYTES,
+    return project_impl(p, "lora_project_noalloc", 1, &x, &W, &pt, ids, ranks, scale, T, &y, ws, NOALLOC_SCRATCH_BYTES,
                         stream);
 }
 

@@ -1,6 +1,7 @@
-"""One call for several slots that share the tokens (the q, k and v projections of a layer): the
-outputs must equal, bit for bit, what one lora_project call per slot gives, on each path (decode
-T <= 64, decode 64 < T <= 256, prefill), and match the fp64 oracle."""
+"""One call for several slots that share the tokens (the q, k and v projections of a layer, one x;
+lora_project_slots_x: q, k, v and o, each slot with its own x): the outputs must equal, bit for bit,
+what one lora_project call per slot gives, on each path (decode T <= 64, decode 64 < T <= 256,
+prefill, float32), and match the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -49,6 +50,40 @@ def test_slots_call_equals_one_call_per_slot(T, slots):
         rel, mx = errors(y, oracle_y(w, s, x=x))
         say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
         assert rel <= BF16_REL and mx <= BF16_ABS
+    pool.close()
+
+
+@pytest.mark.parametrize("T,dtype", [(48, "bf16"), (200, "bf16"), (700, "bf16"), (257, "bf16"), (40, "f32")])
+def test_slots_with_own_x_equal_one_call_per_slot(T, dtype):
+    """q, k, v read x, o reads x_o: one lora_project_slots_x call for all four."""
+    rng = np.random.default_rng(T * 7 + 1)
+    ranks = [8, 16, 32, 64, 0, 16]
+    ids = rng.integers(-1, len(ranks), T).astype(np.int32)
+    if T > 256:
+        ids = np.repeat(rng.integers(-1, len(ranks), T // 60 + 1), 60)[:T].astype(np.int32)
+    w = custom(512, ranks, ids, n_slots=4, slot_x=[0, 0, 0, 1], n_x=2, dtype=dtype, device="cuda", seed=1200 + T)
+    say(f"case slots with own x T={T} {dtype}")
+    pool = device_pool(w)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    slots = [0, 1, 2, 3]
+    xs = [w.x_for_slot(s) for s in slots]
+    ys = pool.project_slots(slots, xs, [w.W(s) for s in slots], d_ids, d_ranks, d_scale)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for s, y in zip(slots, ys):
+        y1 = pool.project(s, xs[s], w.W(s), d_ids, d_ranks, d_scale)
+        assert torch.equal(bits(y), bits(y1)), s
+        rel, mx = errors(y, oracle_y(w, s))
+        say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
+        assert rel <= (BF16_REL if dtype == "bf16" else 1e-4) and (dtype != "bf16" or mx <= BF16_ABS)
+    # an output over another slot's input is refused before any device work
+    ws = torch.empty(rg.lora_project_slots_workspace_size(pool.handle, 2, w.T), dtype=torch.uint8, device="cuda")
+    x0, x1 = xs[0].clone(), xs[3].clone()
+    rc = rg.lora_project_slots_x(pool.handle, [0, 3], [x0, x1], [w.W(0), w.W(3)], d_ids, d_ranks, d_scale, w.T,
+                                 [torch.empty_like(x0), x1], ws, check=False)
+    assert rc == rg.LORA_EINVAL and "overlaps" in rg.lora_last_error()
+    assert torch.equal(x1, xs[3])
     pool.close()
 
 

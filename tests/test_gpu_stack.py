@@ -5,12 +5,12 @@ on all 160 slots: about 91.6 GiB of pages), a pool of pages / 0.80 (about 114 Gi
 seeded alloc/free churn with KV pages up to 15 % of it ("S-LoRA, in depth", section "Unified
 paging": adapters and KV share one pool of H-vector pages).  One batch of 8448 rows: 4 prefill
 requests of 2048 rows and 256 decode rows, Zipf(1.2) ids.  One step through the stack is 40 x (the
-layer's q, k and v in one lora_project_slots call, then o in one lora_project call); every slot's
-output is kept.
+layer's q, k, v and o in one lora_project_slots_x call, o reading its own x); every slot's output
+is kept.
 
 Checked against the fp64 oracle: every row of 8 slots spread over the stack; on all 160 slots every
 decode row and 64 seeded rows of each prefill request, with the per-token low-rank delta; the pages
-the kernels read and the grouping they consume, bit for bit, on several slots; q/k/v in one call
+the kernels read and the grouping they consume, bit for bit, on several slots; q/k/v/o in one call
 equal to one call per slot, bit for bit; the fragmentation of the whole pool; KV pages unchanged."""
 import time
 
@@ -69,11 +69,10 @@ def stack():
     # one step through the stack
     d_ids, d_ranks, d_scale = ids_ranks_scale(w)
     ys = [None] * w.n_slots
-    for layer in range(w.n_slots // 4):
-        q = 4 * layer
-        ys[q:q + 3] = pool.project_slots([q, q + 1, q + 2], w.x(0), [w.W(s) for s in (q, q + 1, q + 2)],
-                                         d_ids, d_ranks, d_scale)
-        ys[q + 3] = pool.project(q + 3, w.x(1), w.W(q + 3), d_ids, d_ranks, d_scale)
+    for layer in range(w.n_slots // 4):   # q, k, v (layer input x) and o (x_o) in one call
+        sl = list(range(4 * layer, 4 * layer + 4))
+        ys[sl[0]:sl[0] + 4] = pool.project_slots(sl, [w.x_for_slot(s) for s in sl], [w.W(s) for s in sl],
+                                                 d_ids, d_ranks, d_scale)
     torch.cuda.synchronize()
     assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
     say(f"stack step done at {time.time() - t0:.0f} s")
@@ -178,9 +177,9 @@ def test_stack_sampled_rows_all_slots(stack):
 
 
 @pytest.mark.parametrize("layer", [0, 21, 39])
-def test_stack_qkv_in_one_call_equals_per_slot(stack, layer):
+def test_stack_qkvo_in_one_call_equals_per_slot(stack, layer):
     w, pool, ys, _ = stack
     d_ids, d_ranks, d_scale = ids_ranks_scale(w)
-    for s in range(4 * layer, 4 * layer + 3):
+    for s in range(4 * layer, 4 * layer + 4):
         y1 = pool.project(s, w.x_for_slot(s), w.W(s), d_ids, d_ranks, d_scale)
         assert torch.equal(y1.view(torch.int16), ys[s].view(torch.int16)), s
