@@ -534,12 +534,11 @@ __device__ __forceinline__ void prefill_main_body(
                 // B(li + 1), ids(li + 3)] -- those that were issued
                 const int n = li == 1 ? (nlist > 2) + (nlist > 4)
                                       : (li + 2 < nlist) + (li + 1 < nlist) + (li + 3 < nlist);
-                static_assert(LR_K == 4, "wait counts");
                 // (the debug instantiation's atomics count as memory operations too: it waits for all)
                 if (n == 0 || DBG) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-                else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LR_K) : "memory");
+                else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LR_K) : "memory");
+                else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LR_K) : "memory");
             }
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
