@@ -17,7 +17,9 @@ Prints one JSON line: the throughput, the dominant kernel's roofline fraction (i
 bytes or flops over its average device time, from HIP events recorded on its launch stream) with
 the whole call's fraction beside it (roofline.call), and the fp64 CPU oracle timed on this host as a
 baseline.  The default run also times the prefill batch (MFMA-bound) and the 2000-adapter batch
-(HBM-bound) and adds their lines' figures under "more_workloads".  With --fuse-slots a layer's q, k, v
+(HBM-bound, its q/k/v/o in one call) and adds their lines' figures under "more_workloads".  The
+roofline's "traffic" (HBM bytes per launch from committed rocprofv3 counters) is given for one-slot
+launches taken on the current kernel source, null otherwise.  With --fuse-slots a layer's q, k, v
 and o (each with its own x) are projected by one lora_project_slots_x call; the per-launch figures then
 cover every slot of the launch.  --workload stack13b runs the whole 40-layer stack
 (160 slots, a 115 GiB pool, one replica: a step moves 42 GiB, far beyond the Infinity Cache).
@@ -441,10 +443,12 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "kernel": ("k_decode_stream (W stream + MFMA partials, gathered-A shrink)" if stream_kernel else
-                           "k_decode_wide (x and W through LDS + MFMA partials, shrink work units)"),
+                           "k_decode_wide (x and W through LDS + MFMA partials, shrink work units)")
+                          + (f" ({per_call:g} slots per launch)" if per_call != 1 else ""),
                 "algorithmic_bytes_per_launch": info["decode_first_bytes"] * per_call, "avg_launch_us": first_us,
-                "traffic": (traffic_from_profiles("decode_stream", os.path.join(src, "k_decode.hip")) if stream_kernel
-                            else traffic_from_profiles("decode_wide", os.path.join(src, "k_decode_wide.hip"))),
+                "traffic": None if per_call != 1 else (
+                    traffic_from_profiles("decode_stream", os.path.join(src, "k_decode.hip")) if stream_kernel
+                    else traffic_from_profiles("decode_wide", os.path.join(src, "k_decode_wide.hip"))),
                 "timing": timing,
                 "second_kernel": {"kernel": "k_decode_finish (partials + gathered-B expand + rounding)",
                                   "avg_launch_us": second_us,
@@ -457,9 +461,9 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
         call_tf = info["flops"] / (ms_per_step / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)" + (" (q/k/v in one launch)" if fuse_slots else ""),
+                "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)" + (f" ({per_call:g} slots per launch)" if per_call != 1 else ""),
                 "algorithmic_flops_per_launch": info["prefill_second_flops"] * per_call, "avg_launch_us": second_us,
-                "traffic": traffic_from_profiles("prefill_main", os.path.join(src, "k_prefill.hip")),
+                "traffic": None if per_call != 1 else traffic_from_profiles("prefill_main", os.path.join(src, "k_prefill.hip")),
                 "timing": timing,
                 "call": {"what": "the whole step (every launch of every call), event-free loop",
                          "algorithmic_flops": info["flops"], "us": ms_per_step * 1e3, "achieved": call_tf,
@@ -554,8 +558,9 @@ def main():
     if args.workload == "decode" and not args.no_more:
         # the prefill (MFMA-bound) and many-adapter (HBM-bound) workloads, timed in the same run
         more = {}
-        for name, n_steps in (("prefill", 300), ("many", 300)):
-            w2, r2 = measure(rg, torch, name, n_steps, 30, False, args.profile_calls)
+        # (the many-adapter layer as a user projects it: q, k, v and o in one lora_project_slots_x call)
+        for name, n_steps, fuse in (("prefill", 300, False), ("many", 300, True)):
+            w2, r2 = measure(rg, torch, name, n_steps, 30, fuse, args.profile_calls)
             more[name] = {k: r2[k] for k in ("value", "unit", "ms_per_step", "steps", "config", "step_hbm_frac",
                                              "roofline")}
             w2.drop_cache()
