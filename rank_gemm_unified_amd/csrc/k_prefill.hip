@@ -49,7 +49,7 @@ __device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, cons
     extern __shared__ __align__(16) uint16_t st[];   // SNS stages
     __shared__ int32_t s_perm[SH_ROWS];
     __shared__ int32_t s_pid[DBG ? SH_ROWS : 1];     // debug: the page of each column of v
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int32_t a = rec.x, r = rec.y, row0 = rec.z, n = rec.w;   // 1 <= r, 1 <= n <= 64
     const int split = blockIdx.y;
     const int ktiles = H / SK;
@@ -218,7 +218,8 @@ __device__ __forceinline__ void prefill_main_body(
     int32_t n_tiles_n, uint16_t *__restrict__ y, const DebugOut dbg = DebugOut{}) {
     extern __shared__ __align__(16) uint16_t sm[];
     __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile chunk addresses stay scalar
     const int wm = wave / WGN, wn = wave % WGN;
     // Tile order.  The first P0 = roundup(n_tiles_n, 8) workgroups take the last row of tiles, one
     // tile each, spread over the XCDs: when decode rows (one adapter each) follow the prefill rows,
