@@ -9,13 +9,13 @@
 // so one feeds the MFMA pipe while the other waits for LDS).  Wave w owns rows 16 MBW w + [0, 16 MBW)
 // (its tokens) x all 64 columns of the tile:
 //  * x and W: the split's K range streams through LDS in chunks of 64 (x: [TP rows][64], three
-//    stages; W: the tile's [64 rows][64], five stages, as it comes from HBM), loaded straight from
+//    stages; W: the tile's [64 rows][64], four stages, as it comes from HBM), loaded straight from
 //    global memory into LDS, row-contiguous; each wave reads its own x rows and the chunk's W rows;
 //  * the shrink: work units (adapter segment, 16 of its A pages, 16 of its tokens) dealt round robin,
-//    tiles first, then waves; a unit's operands are its page rows (MFMA operands straight into
-//    registers, DW K steps in flight) and its tokens' x rows, gathered from the LDS chunk by row
-//    index.  So the A pages of the batch are read once per call and x A costs one MFMA per unit and
-//    K step.
+//    tiles first, then waves; a unit's operands are its page rows (loaded row-contiguously into
+//    registers, DW K steps in flight, and put into the MFMA operand layout through the wave's LDS
+//    buffer) and its tokens' x rows, gathered from the LDS chunk by row index.  So the A pages of the
+//    batch are read once per call and x A costs one MFMA per unit and K step.
 // The grouping of tokens by adapter (segments in order of first token, tokens in order within a
 // segment) is worked out by every workgroup from the ids, deterministically, so all agree.
 // Outputs as the T <= 64 kernel: float32 partials of x W (ypart[split]) and of s x A
@@ -30,7 +30,7 @@ namespace wide {
 constexpr int WT = 256;       // most tokens (thread t holds token t during the grouping)
 constexpr int KC = 64;        // K chunk staged in LDS: two MFMA steps of 32
 constexpr int NSTAGE = 3;     // x chunk stages (x chunk c + 2 loads while c computes; x sits in L2)
-constexpr int NWS = 5;        // W chunk stages (W chunk c + 4 loads while c computes; W comes from HBM)
+constexpr int NWS = 4;        // W chunk stages (W chunk c + 3 loads while c computes; W comes from HBM)
 constexpr int DW = 8;         // K steps of page loads in flight per wave
 #ifndef WIDE_UPW
 #define WIDE_UPW 1
@@ -54,6 +54,16 @@ struct WideGroup {
 };
 
 __device__ __forceinline__ int wswz(int r, int p) { return r * KC + ((p ^ ((r >> 1) & 7)) << 3); }
+
+// Unit page rows are loaded row-contiguously, 8 page rows x 128 bytes (one chunk's K) per load, and each
+// wave reorders them into the MFMA operand layout through a 2 KiB LDS buffer of its own (16 rows x 64 K,
+// swizzled as wswz): loads of 16 rows x 64 bytes straight in the operand layout cost the load path about
+// twice as much (1 us per projection at 2000 adapters).  The buffers sit after the W stages, over the
+// grouping's hash arrays (dead once the grouping is done); the group struct moves up by what they do not
+// cover.
+constexpr int UBUF_BYTES = NW * UPW * 2048;
+constexpr int UBUF_OVER = (int)(HSLOTS * 4 + HSLOTS * 4 * 8);   // hkey + hmask: the first fields of WideGroup
+constexpr int GROUP_GAP = UBUF_BYTES > UBUF_OVER ? UBUF_BYTES - UBUF_OVER : 0;
 
 // LDS-only barrier: a full __syncthreads would also wait for every outstanding global load
 __device__ __forceinline__ void lds_sync() {
@@ -94,7 +104,9 @@ __device__ __forceinline__ void decode_wide_body(
     extern __shared__ __align__(16) char lds_raw[];
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds_raw);
     uint16_t *wst = xs + NSTAGE * XSTAGE;
-    WideGroup &g = *reinterpret_cast<WideGroup *>(lds_raw + (size_t)(NSTAGE * XSTAGE + NWS * WSTAGE) * 2);
+    WideGroup &g = *reinterpret_cast<WideGroup *>(lds_raw + (size_t)(NSTAGE * XSTAGE + NWS * WSTAGE) * 2 + GROUP_GAP);
+    static_assert(offsetof(WideGroup, slot_seg) == UBUF_OVER, "the page buffers may cover hkey and hmask only");
+    uint16_t *const ubuf = wst + NWS * WSTAGE;   // the waves' page buffers (used after the grouping)
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lrow = lane & 15, lq = lane >> 4;
     const bool tokt = tid < WT;                // threads 0..255 hold one token each in the grouping
@@ -297,7 +309,7 @@ __device__ __forceinline__ void decode_wide_body(
         // adapters than filling whole workgroups first)
         int32_t u_seg[UPW], u_pb[UPW], u_tc[UPW];
         bool u_live[UPW];
-        const uint16_t *upr[UPW];
+        const uint16_t *urp[UPW][2];   // rows 0..7 and 8..15 of the unit's pages (or stand-ins), this lane's piece
         int32_t u_pid[UPW];
         int u_row[UPW];
         float u_sc[UPW];
@@ -316,14 +328,25 @@ __device__ __forceinline__ void decode_wide_body(
             const int32_t pid = pt[u_live[e] && j < rs ? (int64_t)a * stride + j : 0];
             u_pid[e] = pid;
             const bool pok = u_live[e] && j < rs && pid >= 0 && (int64_t)pid < num_pages;
-            upr[e] = pok ? pages + (int64_t)pid * H + kb + lq * 8 : x + lq * 8;
+            {   // lane l loads page row (l >> 3) + 8 h, 16-byte piece l & 7: the page id comes from lane (that row)
+                const int rr = lane >> 3;
+                const int32_t p0 = __shfl(pid, rr, 64), p1 = __shfl(pid, rr + 8, 64);
+                const int ok0 = __shfl((int)pok, rr, 64), ok1 = __shfl((int)pok, rr + 8, 64);
+                urp[e][0] = ok0 ? pages + (int64_t)p0 * H + kb + (lane & 7) * 8 : x + (lane & 7) * 8;
+                urp[e][1] = ok1 ? pages + (int64_t)p1 * H + kb + (lane & 7) * 8 : x + (lane & 7) * 8;
+            }
             u_sc[e] = scale[u_live[e] ? a : 0];
         }
+        // the page load of K step sn, for ring slot i (sn = i mod DW): rows 8 (sn & 1) + [0, 8) of chunk sn >> 1;
+        // past the range the last step of the same parity, so that the half, i & 1, is known at compile time
+        auto page_load = [&](int e, int i, int sn) {
+            return load16(urp[e][i & 1] + KC * (min(sn, nst - 2 + (i & 1)) >> 1));
+        };
         u32x4_t pv[UPW][DW];
 #pragma unroll
         for (int i = 0; i < DW; ++i)
 #pragma unroll
-            for (int e = 0; e < UPW; ++e) pv[e][i] = load16(upr[e] + 32 * min(i, nst - 1));
+            for (int e = 0; e < UPW; ++e) pv[e][i] = page_load(e, i, i);
         f32x4_t uacc[UPW];
 #pragma unroll
         for (int e = 0; e < UPW; ++e) uacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -354,13 +377,25 @@ __device__ __forceinline__ void decode_wide_body(
             for (int i = 0; i < DW; ++i) {
                 const int st = st0 + i, c = st >> 1, h = i & 1;
                 const bool sl = st < nst;
+                // at a chunk's first step both of its page loads are in (ring slots i and i + 1): the rows go
+                // into the wave's buffer (LDS accesses of one wave are done in order), and each step reads its
+                // operand, pieces 4 h + lq of row lrow, back out
                 u32x4_t pb[UPW];
 #pragma unroll
-                for (int e = 0; e < UPW; ++e) pb[e] = sl && u_live[e] ? pv[e][i] : zero;
-                // the loads of step st + DW refill this slot of the ring
-                const int sn = min(st + DW, nst - 1);
+                for (int e = 0; e < UPW; ++e) {
+                    uint16_t *ub = ubuf + (wave * UPW + e) * (16 * KC);
+                    if (h == 0) {
+                        const int rr = lane >> 3;
+                        *reinterpret_cast<u32x4_t *>(ub + wswz(rr, lane & 7)) = pv[e][i];
+                        *reinterpret_cast<u32x4_t *>(ub + wswz(rr + 8, lane & 7)) = pv[e][i + 1];
+                    }
+                    const u32x4_t op = load16(ub + wswz(lrow, h * 4 + lq));
+                    pb[e] = sl && u_live[e] ? op : zero;
+                }
+                // the loads of step st + DW refill this slot of the ring (slot i + 1, whose rows went into the
+                // buffer at step st, refills at step st + 1)
 #pragma unroll
-                for (int e = 0; e < UPW; ++e) pv[e][i] = load16(upr[e] + 32 * sn);
+                for (int e = 0; e < UPW; ++e) pv[e][i] = page_load(e, i, st + DW);
                 if (h == 1) {   // chunk c's stages are free: refill them
                     dma_w(c + NWS);
                     dma_x(c + NSTAGE);
@@ -514,7 +549,8 @@ __global__ __launch_bounds__(NTH, 1) void k_decode_wide_slots(
                                   (int4 *)sp.sorted_tok[z], sp.spages[z], err_word, nullptr);
 }
 
-size_t decode_wide_lds(int mb16) { return (size_t)(NSTAGE * mb16 * 16 + NWS * 64) * KC * 2 + sizeof(WideGroup); }
+size_t decode_wide_lds(int mb16) { return (size_t)(NSTAGE * mb16 * 16 + NWS * 64) * KC * 2 + GROUP_GAP + sizeof(WideGroup); }
+static_assert((size_t)(NSTAGE * WT + NWS * 64) * KC * 2 + GROUP_GAP + sizeof(WideGroup) <= 160 * 1024, "LDS of the widest case");
 
 template <int MB16>
 static hipError_t launch_wide_t(const lora_pool *p, const Plan &plan, const void *x, const int32_t *ids,
