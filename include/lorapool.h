@@ -74,6 +74,7 @@ enum lora_victim_rule {         /* which idle adapter a load that is short of pa
 
 #define LORA_MAX_RANK 64        /* largest rank a pool can be created for                       */
 #define LORA_MAX_ADAPTERS 8192  /* largest adapter id + 1                                       */
+#define LORA_MAX_TOKENS (1 << 22) /* most tokens (T) one projection call takes                  */
 
 typedef struct lora_pool lora_pool;
 
@@ -238,7 +239,7 @@ size_t lora_project_workspace_size(const lora_pool *pool, int64_t T);
  *   workspace    device, >= lora_project_workspace_size(pool, T) bytes, 256-byte aligned; its
  *                contents on entry do not matter.  Calls that share a workspace must be ordered
  *                (same stream, or events).
- * T == 0 is a no-op.  Ids, ranks and page ids are checked on the device: a token whose adapter id
+ * T == 0 is a no-op; T above LORA_MAX_TOKENS is LORA_EINVAL.  Ids, ranks and page ids are checked on the device: a token whose adapter id
  * is out of range, whose rank is out of range or differs from the page table, or whose page ids
  * are out of range gets the base product only, and the pool's device error word records the
  * fault; lora_check_device_errors() reports and clears it.

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblorapool
 LORA_OK, LORA_EINVAL, LORA_ENOMEM, LORA_ENOENT = 0, -1, -2, -3
 LORA_ERANK, LORA_EBUSY, LORA_EEXIST, LORA_EHIP, LORA_EDEVICE = -4, -5, -6, -7, -8
 LORA_F32, LORA_BF16 = 0, 1
-LORA_MAX_RANK, LORA_MAX_ADAPTERS = 64, 8192
+LORA_MAX_RANK, LORA_MAX_ADAPTERS, LORA_MAX_TOKENS = 64, 8192, 1 << 22
 LORA_VICTIM_LOAD_ORDER, LORA_VICTIM_LRU, LORA_VICTIM_FARTHEST = 0, 1, 2
 LORA_MAX_CALL_SLOTS = 4
 LORA_NOALLOC_SCRATCH_MB = 32

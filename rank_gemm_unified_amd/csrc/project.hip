@@ -15,7 +15,7 @@ using namespace lorapool;
 
 namespace lorapool {
 
-constexpr int64_t MAX_TOKENS = int64_t(1) << 22;
+constexpr int64_t MAX_TOKENS = LORA_MAX_TOKENS;
 constexpr int64_t DECODE_MAX_T = 256;
 
 static size_t up256(size_t v) { return (v + 255) & ~size_t(255); }

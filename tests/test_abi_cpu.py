@@ -42,6 +42,7 @@ def test_version_and_constants():
     text = open(HEADER).read()
     assert f"#define LORA_MAX_RANK {rg.LORA_MAX_RANK}" in text
     assert re.search(rf"#define LORA_MAX_ADAPTERS {rg.LORA_MAX_ADAPTERS}\b", text)
+    assert "#define LORA_MAX_TOKENS (1 << 22)" in text and rg.LORA_MAX_TOKENS == 1 << 22
 
 
 def test_library_built_from_other_sources_is_refused(tmp_path):
@@ -282,6 +283,8 @@ def test_error_codes():
                                               None) == rg.LORA_EINVAL
             assert msg in rg.lora_last_error(), (msg, rg.lora_last_error())
         assert rg.lora_project_slots_workspace_size(pool, 0, 16) == 0
+        assert rg.lora_project_workspace_size(pool, rg.LORA_MAX_TOKENS) > 0
+        assert rg.lora_project_workspace_size(pool, rg.LORA_MAX_TOKENS + 1) == 0
         assert rg.lora_project_slots_workspace_size(pool, rg.LORA_MAX_CALL_SLOTS + 1, 16) == 0
         st = rg.lora_pool_stats(pool)
         assert st["adapter_pages"] == 16 and st["kv_pages"] == 4 and st["free_pages"] == 0
