@@ -18,8 +18,9 @@ bytes or flops over its average device time, from HIP events recorded on its lau
 the whole call's fraction beside it (roofline.call), and the fp64 CPU oracle timed on this host as a
 baseline.  The default run also times the prefill batch (MFMA-bound) and the 2000-adapter batch
 (HBM-bound, its q/k/v/o in one call) and adds their lines' figures under "more_workloads".  The
-roofline's "traffic" (HBM bytes per launch from committed rocprofv3 counters) is given for one-slot
-launches taken on the current kernel source, null otherwise.  With --fuse-slots a layer's q, k, v
+roofline's "traffic" (HBM bytes per launch from committed rocprofv3 counters) is given when the
+counters were taken on the current kernel source, the same workload and the same slots per launch;
+null otherwise.  With --fuse-slots a layer's q, k, v
 and o (each with its own x) are projected by one lora_project_slots_x call; the per-launch figures then
 cover every slot of the launch.  --workload stack13b runs the whole 40-layer stack
 (160 slots, a 115 GiB pool, one replica: a step moves 42 GiB, far beyond the Infinity Cache).
@@ -81,15 +82,15 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key, src_file, launches_bytes_ok=True):
+def traffic_from_profiles(kernel_key, src_file, workload):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were taken on the
-    current kernel source; None otherwise."""
+    current kernel source and on this workload; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256_16") != source_hash(src_file):
+    if d.get("source_sha256_16") != source_hash(src_file) or d.get("workload") != workload:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -446,9 +447,9 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
                            "k_decode_wide (x and W through LDS + MFMA partials, shrink work units)")
                           + (f" ({per_call:g} slots per launch)" if per_call != 1 else ""),
                 "algorithmic_bytes_per_launch": info["decode_first_bytes"] * per_call, "avg_launch_us": first_us,
-                "traffic": None if per_call != 1 else (
-                    traffic_from_profiles("decode_stream", os.path.join(src, "k_decode.hip")) if stream_kernel
-                    else traffic_from_profiles("decode_wide", os.path.join(src, "k_decode_wide.hip"))),
+                "traffic": traffic_from_profiles(
+                    ("decode_stream" if stream_kernel else "decode_wide") + ("" if per_call == 1 else f"_slots{per_call:g}"),
+                    os.path.join(src, "k_decode.hip" if stream_kernel else "k_decode_wide.hip"), w.name),
                 "timing": timing,
                 "second_kernel": {"kernel": "k_decode_finish (partials + gathered-B expand + rounding)",
                                   "avg_launch_us": second_us,
@@ -463,7 +464,8 @@ def measure(rg, torch, name, steps, warmup, fuse_slots, profile_calls, replicas=
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                 "kernel": "k_prefill_main (tiled MFMA GEMM + fused expand)" + (f" ({per_call:g} slots per launch)" if per_call != 1 else ""),
                 "algorithmic_flops_per_launch": info["prefill_second_flops"] * per_call, "avg_launch_us": second_us,
-                "traffic": None if per_call != 1 else traffic_from_profiles("prefill_main", os.path.join(src, "k_prefill.hip")),
+                "traffic": traffic_from_profiles("prefill_main" + ("" if per_call == 1 else f"_slots{per_call:g}"),
+                                                 os.path.join(src, "k_prefill.hip"), w.name),
                 "timing": timing,
                 "call": {"what": "the whole step (every launch of every call), event-free loop",
                          "algorithmic_flops": info["flops"], "us": ms_per_step * 1e3, "achieved": call_tf,
