@@ -22,7 +22,8 @@ roofline's "traffic" (HBM bytes per launch from committed rocprofv3 counters) is
 counters were taken on the current kernel source, the same workload and the same slots per launch;
 null otherwise.  With --fuse-slots a layer's q, k, v
 and o (each with its own x) are projected by one lora_project_slots_x call; the per-launch figures then
-cover every slot of the launch.  --workload stack13b runs the whole 40-layer stack
+cover every slot of the launch.  (The workloads give o its own input; in a model's forward pass o
+follows attention and would be a call of its own.)  --workload stack13b runs the whole 40-layer stack
 (160 slots, a 115 GiB pool, one replica: a step moves 42 GiB, far beyond the Infinity Cache).
 """
 from __future__ import annotations
