@@ -69,6 +69,16 @@ def errors(y_gpu: torch.Tensor, y_ref: np.ndarray):
     return rel, mx
 
 
+def within_one_rounding(y: torch.Tensor, y_other: torch.Tensor, floor: float = 1e-5) -> bool:
+    """Two bfloat16 results of the same sums taken in different float32 orders (another split of K):
+    equal up to one bfloat16 step at the larger magnitude, plus a small absolute floor for the
+    float32 order difference near zero."""
+    a, b = y.float(), y_other.float()
+    m = torch.maximum(a.abs(), b.abs())
+    ulp = torch.where(m > 0, torch.exp2(torch.floor(torch.log2(m)) - 7), torch.zeros_like(m))
+    return bool(((a - b).abs() <= ulp + floor).all())
+
+
 def bf16_round_f64(y: np.ndarray) -> torch.Tensor:
     """Round exactly-representable-in-f32 values to bfloat16 (single rounding)."""
     return torch.as_tensor(y.astype(np.float32)).to(torch.bfloat16)

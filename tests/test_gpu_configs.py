@@ -4,14 +4,15 @@ a 60 %-KV pool of about 1.37 M pages (11 GB: page offsets beyond 4 GiB).
 
 Every gather index the kernels use is compared bit for bit (lora_debug_project); outputs against the
 fp64 oracle on every row, with the per-token low-rank delta; the q, k and v projections made by one
-lora_project_slots call must equal, bit for bit, one lora_project call per slot.  The 13B-shaped
+lora_project_slots call (which splits K into fewer ranges than a one-slot call) must agree with one
+lora_project call per slot up to one bfloat16 rounding step, and two identical calls bit for bit.  The 13B-shaped
 stack is checked at its configured size in test_gpu_stack.py."""
 import numpy as np
 import pytest
 import torch
 
 import rank_gemm_unified_amd as rg
-from gpu_helpers import check_indices, device_pool, errors, ids_ranks_scale, oracle_y, run, say
+from gpu_helpers import check_indices, device_pool, errors, ids_ranks_scale, oracle_y, run, say, within_one_rounding
 from workloads import build, storage_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -84,8 +85,10 @@ def test_many_adapters_qkv_in_one_call(many):
     say("case many: q/k/v in one call")
     d_ids, d_ranks, d_scale = ids_ranks_scale(w)
     ys = pool.project_slots([0, 1, 2], w.x_for_slot(0), [w.W(s) for s in (0, 1, 2)], d_ids, d_ranks, d_scale)
-    for s, y in zip((0, 1, 2), ys):
-        assert torch.equal(y.view(torch.int16), run(pool, w, s).view(torch.int16)), s
+    again = pool.project_slots([0, 1, 2], w.x_for_slot(0), [w.W(s) for s in (0, 1, 2)], d_ids, d_ranks, d_scale)
+    for s, y, y2 in zip((0, 1, 2), ys, again):
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), s
+        assert within_one_rounding(y, run(pool, w, s)), s
     torch.cuda.synchronize()
     assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
     rel, mx = errors(ys[1], oracle_y(w, 1))

@@ -1,13 +1,15 @@
 """One call for several slots that share the tokens (the q, k and v projections of a layer, one x;
 lora_project_slots_x: q, k, v and o, each slot with its own x): the outputs must equal, bit for bit,
-what one lora_project call per slot gives, on each path (decode T <= 64, decode 64 < T <= 256,
-prefill, float32), and match the fp64 oracle."""
+what one lora_project call per slot gives on the decode T <= 64, prefill and float32 paths, and match
+the fp64 oracle.  On the decode path for 64 < T <= 256 a call with several slots may split K into
+fewer ranges than a one-slot call (the slots already fill the chip), so there the outputs must agree
+with one call per slot up to one bfloat16 rounding step, and two identical calls bit for bit."""
 import numpy as np
 import pytest
 import torch
 
 import rank_gemm_unified_amd as rg
-from gpu_helpers import device_pool, errors, ids_ranks_scale, oracle_y, say
+from gpu_helpers import device_pool, errors, ids_ranks_scale, oracle_y, say, within_one_rounding
 from workloads import custom
 
 pytestmark = pytest.mark.gpu
@@ -38,6 +40,7 @@ def test_slots_call_equals_one_call_per_slot(T, slots):
     d_ids, d_ranks, d_scale = ids_ranks_scale(w)
     x = w.x(0)
     ys = pool.project_slots(slots, x, [w.W(s) for s in slots], d_ids, d_ranks, d_scale)
+    again = pool.project_slots(slots, x, [w.W(s) for s in slots], d_ids, d_ranks, d_scale)
     singles = []
     for s in slots:
         y = torch.empty_like(x)
@@ -45,8 +48,13 @@ def test_slots_call_equals_one_call_per_slot(T, slots):
         singles.append(y)
     torch.cuda.synchronize()
     assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
-    for s, y, y1 in zip(slots, ys, singles):
-        assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), s
+    wide = 64 < T <= 256
+    for s, y, y1, y2 in zip(slots, ys, singles, again):
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), s
+        if wide:
+            assert within_one_rounding(y, y1), s
+        else:
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), s
         rel, mx = errors(y, oracle_y(w, s, x=x))
         say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
         assert rel <= BF16_REL and mx <= BF16_ABS
@@ -71,9 +79,15 @@ def test_slots_with_own_x_equal_one_call_per_slot(T, dtype):
     torch.cuda.synchronize()
     assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
     bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
-    for s, y in zip(slots, ys):
+    again = pool.project_slots(slots, xs, [w.W(s) for s in slots], d_ids, d_ranks, d_scale)
+    wide = dtype == "bf16" and 64 < T <= 256
+    for s, y, y2 in zip(slots, ys, again):
         y1 = pool.project(s, xs[s], w.W(s), d_ids, d_ranks, d_scale)
-        assert torch.equal(bits(y), bits(y1)), s
+        assert torch.equal(bits(y), bits(y2)), s
+        if wide:
+            assert within_one_rounding(y, y1), s
+        else:
+            assert torch.equal(bits(y), bits(y1)), s
         rel, mx = errors(y, oracle_y(w, s))
         say(f"  slot {s}: relL2={rel:.3e} maxabs={mx:.3e}")
         assert rel <= (BF16_REL if dtype == "bf16" else 1e-4) and (dtype != "bf16" or mx <= BF16_ABS)
