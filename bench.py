@@ -78,20 +78,26 @@ def algorithmic(w, T_ids, slots):
     }
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    """First 16 hex digits of the SHA-256 of the files' contents, in the given order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel_key, src_file, workload):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were taken on the
-    current kernel source and on this workload; None otherwise."""
+    current kernel source and launch planning (project.hip picks the grid and the K splits) and on
+    this workload; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256_16") != source_hash(src_file) or d.get("workload") != workload:
+    planner = os.path.join(os.path.dirname(src_file), "project.hip")
+    if d.get("source_sha256_16") != source_hash([src_file, planner]) or d.get("workload") != workload:
         return None
     return d.get("hbm_bytes_per_launch")
 
