@@ -306,9 +306,10 @@ int lora_project_slots_x(lora_pool *pool, int32_t n, const int32_t *slots, const
  *                entry that two workgroups or kernels filled with different pages reads -2.
  *   order_out    [T][2], per sorted position q (the grouping the kernels consumed): the token at q
  *                and the adapter of its segment.  T <= 256 (bfloat16): every token, the ones with a
- *                low-rank term first, grouped by adapter in order of first token, then the others
- *                with adapter -1.  Otherwise: positions [0, n) hold the n tokens with a low-rank term,
- *                grouped by adapter in adapter order; the rest stay (-1, -1).
+ *                low-rank term first, grouped by adapter (segments by ceil(r / 16) from 4 down to 1,
+ *                then by first token), then the others with adapter -1.  Otherwise: positions
+ *                [0, n) hold the n tokens with a low-rank term, grouped by adapter in adapter
+ *                order; the rest stay (-1, -1).
  * Other arguments, checks and errors as lora_project.  For tests and debugging; not a fast path.
  */
 int lora_debug_project(lora_pool *pool, const void *x, const void *W, const int32_t *page_table,

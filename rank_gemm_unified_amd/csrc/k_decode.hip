@@ -130,7 +130,7 @@ __device__ __forceinline__ uint64_t same_key_lanes(int32_t key, int lane, GroupT
 //    operand layout) costs the CU's load path about twice what a row-contiguous one does;
 //  * W: 16 x 32 operand tiles, DS steps in flight.  A shallow queue streams W as fast as a deep
 //    one and keeps the latency of the metadata loads queued behind it near one microsecond;
-//  * the shrink: block `tile` of the batch's A-page list (adapters in order of first token, pages
+//  * the shrink: block `tile` of the batch's A-page list (adapters in segment order, pages
 //    0..r-1 each, 16 pages a block) is 16 extra MFMA columns over the same K quarter.  Each wave
 //    works the block out itself (ids -> ranks -> grouping -> page table) at fixed steps of its W
 //    loop, so the dependent loads ride between W steps and no wave waits for another.
@@ -270,10 +270,18 @@ __device__ __forceinline__ void decode_stream_body(
             const uint64_t same = same_key_lanes(key, lane, gtab);
             const int first = key >= 0 ? __ffsll((unsigned long long)same) - 1 : lane;
             const int rank_in = __popcll(same & ((1ull << lane) - 1ull)), cnt = __popcll(same);
-            const uint64_t first_mask = __ballot(key >= 0 && first == lane);
-            nseg = __popcll(first_mask);
-            const int my_seg = key >= 0 ? __popcll(first_mask & ((1ull << first) - 1ull)) : 0;
-            // lane s < nseg describes segment s (segments in order of their first token): the first
+            // segments ordered by the quarter count of their rank, ceil(r / 16), from 4 down to 1, then by
+            // first token: the finishing kernel's groups of 8 sorted tokens then mostly share their live
+            // quarters, and its waves for quarters past every rank of a group skip their loads
+            const int cls = key >= 0 ? (r + 15) >> 4 : 0;   // 1..4 (r <= 64)
+            const bool fl = key >= 0 && first == lane;
+            const uint64_t fm4 = __ballot(fl && cls == 4), fm3 = __ballot(fl && cls == 3), fm2 = __ballot(fl && cls == 2),
+                           fm1 = __ballot(fl && cls == 1);
+            nseg = __popcll(fm4 | fm3 | fm2 | fm1);
+            const uint64_t fmc = cls == 4 ? fm4 : cls == 3 ? fm3 : cls == 2 ? fm2 : fm1;
+            const int above = (cls < 4 ? __popcll(fm4) : 0) + (cls < 3 ? __popcll(fm3) : 0) + (cls < 2 ? __popcll(fm2) : 0);
+            const int my_seg = key >= 0 ? above + __popcll(fmc & ((1ull << first) - 1ull)) : 0;
+            // lane s < nseg describes segment s (segments in the order above): the first
             // lanes write their segment's adapter, rank and token count to the table, lane s reads
             int32_t *segtab = gtab->key;   // the claimed slots are no longer needed
             __builtin_amdgcn_wave_barrier();
@@ -538,13 +546,15 @@ __global__ __launch_bounds__(256, 1) void k_decode_stream_slots(
 }
 
 // ---- finishing kernel: sum partials + expand + round ---------------------------------------------------
-// Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Thread -> (token i of the
-// group, 8 columns c, quarter q of j: j in [16 q, 16 q + 16)).  Two dependent round trips:
+// Grid (H/64 column tiles, ceil(T/8) groups of sorted tokens), 256 threads.  Wave q takes quarter q of
+// j (j in [16 q, 16 q + 16)) for all 8 tokens of the group; lane -> (token i, 8 columns c).  Two
+// dependent round trips:
 //  1. by sorted position only: the token record, this quarter's B page ids, the x W partials of splits
 //     q, q + 4 and the v partials of two j's (both stored by sorted position);
-//  2. the quarter's 16 B-row slices.
-// The four quarter threads of a token then add their x W partials and expand terms by two lane
-// shuffles (a fixed order), and one of them rounds and stores.
+//  2. the quarter's 16 B-row slices -- skipped by a wave whose quarter lies past the rank of every
+//     token of the group (a wave-uniform branch: half the quarters are past the rank at mixed ranks).
+// The four waves' sums (x W partials and expand terms) are then added in LDS in a fixed order,
+// ((q0 + q1) + (q2 + q3)), and wave 0 rounds and stores.
 template <int SY, int SV, bool DBG>
 __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sorted_tok, const int32_t *__restrict__ spages,
                                                    const float *__restrict__ ypart, const float *__restrict__ vpart,
@@ -553,12 +563,14 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
                                                    const DebugOut dbg = DebugOut{}, int32_t stride = 0) {
     constexpr int SQ = (SY + 3) / 4;   // x W splits per quarter thread
     __shared__ float s_v[8][64];
+    __shared__ f32x4_t s_o[4][8][8][2];   // [quarter][token][column group][half]
     const int n0 = blockIdx.x * 64;
-    const int i = threadIdx.x >> 5, c = ((threadIdx.x >> 2) & 7) * 8, q = threadIdx.x & 3;
+    const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int i = lane >> 3, cg = lane & 7, c = cg * 8;
     const int sp = min((int)blockIdx.y * 8 + i, T - 1);
     const bool live_tok = (int)blockIdx.y * 8 + i < T;
-    // ---- round trip 1: the record, the B page ids, and the x W and v partials (stored by sorted position,
-    // so they need nothing from the record)
+    // ---- round trip 1: the records, the B page ids, and the x W and v partials (stored by sorted
+    // position, so they need nothing from the record)
     f32x4_t part[SQ][2];
 #pragma unroll
     for (int k = 0; k < SQ; ++k) {
@@ -566,13 +578,15 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
         part[k][0] = *reinterpret_cast<const f32x4_t *>(src);
         part[k][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
     }
-    const int jj = (threadIdx.x & 31) * 2;   // this thread's two j's of v
+    const int vi = threadIdx.x >> 5, jj = (threadIdx.x & 31) * 2;   // v: token vi of the group, j's jj, jj + 1
+    const int vsp = min((int)blockIdx.y * 8 + vi, T - 1);
     float pv[2 * SV];
     {
-        const float *src = vpart + ((int64_t)sp * RP + min(jj, RP - 2)) * SV;
+        const float *src = vpart + ((int64_t)vsp * RP + min(jj, RP - 2)) * SV;
 #pragma unroll
         for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
     }
+    const int4 vst = sorted_tok[vsp];
     const int4 st = sorted_tok[sp];
     int32_t pid[16];
     {
@@ -594,43 +608,32 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
     const int r = has ? st.z : 0;
     const int j0 = 16 * q;
     const bool qlive = has && j0 < r;
+    const bool wlive = __builtin_amdgcn_readfirstlane((int)(__ballot(qlive) != 0ull)) != 0;
     if constexpr (DBG) {   // the B pages this thread multiplies into the token's output, and the grouping it used
         if (live_tok) {
 #pragma unroll
             for (int u = 0; u < 16; ++u)
                 if (qlive && j0 + u < r) dbg_put(dbg.gather + (int64_t)t * stride + r + j0 + u, pid[u]);
-            if (q == 0 && c == 0) {
+            if (q == 0 && cg == 0) {
                 dbg_put(dbg.order + 2 * sp, t);
                 dbg_put(dbg.order + 2 * sp + 1, a);
             }
         }
     }
-    // ---- round trip 2 (every load unconditional, stand-in addresses for dead entries)
-    u32x4_t bv[16];
-    uint32_t okm = 0;   // rows whose page id is in range
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int32_t pg = qlive && j0 + u < r ? pid[u] : pid[0];
-        const bool pok = pg >= 0 && (int64_t)pg < num_pages;
-        okm |= pok ? 1u << u : 0u;
-        bv[u] = load16(pages + (int64_t)(qlive && pok ? pg : 0) * H + n0 + c);
-    }
     // ---- v[t][j] summed over the splits in order; entries past the rank (never written) are dropped
     {
+        const bool vlive = (int)blockIdx.y * 8 + vi < T && vst.y >= 0;
+        const int vr = vlive ? vst.z : 0;
         float v0 = 0.f, v1 = 0.f;
 #pragma unroll
         for (int u = 0; u < SV; ++u) {
             v0 += pv[u];
             v1 += pv[SV + u];
         }
-        s_v[i][jj] = jj < r ? v0 : 0.f;
-        s_v[i][jj + 1] = jj + 1 < r ? v1 : 0.f;
+        s_v[vi][jj] = jj < vr ? v0 : 0.f;
+        s_v[vi][jj + 1] = jj + 1 < vr ? v1 : 0.f;
     }
-    __syncthreads();
-    // ---- this thread's x W splits + its quarter of the expand.  Rows past the token's rank load a
-    // stand-in row and are zeroed before use: the page they read (page 0, or the token's first B page)
-    // may hold any bits, NaN included, and 0 * NaN is NaN.
-    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+    // ---- this thread's x W splits
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
@@ -644,21 +647,47 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
             }
         }
     }
+    // ---- round trip 2 (live waves; every load unconditional within them, stand-in addresses for dead
+    // entries), then the quarter's expand.  Rows past the token's rank load a stand-in row and are
+    // zeroed before use: the page they read (page 0, or the token's first B page) may hold any bits,
+    // NaN included, and 0 * NaN is NaN.
+    const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+    u32x4_t bv[16];
+    uint32_t okm = 0;   // rows whose page id is in range
+    if (wlive) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const bool lu = qlive && j0 + u < r && ((okm >> u) & 1u);
-        float bf[8];
-        unpack_bf16x8(lu ? bv[u] : zero, bf);
-        const float w = lu ? s_v[i][j0 + u] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(w, bf[e], o[e]);
+        for (int u = 0; u < 16; ++u) {
+            const int32_t pg = qlive && j0 + u < r ? pid[u] : pid[0];
+            const bool pok = pg >= 0 && (int64_t)pg < num_pages;
+            okm |= pok ? 1u << u : 0u;
+            bv[u] = load16(pages + (int64_t)(qlive && pok ? pg : 0) * H + n0 + c);
+        }
     }
+    __syncthreads();   // s_v
+    if (wlive) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        o[e] += __shfl_xor(o[e], 1, 64);
-        o[e] += __shfl_xor(o[e], 2, 64);
+        for (int u = 0; u < 16; ++u) {
+            const bool lu = qlive && j0 + u < r && ((okm >> u) & 1u);
+            float bf[8];
+            unpack_bf16x8(lu ? bv[u] : zero, bf);
+            const float w = lu ? s_v[i][j0 + u] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(w, bf[e], o[e]);
+        }
     }
-    if (q == 0 && live_tok) store16_nt(y + (int64_t)t * H + n0 + c, pack_bf16x8(o));
+    s_o[q][i][cg][0] = f32x4_t{o[0], o[1], o[2], o[3]};
+    s_o[q][i][cg][1] = f32x4_t{o[4], o[5], o[6], o[7]};
+    __syncthreads();
+    if (q == 0 && live_tok) {
+        float f[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4_t sum = (s_o[0][i][cg][h] + s_o[1][i][cg][h]) + (s_o[2][i][cg][h] + s_o[3][i][cg][h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[4 * h + e] = sum[e];
+        }
+        store16_nt(y + (int64_t)t * H + n0 + c, pack_bf16x8(f));
+    }
 }
 
 template <int SY, int SV>

@@ -16,7 +16,8 @@
 //    registers, DW K steps in flight, and put into the MFMA operand layout through the wave's LDS
 //    buffer) and its tokens' x rows, gathered from the LDS chunk by row index.  So the A pages of the
 //    batch are read once per call and x A costs one MFMA per unit and K step.
-// The grouping of tokens by adapter (segments in order of first token, tokens in order within a
+// The grouping of tokens by adapter (segments by the quarter count of their rank, ceil(r / 16), from 4
+// down to 1, then by first token; tokens in order within a
 // segment) is worked out by every workgroup from the ids, deterministically, so all agree.
 // Outputs as the T <= 64 kernel: float32 partials of x W (ypart[split]) and of s x A
 // (vpart[pos][j][split]), rows in sorted-position order; the workgroups that own a segment check its page-table row and publish its
@@ -50,6 +51,7 @@ struct WideGroup {
     int32_t pos[WT];                        // token -> sorted position
     int32_t pub_ent[2 * 64 + 1];           // page-table row of the segment being published
     int32_t wsum[3][NW];
+    int32_t wcls[4][NW];                    // segment-first tokens per rank class and wave
     int32_t pub_bad, nseg, nvalid, nunits;
 };
 
@@ -218,22 +220,33 @@ __device__ __forceinline__ void decode_wide_body(
         }
     }
     const int is_first = key >= 0 && first == tid;
-    // segment ids in order of first token (exclusive scan over the tokens)
+    // segment ids: by the quarter count of the rank, ceil(r / 16), from 4 down to 1, then by first token
+    // (the finishing kernel's groups of 8 sorted tokens then mostly share their live quarters, and its
+    // waves for quarters past every rank of a group skip their loads)
     int nseg;
     {
-        const int incl = wave_incl_scan(is_first, lane);
-        if (lane == 63) g.wsum[0][wave] = incl;
+        const int ord = is_first ? 4 - ((r_tok + 15) >> 4) : 0;   // 0..3 (r <= 64)
+        uint64_t bl[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bl[k] = __ballot(is_first && ord == k);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) g.wcls[k][wave] = __popcll(bl[k]);
+        }
         lds_sync();
         int before = 0;
         nseg = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const int s = g.wsum[0][w];
-            before += w < wave ? s : 0;
-            nseg += s;
-        }
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int s = g.wcls[k][w];
+                before += k < ord || (k == ord && w < wave) ? s : 0;
+                nseg += s;
+            }
+        const uint64_t mine = ord == 0 ? bl[0] : ord == 1 ? bl[1] : ord == 2 ? bl[2] : bl[3];
         if (is_first) {
-            const int sid = before + incl - 1;
+            const int sid = before + __popcll(mine & ((1ull << lane) - 1ull));
             g.slot_seg[slot] = sid;
             g.seg_a[sid] = key;
             g.seg_r[sid] = r_tok;

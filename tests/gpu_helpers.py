@@ -87,8 +87,9 @@ def bf16_round_f64(y: np.ndarray) -> torch.Tensor:
 def check_grouping(order: np.ndarray, ids: np.ndarray, ranks: np.ndarray, decode: bool) -> None:
     """The token grouping the kernels consumed (lora_debug_project's order_out) is valid: its first n
     positions hold exactly the n tokens with a low-rank term, each once and with its own adapter, and
-    each adapter's tokens form one contiguous run.  Decode path: runs in order of first token, then
-    every other token with adapter -1.  Prefill path: runs in adapter order, the rest untouched (-1)."""
+    each adapter's tokens form one contiguous run.  Decode path: runs ordered by the quarter count of
+    the rank, ceil(r / 16), from 4 down to 1, then by first token; then every other token with
+    adapter -1.  Prefill path: runs in adapter order, the rest untouched (-1)."""
     ids = np.asarray(ids)
     live = np.array([a >= 0 and int(ranks[a]) > 0 for a in ids], bool)
     n = int(live.sum())
@@ -102,7 +103,8 @@ def check_grouping(order: np.ndarray, ids: np.ndarray, ranks: np.ndarray, decode
         for t, a in enumerate(ids):
             if live[t]:
                 first.setdefault(int(a), t)
-        assert runs == sorted(first, key=first.get), "segments not in order of first token"
+        assert runs == sorted(first, key=lambda a: (-((int(ranks[a]) + 15) // 16), first[a])), \
+            "segments not ordered by rank quarters, then first token"
         assert np.array_equal(np.sort(toks[n:]), np.nonzero(~live)[0]) and (ads[n:] == -1).all()
     else:
         assert runs == sorted(runs), "segments not in adapter order"
