@@ -586,7 +586,6 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
 #pragma unroll
         for (int u = 0; u < 2 * SV; ++u) pv[u] = src[u];
     }
-    const int4 vst = sorted_tok[vsp];
     const int4 st = sorted_tok[sp];
     int32_t pid[16];
     {
@@ -620,18 +619,17 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
             }
         }
     }
-    // ---- v[t][j] summed over the splits in order; entries past the rank (never written) are dropped
+    // ---- v[t][j] summed over the splits in order (entries past the rank were never written and are
+    // never used: the expand below takes j < r only)
     {
-        const bool vlive = (int)blockIdx.y * 8 + vi < T && vst.y >= 0;
-        const int vr = vlive ? vst.z : 0;
         float v0 = 0.f, v1 = 0.f;
 #pragma unroll
         for (int u = 0; u < SV; ++u) {
             v0 += pv[u];
             v1 += pv[SV + u];
         }
-        s_v[vi][jj] = jj < vr ? v0 : 0.f;
-        s_v[vi][jj + 1] = jj + 1 < vr ? v1 : 0.f;
+        s_v[vi][jj] = v0;
+        s_v[vi][jj + 1] = v1;
     }
     // ---- this thread's x W splits
     float o[8];
