@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check_indices, device_pool, say
+from gpu_helpers import check_indices, device_pool, errors, oracle_y, run, say
 from workloads import build, custom
 
 pytestmark = pytest.mark.gpu
@@ -58,3 +58,22 @@ def test_indices_one_adapter_and_no_adapter():
         check_indices(pool, w, 0)
         check_indices(pool, w, 0, ids=np.full(T, -1, np.int32))
         pool.close()
+
+
+@pytest.mark.parametrize("T", [40, 200])
+def test_indices_ranks_at_quarter_boundaries(T):
+    """Ranks on both sides of every quarter of j (1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64) on the
+    stream (T = 40) and wide (T = 200) decode kernels: the decode grouping orders segments by
+    ceil(r / 16) and the finishing kernel skips quarters past every rank of its group of 8 tokens,
+    so each class boundary must give the right pages, grouping and values."""
+    ranks = [1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64]
+    rng = np.random.default_rng(700 + T)
+    ids = rng.integers(-1, len(ranks), T).astype(np.int32)
+    w = custom(1024, ranks, ids, device="cuda", seed=800 + T)
+    say("case indices, ranks at quarter boundaries, T", T)
+    pool = device_pool(w)
+    info = check_indices(pool, w, 0)
+    rel, mx = errors(run(pool, w, 0), oracle_y(w, 0))
+    say(T, info, f"relL2={rel:.3e} maxabs={mx:.3e}")
+    assert rel <= 1e-2 and mx <= 5e-2
+    pool.close()
