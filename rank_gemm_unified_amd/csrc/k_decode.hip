@@ -574,9 +574,12 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
     f32x4_t part[SQ][2];
 #pragma unroll
     for (int k = 0; k < SQ; ++k) {
-        const float *src = ypart + ((int64_t)min(q + 4 * k, SY - 1) * T + sp) * H + n0 + c;
-        part[k][0] = *reinterpret_cast<const f32x4_t *>(src);
-        part[k][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
+        part[k][0] = part[k][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (q + 4 * k < SY) {   // wave-uniform: with fewer than four splits the other waves load none
+            const float *src = ypart + ((int64_t)(q + 4 * k) * T + sp) * H + n0 + c;
+            part[k][0] = *reinterpret_cast<const f32x4_t *>(src);
+            part[k][1] = *reinterpret_cast<const f32x4_t *>(src + 4);
+        }
     }
     const int vi = threadIdx.x >> 5, jj = (threadIdx.x & 31) * 2;   // v: token vi of the group, j's jj, jj + 1
     const int vsp = min((int)blockIdx.y * 8 + vi, T - 1);
