@@ -561,7 +561,7 @@ __device__ __forceinline__ void decode_finish_body(const int4 *__restrict__ sort
                                                    int32_t RP, const uint16_t *__restrict__ pages, int64_t num_pages,
                                                    int32_t H, int32_t T, uint16_t *__restrict__ y,
                                                    const DebugOut dbg = DebugOut{}, int32_t stride = 0) {
-    constexpr int SQ = (SY + 3) / 4;   // x W splits per quarter thread
+    constexpr int SQ = (SY + 3) / 4;   // x W splits per wave (wave q takes splits q, q + 4)
     __shared__ float s_v[8][64];
     __shared__ f32x4_t s_o[4][8][8][2];   // [quarter][token][column group][half]
     const int n0 = blockIdx.x * 64;

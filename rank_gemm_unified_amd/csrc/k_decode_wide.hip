@@ -17,8 +17,8 @@
 //    buffer) and its tokens' x rows, gathered from the LDS chunk by row index.  So the A pages of the
 //    batch are read once per call and x A costs one MFMA per unit and K step.
 // The grouping of tokens by adapter (segments by the quarter count of their rank, ceil(r / 16), from 4
-// down to 1, then by first token; tokens in order within a
-// segment) is worked out by every workgroup from the ids, deterministically, so all agree.
+// down to 1, then by first token; tokens in order within a segment) is worked out by every
+// workgroup from the ids, deterministically, so all agree.
 // Outputs as the T <= 64 kernel: float32 partials of x W (ypart[split]) and of s x A
 // (vpart[pos][j][split]), rows in sorted-position order; the workgroups that own a segment check its page-table row and publish its
 // sorted-token records and B page ids for the finishing kernel.
