@@ -6,7 +6,8 @@ import torch
 
 import oracle
 import rank_gemm_unified_amd as rg
-from gpu_helpers import bf16_round_f64, check_indices, device_pool, errors, ids_ranks_scale, oracle_y, run, say
+from gpu_helpers import (bf16_round_f64, check_indices, device_pool, errors, ids_ranks_scale, oracle_y, run, say,
+                         within_one_rounding)
 from workloads import build, custom, storage_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -302,3 +303,32 @@ def test_host_validation_touches_nothing():
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
     assert rg.lora_project(pool.handle, w.x(), w.W(0), pool.table[0], d_ids, d_ranks, d_scale, 0, y, ws) == 0
+
+
+# (H, T) on the T > 64 kernel: one column tile (64), ragged quarters (192), a split count that is not
+# a divisor of 8 (5120: three splits, uneven K ranges), two splits (8192) and the smallest T (65);
+# each also as one call for three slots (fewer K splits per slot)
+@pytest.mark.parametrize("H,T", [(64, 100), (192, 130), (3072, 65), (5120, 200), (8192, 256)])
+def test_decode_wide_hidden_sizes(H, T):
+    rng = np.random.default_rng(H + T)
+    ranks = [8, 16, 64, 0, 32, 1, 48]
+    ids = rng.integers(-1, len(ranks), T)
+    w = custom(H, ranks, ids, n_slots=3, device="cuda", seed=H + T)
+    say("case wide hidden", H, "T", T)
+    pool = device_pool(w)
+    d_ids, d_ranks, d_scale = ids_ranks_scale(w)
+    x = w.x(0)
+    ys = pool.project_slots([0, 1, 2], x, [w.W(s) for s in range(3)], d_ids, d_ranks, d_scale)
+    again = pool.project_slots([0, 1, 2], x, [w.W(s) for s in range(3)], d_ids, d_ranks, d_scale)
+    for s in range(3):
+        y1 = pool.project(s, x, w.W(s), d_ids, d_ranks, d_scale)
+        torch.cuda.synchronize()
+        assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+        ref = oracle_y(w, s, x=x)
+        for y in (y1, ys[s]):
+            rel, mx = errors(y, ref)
+            assert rel <= BF16_REL and mx <= BF16_ABS, (s, rel, mx)
+        assert torch.equal(ys[s].view(torch.int16), again[s].view(torch.int16)), s
+        assert within_one_rounding(ys[s], y1), s
+    say(f"H={H} T={T}: 3 slots, one call and one call per slot")
+    pool.close()
