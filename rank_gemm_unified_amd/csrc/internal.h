@@ -99,19 +99,18 @@ struct Plan {
     int32_t ysplit;         // K-splits of the decode base GEMM
     int32_t n_tiles;        // decode: 64-column tiles
     int32_t mb;             // decode: 16-row blocks per wave
-    int32_t n_counters;     // arrival counters the grouping kernel zeroes
     int32_t rp;             // row stride of v and per-token page lists (max_rank rounded up to 16)
     int32_t stream;         // decode: 1 = k_decode_stream (T <= 64), 0 = k_decode_wide
     int32_t ks;             // decode streaming kernel: max K steps of 32 per wave (a quarter of a split)
     // byte offsets into the workspace
     size_t off_tok_a, off_tok_r, off_perm, off_seg_a, off_seg_start, off_item_seg, off_item_row, off_item_rec,
-        off_ctrl, off_counters, off_v, off_ypart, off_sorted_tok, off_v16, off_spages, total;
+        off_ctrl, off_v, off_ypart, off_sorted_tok, off_v16, off_spages, total;
 };
 
 bool make_plan(const lora_pool *p, int64_t T, Plan *plan);
 
 struct Ws {
-    int32_t *tok_a, *tok_r, *perm, *seg_a, *seg_start, *item_seg, *item_row, *ctrl, *counters;
+    int32_t *tok_a, *tok_r, *perm, *seg_a, *seg_start, *item_seg, *item_row, *ctrl;
     int4 *item_rec;         // prefill: per shrink work item {adapter, rank, first sorted row, rows}; adapter -1 past the last
     float *v, *ypart;
     int32_t *sorted_tok;    // decode: int4 {token, adapter or -1, rank, 0} per sorted position

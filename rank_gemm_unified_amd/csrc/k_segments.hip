@@ -114,8 +114,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     int32_t *__restrict__ tok_a, int32_t *__restrict__ tok_r, int32_t *__restrict__ perm,
     int32_t *__restrict__ seg_a, int32_t *__restrict__ seg_start, int32_t *__restrict__ item_seg,
     int32_t *__restrict__ item_row, int4 *__restrict__ item_rec, int32_t n_items_max,
-    int32_t *__restrict__ ctrl, int32_t *__restrict__ counters,
-    int32_t n_counters, int *__restrict__ err) {
+    int32_t *__restrict__ ctrl, int *__restrict__ err) {
     extern __shared__ int32_t lds[];
     int32_t *cnt = lds, *uidx = lds + max_adapters, *ulist = lds + 2 * max_adapters, *rk = lds + 3 * max_adapters;
     int32_t *scratch = lds + 4 * max_adapters;
@@ -124,7 +123,6 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     const bool cached = T <= KPT * SEG_THREADS;
     int my_err = 0;
     if (tid == 0) s_err = 0;
-    for (int i = tid; i < n_counters; i += SEG_THREADS) counters[i] = 0;
     for (int a = tid; a < max_adapters; a += SEG_THREADS) cnt[a] = 0;
     __syncthreads();
 
@@ -313,8 +311,7 @@ hipError_t launch_segments(const lora_pool *p, const Plan &plan, const Ws &ws, c
     hipLaunchKernelGGL(k_segments, dim3(1), dim3(SEG_THREADS), lds, s, ids, ranks, rows, n, 2 * p->max_rank,
                        (int32_t)plan.T, p->max_adapters, p->max_rank, p->num_pages, plan.chunk, ws.tok_a, ws.tok_r,
                        ws.perm, ws.seg_a, ws.seg_start, ws.item_seg, ws.item_row, ws.item_rec, plan.n_items_max,
-                       ws.ctrl, ws.counters,
-                       plan.n_counters, p->dev_err);
+                       ws.ctrl, p->dev_err);
     return hipGetLastError();
 }
 

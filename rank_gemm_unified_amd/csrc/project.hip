@@ -64,7 +64,6 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
         pl->vsplit = 4;
         pl->n_tiles = 0;
     }
-    pl->n_counters = 0;   // no kernel uses arrival counters (cross-workgroup sums go through kernel boundaries)
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
     pl->off_tok_a = take(T * 4);
@@ -76,7 +75,6 @@ bool make_plan(const lora_pool *p, int64_t T, Plan *pl) {
     pl->off_item_row = take((size_t)pl->n_items_max * 4);
     pl->off_item_rec = take((size_t)pl->n_items_max * 16);
     pl->off_ctrl = take(CTRL_WORDS * 4);
-    pl->off_counters = take((size_t)std::max(pl->n_counters, 1) * 4);
     const int64_t sv = pl->path == PATH_DECODE ? pl->ysplit : 1;
     pl->off_v = take(pl->path == PATH_F32 ? (size_t)T * R * 4 : (size_t)pl->vsplit * T * pl->rp * sv * 4);
     pl->off_ypart = take(pl->path == PATH_DECODE ? (size_t)pl->ysplit * T * H * 4 : 0);
@@ -99,7 +97,6 @@ Ws carve(void *base, const Plan &pl) {
     w.item_row = (int32_t *)(b + pl.off_item_row);
     w.item_rec = (int4 *)(b + pl.off_item_rec);
     w.ctrl = (int32_t *)(b + pl.off_ctrl);
-    w.counters = (int32_t *)(b + pl.off_counters);
     w.v = (float *)(b + pl.off_v);
     w.ypart = (float *)(b + pl.off_ypart);
     w.sorted_tok = (int32_t *)(b + pl.off_sorted_tok);
