@@ -101,7 +101,6 @@ __device__ __forceinline__ void decode_wide_body(
     constexpr int WSTAGE = 64 * KC;         // elements per W stage
     constexpr int DX = TP / 64;             // x chunk loads per wave (1 KiB each)
     constexpr int DWL = 64 / 64;            // W chunk loads per wave
-    constexpr int LPS = UPW;                // page loads per K step per wave
     static_assert(MB16 % NW == 0, "rows per wave");
     extern __shared__ __align__(16) char lds_raw[];
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds_raw);
@@ -355,117 +354,131 @@ __device__ __forceinline__ void decode_wide_body(
         auto page_load = [&](int e, int i, int sn) {
             return load16(urp[e][i & 1] + KC * (min(sn, nst - 2 + (i & 1)) >> 1));
         };
-        u32x4_t pv[UPW][DW];
-#pragma unroll
-        for (int i = 0; i < DW; ++i)
-#pragma unroll
-            for (int e = 0; e < UPW; ++e) pv[e][i] = page_load(e, i, i);
-        f32x4_t uacc[UPW];
-#pragma unroll
-        for (int e = 0; e < UPW; ++e) uacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // the first chunks have landed (the DW UPW page loads just issued are the only younger ones)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DW * UPW) : "memory");
-        lds_sync();
+        // A wave whose units are all past the last (with one unit per wave, about half the waves at 256
+        // tokens of 137 adapters and 4096 columns) runs the K loop without page loads, buffer work and
+        // unit MFMAs: stand-in loads cost the CU's load path as much as real ones.
+        const bool any_live = __builtin_amdgcn_readfirstlane((int)u_live[0]) != 0;   // units grow with e
+        auto kloop = [&](auto live_c) {
+            constexpr bool LIVE = decltype(live_c)::value;
+            constexpr int NU = LIVE ? UPW : 0;   // units whose operands this wave loads and multiplies
+            u32x4_t pv[UPW][DW];
+            if constexpr (LIVE) {
+    #pragma unroll
+                for (int i = 0; i < DW; ++i)
+    #pragma unroll
+                    for (int e = 0; e < UPW; ++e) pv[e][i] = page_load(e, i, i);
+            }
+            f32x4_t uacc[UPW];
+    #pragma unroll
+            for (int e = 0; e < UPW; ++e) uacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // the first chunks have landed (the DW UPW page loads just issued are the only younger ones)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DW * NU) : "memory");
+            lds_sync();
 
-        // ---- K loop, in chunks of two steps of 32.  A chunk's one barrier sits between its steps: before
-        // it each wave has read both halves of its operands from the chunk's stages and waited for its
-        // loads of chunk c + 1; after it the stages of chunk c are free, so they refill with chunks
-        // c + NSTAGE (x) and c + NWS (W) while the second step's MFMAs run and the next chunk's first
-        // operands are read -- no MFMA waits for LDS at a chunk boundary.  DW steps per round (the
-        // ring of page loads in flight is indexed statically).
-        u32x4_t wf[2][4], xf[2][MBW], uf[2][UPW];
-        auto frags = [&](int c, int half, u32x4_t *wfo, u32x4_t *xfo, u32x4_t *ufo) {
-            const uint16_t *stg = xs + (c % NSTAGE) * XSTAGE, *wsg = wst + (c % NWS) * WSTAGE;
-            const int pc = half * 4 + lq;           // 16-byte piece of the row for this lane
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) wfo[nb] = load16(wsg + wswz(16 * nb + lrow, pc));
-#pragma unroll
-            for (int m = 0; m < MBW; ++m) xfo[m] = load16(stg + wswz((wave * MBW + m) * 16 + lrow, pc));
-#pragma unroll
-            for (int e = 0; e < UPW; ++e) ufo[e] = load16(stg + wswz(u_row[e], pc));
-        };
-        frags(0, 0, wf[0], xf[0], uf[0]);
-        for (int st0 = 0; st0 < nst; st0 += DW) {
-#pragma unroll
-            for (int i = 0; i < DW; ++i) {
-                const int st = st0 + i, c = st >> 1, h = i & 1;
-                const bool sl = st < nst;
-                // at a chunk's first step both of its page loads are in (ring slots i and i + 1): the rows go
-                // into the wave's buffer (LDS accesses of one wave are done in order), and each step reads its
-                // operand, pieces 4 h + lq of row lrow, back out
-                u32x4_t pb[UPW];
-#pragma unroll
-                for (int e = 0; e < UPW; ++e) {
-                    uint16_t *ub = ubuf + (wave * UPW + e) * (16 * KC);
-                    if (h == 0) {
-                        const int rr = lane >> 3;
-                        *reinterpret_cast<u32x4_t *>(ub + wswz(rr, lane & 7)) = pv[e][i];
-                        *reinterpret_cast<u32x4_t *>(ub + wswz(rr + 8, lane & 7)) = pv[e][i + 1];
+            // ---- K loop, in chunks of two steps of 32.  A chunk's one barrier sits between its steps: before
+            // it each wave has read both halves of its operands from the chunk's stages and waited for its
+            // loads of chunk c + 1; after it the stages of chunk c are free, so they refill with chunks
+            // c + NSTAGE (x) and c + NWS (W) while the second step's MFMAs run and the next chunk's first
+            // operands are read -- no MFMA waits for LDS at a chunk boundary.  DW steps per round (the
+            // ring of page loads in flight is indexed statically).
+            u32x4_t wf[2][4], xf[2][MBW], uf[2][UPW];
+            auto frags = [&](int c, int half, u32x4_t *wfo, u32x4_t *xfo, u32x4_t *ufo) {
+                const uint16_t *stg = xs + (c % NSTAGE) * XSTAGE, *wsg = wst + (c % NWS) * WSTAGE;
+                const int pc = half * 4 + lq;           // 16-byte piece of the row for this lane
+    #pragma unroll
+                for (int nb = 0; nb < 4; ++nb) wfo[nb] = load16(wsg + wswz(16 * nb + lrow, pc));
+    #pragma unroll
+                for (int m = 0; m < MBW; ++m) xfo[m] = load16(stg + wswz((wave * MBW + m) * 16 + lrow, pc));
+                if constexpr (LIVE) {
+    #pragma unroll
+                    for (int e = 0; e < UPW; ++e) ufo[e] = load16(stg + wswz(u_row[e], pc));
+                }
+            };
+            frags(0, 0, wf[0], xf[0], uf[0]);
+            for (int st0 = 0; st0 < nst; st0 += DW) {
+    #pragma unroll
+                for (int i = 0; i < DW; ++i) {
+                    const int st = st0 + i, c = st >> 1, h = i & 1;
+                    const bool sl = st < nst;
+                    // at a chunk's first step both of its page loads are in (ring slots i and i + 1): the rows go
+                    // into the wave's buffer (LDS accesses of one wave are done in order), and each step reads its
+                    // operand, pieces 4 h + lq of row lrow, back out
+                    u32x4_t pb[UPW];
+    #pragma unroll
+                    for (int e = 0; e < NU; ++e) {
+                        uint16_t *ub = ubuf + (wave * UPW + e) * (16 * KC);
+                        if (h == 0) {
+                            const int rr = lane >> 3;
+                            *reinterpret_cast<u32x4_t *>(ub + wswz(rr, lane & 7)) = pv[e][i];
+                            *reinterpret_cast<u32x4_t *>(ub + wswz(rr + 8, lane & 7)) = pv[e][i + 1];
+                        }
+                        const u32x4_t op = load16(ub + wswz(lrow, h * 4 + lq));
+                        pb[e] = sl && u_live[e] ? op : zero;
                     }
-                    const u32x4_t op = load16(ub + wswz(lrow, h * 4 + lq));
-                    pb[e] = sl && u_live[e] ? op : zero;
-                }
-                // the loads of step st + DW refill this slot of the ring (slot i + 1, whose rows went into the
-                // buffer at step st, refills at step st + 1)
-#pragma unroll
-                for (int e = 0; e < UPW; ++e) pv[e][i] = page_load(e, i, st + DW);
-                if (h == 1) {   // chunk c's stages are free: refill them
-                    dma_w(c + NWS);
-                    dma_x(c + NSTAGE);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (h == 0) frags(c, 1, wf[1], xf[1], uf[1]);
-                else frags(c + 1, 0, wf[0], xf[0], uf[0]);
-                const bool wl = sl && with_w;   // steps past the range and unit-only passes add nothing to x W
-#pragma unroll
-                for (int m = 0; m < MBW; ++m)
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xf[h][m]), __builtin_bit_cast(bf16x8_t, wl ? wf[h][nb] : zero),
-                            acc[m][nb], 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < UPW; ++e)
-                    uacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, uf[h][e]),
-                                                                      __builtin_bit_cast(bf16x8_t, pb[e]), uacc[e], 0, 0, 0);
-#pragma unroll
-                for (int g2 = 0; g2 < MBW * 4 + UPW; ++g2) {   // one operand read after each MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (g2 < 4 + MBW + UPW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                if (h == 0) {
-                    // mid-chunk: this wave's loads of x chunk c + 1 (and of the older W chunk c + 1) have
-                    // landed.  x chunk c + 1 went out last in chunk c + 1 - NSTAGE; younger are, for
-                    // each chunk between, its two steps of page loads and its W and x loads, and this
-                    // chunk's first step of page loads
+                    // the loads of step st + DW refill this slot of the ring (slot i + 1, whose rows went into the
+                    // buffer at step st, refills at step st + 1)
+    #pragma unroll
+                    for (int e = 0; e < NU; ++e) pv[e][i] = page_load(e, i, st + DW);
+                    if (h == 1) {   // chunk c's stages are free: refill them
+                        dma_w(c + NWS);
+                        dma_x(c + NSTAGE);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * (2 * LPS + DWL + DX) + LPS) : "memory");
-                    lds_sync();
+                    if (h == 0) frags(c, 1, wf[1], xf[1], uf[1]);
+                    else frags(c + 1, 0, wf[0], xf[0], uf[0]);
+                    const bool wl = sl && with_w;   // steps past the range and unit-only passes add nothing to x W
+    #pragma unroll
+                    for (int m = 0; m < MBW; ++m)
+    #pragma unroll
+                        for (int nb = 0; nb < 4; ++nb)
+                            acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, xf[h][m]), __builtin_bit_cast(bf16x8_t, wl ? wf[h][nb] : zero),
+                                acc[m][nb], 0, 0, 0);
+    #pragma unroll
+                    for (int e = 0; e < NU; ++e)
+                        uacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, uf[h][e]),
+                                                                          __builtin_bit_cast(bf16x8_t, pb[e]), uacc[e], 0, 0, 0);
+    #pragma unroll
+                    for (int g2 = 0; g2 < MBW * 4 + NU; ++g2) {   // one operand read after each MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (g2 < 4 + MBW + NU) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    if (h == 0) {
+                        // mid-chunk: this wave's loads of x chunk c + 1 (and of the older W chunk c + 1) have
+                        // landed.  x chunk c + 1 went out last in chunk c + 1 - NSTAGE; younger are, for
+                        // each chunk between, its two steps of page loads and its W and x loads, and this
+                        // chunk's first step of page loads
+                        __builtin_amdgcn_sched_barrier(0);
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * (2 * NU + DWL + DX) + NU) : "memory");
+                        lds_sync();
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads past the end have landed
-        lds_sync();
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads past the end have landed
+            lds_sync();
 
-        // ---- units: s v partials of this split (tokens and pages past the segment are dropped; a
-        // segment whose page-table row is bad is dropped by the finishing kernel)
-#pragma unroll
-        for (int e = 0; e < UPW; ++e) {
-            if (!u_live[e]) continue;
-            const int s = u_seg[e];
-            const int32_t rs = g.seg_r[s], ns = g.seg_n[s], to = g.seg_toff[s];
-            const int j = u_pb[e] * 16 + lrow;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int it = u_tc[e] * 16 + 4 * lq + i;
-                if (j < rs && it < ns) {
-                    const int t = g.sorted[to + it];
-                    vpart[((int64_t)(to + it) * RP + j) * S + split] = u_sc[e] * uacc[e][i];   // by sorted position
-                    if constexpr (DBG) dbg_put(dbg_gather + (int64_t)t * stride + j, u_pid[e]);
+            // ---- units: s v partials of this split (tokens and pages past the segment are dropped; a
+            // segment whose page-table row is bad is dropped by the finishing kernel)
+    #pragma unroll
+            for (int e = 0; e < NU; ++e) {
+                if (!u_live[e]) continue;
+                const int s = u_seg[e];
+                const int32_t rs = g.seg_r[s], ns = g.seg_n[s], to = g.seg_toff[s];
+                const int j = u_pb[e] * 16 + lrow;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int it = u_tc[e] * 16 + 4 * lq + i;
+                    if (j < rs && it < ns) {
+                        const int t = g.sorted[to + it];
+                        vpart[((int64_t)(to + it) * RP + j) * S + split] = u_sc[e] * uacc[e][i];   // by sorted position
+                        if constexpr (DBG) dbg_put(dbg_gather + (int64_t)t * stride + j, u_pid[e]);
+                    }
                 }
             }
-        }
+        };
+        if (any_live) kloop(std::true_type{});
+        else kloop(std::false_type{});
     }
 
     // ---- x W partial of this split: lane holds column 16 nb + lrow, rows 16 (wave MBW + m) + 4 lq + i; each
