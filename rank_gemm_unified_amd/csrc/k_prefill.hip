@@ -215,13 +215,14 @@ __device__ __forceinline__ void prefill_main_body(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ pages,
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
-    int32_t n_tiles_n, uint16_t *__restrict__ y, const DebugOut dbg = DebugOut{}) {
+    int32_t n_tiles_n, uint16_t *__restrict__ y, int blk, int nblk, const DebugOut dbg = DebugOut{}) {
     extern __shared__ __align__(16) uint16_t sm[];
     __shared__ int32_t s_key[BM], s_list[BM], s_lr[BM], s_wsum[PF_THREADS / 64], s_nlist;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile chunk addresses stay scalar
     const int wm = wave / WGN, wn = wave % WGN;
-    // Tile order.  The first P0 = roundup(n_tiles_n, 8) workgroups take the last row of tiles, one
+    // Tile order (workgroup blk of the nblk of this output).  The first P0 = roundup(n_tiles_n, 8)
+    // workgroups take the last row of tiles, one
     // tile each, spread over the XCDs: when decode rows (one adapter each) follow the prefill rows,
     // that row holds most of the batch's distinct adapters and the longest low-rank term, so it
     // starts first (the rest of the grid then runs beside it).  The others go to the 8 XCDs in turn
@@ -231,13 +232,13 @@ __device__ __forceinline__ void prefill_main_body(
     int mt, nt;
     {
         const int tm = (T + BM - 1) / BM, P0 = (n_tiles_n + 7) / 8 * 8;
-        const int b = blockIdx.x;
+        const int b = blk;
         if (b < P0) {
             if (b >= n_tiles_n) return;
             mt = tm - 1;
             nt = b;
         } else {
-            const int rest = (tm - 1) * n_tiles_n, G = gridDim.x - P0, b2 = b - P0;   // G: multiple of 8
+            const int rest = (tm - 1) * n_tiles_n, G = nblk - P0, b2 = b - P0;   // G: multiple of 8
             const int t = (b2 & 7) * (G >> 3) + (b2 >> 3);
             if (t >= rest) return;
             constexpr int GM = 4;
@@ -397,11 +398,23 @@ __device__ __forceinline__ void prefill_main_body(
     for (int mi = 0; mi < WMI; ++mi) rkey[mi] = s_key[wm * WTM + mi * 32 + frow];
     auto lr_mfma = [&](const uint16_t *Bn, const uint16_t *Vs, int li) {
         const int32_t a = s_list[li], r = s_lr[li], rp = (r + 15) & ~15;
+        // a 32-row block of this wave with none of the adapter's rows would add only zeros: its v reads
+        // and MFMAs are skipped, and the whole term when no block has one (decode rows: one adapter
+        // for every few rows)
+        bool blk_live[WMI];
+        bool any = false;
+#pragma unroll
+        for (int mi = 0; mi < WMI; ++mi) {
+            blk_live[mi] = __builtin_amdgcn_readfirstlane((int)(__ballot(rkey[mi] == a) != 0ull)) != 0;
+            any = any || blk_live[mi];
+        }
+        if (!any) return;
         for (int ks = 0; ks < rp / 16; ++ks) {
             u32x4_t la[WMI], lb[WNI];
             const int jb = ks * 16 + fk;   // this lane's first j
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi) {
+                if (!blk_live[mi]) continue;
                 u32x4_t v = load16(Vs + swz(wm * WTM + mi * 32 + frow, ks * 2 + (fk >> 3)));
                 const int nv = rkey[mi] == a ? min(max(r - jb, 0), 8) : 0;   // entries kept
 #pragma unroll
@@ -419,12 +432,14 @@ __device__ __forceinline__ void prefill_main_body(
                 }
             }
 #pragma unroll
-            for (int mi = 0; mi < WMI; ++mi)
+            for (int mi = 0; mi < WMI; ++mi) {
+                if (!blk_live[mi]) continue;
 #pragma unroll
                 for (int ni = 0; ni < WNI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, la[mi]),
                                                                           __builtin_bit_cast(bf16x8_t, lb[ni]),
                                                                           acc[mi][ni], 0, 0, 0);
+            }
         }
     };
     // B rows of an adapter straight into a buffer of [64][BN] (LR_K loads per thread, rows past the rank
@@ -585,7 +600,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main(
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
     int32_t n_tiles_n, uint16_t *__restrict__ y) {
-    prefill_main_body<false>(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y);
+    prefill_main_body<false>(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_dbg(
@@ -593,16 +608,30 @@ __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_dbg(
     const int32_t *__restrict__ pt, int32_t stride, const int32_t *__restrict__ tok_a,
     const int32_t *__restrict__ tok_r, const uint16_t *__restrict__ v16, int32_t R, int32_t T, int32_t H,
     int32_t n_tiles_n, uint16_t *__restrict__ y, const DebugOut dbg) {
-    prefill_main_body<true>(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y, dbg);
+    prefill_main_body<true>(x, W, pages, pt, stride, tok_a, tok_r, v16, R, T, H, n_tiles_n, y, blockIdx.x, gridDim.x,
+                            dbg);
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void k_prefill_main_slots(
     const SlotPtrs sp, const uint16_t *__restrict__ pages, int32_t stride,
     const int32_t *__restrict__ tok_a, const int32_t *__restrict__ tok_r, int32_t R, int32_t T, int32_t H,
-    int32_t n_tiles_n) {
-    const int z = blockIdx.z;
+    int32_t n_tiles_n, int32_t n) {
+    // One grid of n x nblk workgroups: first the last row of tiles of every slot (P0 each, slot after
+    // slot), then the other tiles, slot after slot.  So every slot's longest tiles (the decode rows'
+    // adapters) start at the beginning, not only the first slot's; both parts are multiples of 8, so
+    // each workgroup keeps the XCD the one-slot order gives it.
+    const int P0 = (n_tiles_n + 7) / 8 * 8, nblk = (int)gridDim.x / n, b = blockIdx.x;
+    int z, blk;
+    if (b < n * P0) {
+        z = b / P0;
+        blk = b % P0;
+    } else {
+        const int b2 = b - n * P0, G = nblk - P0;   // G > 0 here: b < n nblk
+        z = b2 / G;
+        blk = P0 + b2 % G;
+    }
     prefill_main_body<false>((const uint16_t *)sp.x[z], (const uint16_t *)sp.W[z], pages, sp.pt[z], stride, tok_a, tok_r,
-                             (const uint16_t *)sp.v16[z], R, T, H, n_tiles_n, (uint16_t *)sp.y[z]);
+                             (const uint16_t *)sp.v16[z], R, T, H, n_tiles_n, (uint16_t *)sp.y[z], blk, nblk);
 }
 
 hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, const void *x, const float *scale,
@@ -676,8 +705,8 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
                            pages, sp.pt[0], stride, ws.tok_a, ws.tok_r, (const uint16_t *)sp.v16[0], plan.rp, T,
                            p->hidden, tn, (uint16_t *)sp.y[0]);
     else
-        hipLaunchKernelGGL(k_prefill_main_slots, dim3(grid, 1, n), dim3(PF_THREADS), MAIN_LDS, s, sp, pages,
-                           stride, ws.tok_a, ws.tok_r, plan.rp, T, p->hidden, tn);
+        hipLaunchKernelGGL(k_prefill_main_slots, dim3(grid * n), dim3(PF_THREADS), MAIN_LDS, s, sp, pages,
+                           stride, ws.tok_a, ws.tok_r, plan.rp, T, p->hidden, tn, n);
     return hipGetLastError();
 }
 
