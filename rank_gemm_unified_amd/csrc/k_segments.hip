@@ -107,6 +107,7 @@ __device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int
 // LDS: cnt | uidx | ulist | rk (max_adapters each) | scratch[3 * 17].
 constexpr int KPT = 16;   // tokens per thread held in registers (T <= 16384 reads the ids once)
 constexpr int32_t F_OFF = 1 << 30;   // cnt flag: the adapter's tokens get no low-rank term
+constexpr int EPT = 4;               // page-table entries per thread and round trip (every slot's at once)
 
 __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, const SlotRows sp, int32_t n_slots_call,
@@ -162,34 +163,49 @@ __global__ __launch_bounds__(SEG_THREADS) void k_segments(
     // slot of the call (the later kernels read these rows unchecked; one bad row turns the adapter
     // off in all of them)
     const int32_t nent = nused * stride;
-    for (int z = 0; z < n_slots_call; ++z)   // uniform: one slot's rows at a time
-    for (int e0 = tid; e0 < nent; e0 += 8 * SEG_THREADS) {
-        const int32_t *pz = z == 0 ? sp.pt[0] : z == 1 ? sp.pt[1] : z == 2 ? sp.pt[2] : sp.pt[3];
-        int32_t av[8], jv[8], rv[8], ev[8];
+    for (int e0 = tid; e0 < nent; e0 += EPT * SEG_THREADS) {
+        // the entry's adapter, index and rank are the same in every slot; the entries of all the slots
+        // go out together (one round trip, not one per slot), EPT per thread so that they fit the
+        // registers of a 1024-thread workgroup
+        int32_t av[EPT], jv[EPT], rv[EPT], ev[MAX_CALL_SLOTS][EPT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < EPT; ++u) {
             const int e = min(e0 + u * SEG_THREADS, nent - 1);
             av[u] = ulist[e / stride];
             jv[u] = e % stride;
             rv[u] = ranks[av[u]];
-            ev[u] = pz[(int64_t)av[u] * stride + jv[u]];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int z = 0; z < MAX_CALL_SLOTS; ++z) {
+            if (z >= n_slots_call) break;   // uniform
+            const int32_t *pz = sp.pt[z];
+#pragma unroll
+            for (int u = 0; u < EPT; ++u) ev[z][u] = pz[(int64_t)av[u] * stride + jv[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
             if (e0 + u * SEG_THREADS >= nent) continue;
-            const int32_t r = rv[u], j = jv[u], ent = ev[u];
+            const int32_t r = rv[u], j = jv[u];
             int bad = 0;
             if (r < 0 || r > max_rank) {
-                if (j == 0) { bad = DEV_ERR_RANK; atomicOr(&cnt[av[u]], F_OFF); }
-            } else if (r == 0) {
-                if (j == 0) atomicOr(&cnt[av[u]], F_OFF);
-            } else if (j < 2 * r) {
-                if (ent == -1) bad = DEV_ERR_TABLE;
-                else if (ent < 0 || (int64_t)ent >= num_pages) bad = DEV_ERR_PAGE;
-            } else if (j == 2 * r && ent != -1) {
-                bad = DEV_ERR_TABLE;
+                if (j == 0) bad = DEV_ERR_RANK;
+            } else if (r > 0) {
+#pragma unroll
+                for (int z = 0; z < MAX_CALL_SLOTS; ++z) {
+                    if (z >= n_slots_call) break;
+                    const int32_t ent = ev[z][u];
+                    if (j < 2 * r) {
+                        if (ent == -1) bad |= DEV_ERR_TABLE;
+                        else if (ent < 0 || (int64_t)ent >= num_pages) bad |= DEV_ERR_PAGE;
+                    } else if (j == 2 * r && ent != -1) {
+                        bad |= DEV_ERR_TABLE;
+                    }
+                }
             }
-            if (j == 0) rk[av[u]] = r;
+            if (j == 0) {
+                rk[av[u]] = r;
+                if (r <= 0 || r > max_rank) atomicOr(&cnt[av[u]], F_OFF);   // rank 0 or bad: no low-rank term
+            }
             if (bad) {
                 my_err |= bad;
                 atomicOr(&cnt[av[u]], F_OFF);
