@@ -197,6 +197,16 @@ constexpr int STAGE = (BM + BN) * BK;               // elements per pipeline sta
 __device__ __forceinline__ int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 7)) << 3); }
 constexpr size_t MAIN_LDS = 2 * STAGE * sizeof(uint16_t);
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 12] (the count is an immediate); larger n waits for all
+__device__ __forceinline__ void wait_vmem_le(int n) {
+    switch (n) {
+#define WV(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        WV(1) WV(2) WV(3) WV(4) WV(5) WV(6) WV(7) WV(8) WV(9) WV(10) WV(11) WV(12)
+#undef WV
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
 // PF_WAVES waves in a 2 x (PF_WAVES / 2) grid over the 256 x 256 tile; wave (wm, wn) computes rows
 // WTM wm + [0, WTM) x columns WTN wn + [0, WTN) as WMI x WNI blocks of 32 x 32.
 #ifndef PF_WAVES
@@ -442,12 +452,14 @@ __device__ __forceinline__ void prefill_main_body(
             }
         }
     };
-    // B rows of an adapter straight into a buffer of [64][BN] (LR_K loads per thread, rows past the rank
-    // are stand-ins, so the count is fixed)
-    auto lr_issue_b = [&](uint16_t *buf, const int32_t *pg) {
+    // B rows of adapter li straight into a buffer of [64][BN]: the rows below its rank rounded up to 16
+    // (load k of a thread covers rows 16 k .. 16 k + 15, so nb_of(li) loads per thread; rows from r to
+    // that bound are stand-ins, rows past it are left as they are and never read)
+    auto nb_of = [&](int li) { return min(max(__builtin_amdgcn_readfirstlane((s_lr[li] + 15) >> 4), 1), LR_K); };
+    auto lr_issue_b = [&](uint16_t *buf, const int32_t *pg, int nb) {
 #pragma unroll
         for (int k = 0; k < LR_K; ++k)
-            lds_gload16(bsrc(pg, k), (lds_void *)(buf + (PF_THREADS * k + 64 * wave) * 8));
+            if (k < nb) lds_gload16(bsrc(pg, k), (lds_void *)(buf + (PF_THREADS * k + 64 * wave) * 8));
     };
     // debug: the B page each B row of adapter li was loaded from (as the loads above used it), recorded
     // for every row of the tile that belongs to the adapter (one thread per B row)
@@ -536,7 +548,7 @@ __device__ __forceinline__ void prefill_main_body(
         if (nlist > 3) lr_pages(3, pgB);
         __builtin_amdgcn_sched_barrier(0);
         if (nlist > 1) {
-            lr_issue_b(buf(1), pg1);
+            lr_issue_b(buf(1), pg1, nb_of(1));
             dbg_b(1, pg1);
         }
         dbg_b(0, pg0);
@@ -547,19 +559,17 @@ __device__ __forceinline__ void prefill_main_body(
         auto iter = [&](int li, int32_t *use) {
             if (li >= 1) {
                 // loads younger than adapter li's B rows: li = 1: [B(2), ids(4)]; li >= 2: [ids(li + 2),
-                // B(li + 1), ids(li + 3)] -- those that were issued
-                const int n = li == 1 ? (nlist > 2) + (nlist > 4)
-                                      : (li + 2 < nlist) + (li + 1 < nlist) + (li + 3 < nlist);
+                // B(li + 1), ids(li + 3)] -- those that were issued (ids: LR_K a thread, B(x): nb_of(x))
+                const int n = li == 1 ? (nlist > 2 ? nb_of(2) : 0) + (nlist > 4 ? LR_K : 0)
+                                      : (li + 2 < nlist ? LR_K : 0) + (li + 1 < nlist ? nb_of(li + 1) : 0) +
+                                            (li + 3 < nlist ? LR_K : 0);
                 // (the debug instantiation's atomics count as memory operations too: it waits for all)
-                if (n == 0 || DBG) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LR_K) : "memory");
-                else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LR_K) : "memory");
-                else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LR_K) : "memory");
+                wait_vmem_le(DBG ? 0 : n);
             }
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             if (li + 2 < nlist) {
-                lr_issue_b(buf(li + 2), use);
+                lr_issue_b(buf(li + 2), use, nb_of(li + 2));
                 dbg_b(li + 2, use);
             }
             __builtin_amdgcn_sched_barrier(0);
