@@ -531,8 +531,9 @@ __device__ __forceinline__ void prefill_main_body(
     // adapter li rotate through three buffers -- X's B part and the two halves of stage Y, free since
     // the last K step -- and go out two adapters ahead of their MFMAs; their page ids two further ahead,
     // in two register sets taken in turn.  Each adapter waits for its own loads only (the count of
-    // younger loads is exact: every load group has a fixed size), then for one barrier, after which the
-    // buffer of adapter li - 1 is free for adapter li + 2.
+    // younger loads is exact: page ids are LR_K loads a thread, an adapter's B rows nb_of loads, both
+    // known to every wave), then for one barrier, after which the buffer of adapter li - 1 is free for
+    // adapter li + 2.
     if (nlist > 0) {
         uint16_t *const X = sm + (nk & 1) * STAGE, *const Y = sm + ((nk + 1) & 1) * STAGE;
         const uint16_t *const Vs = X + 64 * BN;

@@ -97,8 +97,9 @@ __device__ int3 block_exclusive_scan3(int32_t *a0, int32_t *a1, int32_t *a2, int
 
 // One workgroup of 1024 threads, two dependent rounds of global reads:
 //  1. the ids (range-checked; tokens counted per adapter id);
-//  2. for every adapter in use, its rank and its whole page-table row, all loaded together and
-//     checked after they arrive (entries [0, 2r) hold pages in range, entry 2r is -1 when 2r < stride).
+//  2. for every adapter in use, its rank and its whole page-table row in every slot of the call, all
+//     loaded together (EPT entries a thread at a time) and checked after they arrive (entries [0, 2r)
+//     hold pages in range, entry 2r is -1 when 2r < stride; a bad row in any slot turns the adapter off).
 // Tokens of an adapter with rank 0, a bad rank or a bad row get no low-rank term.  Segments are in
 // adapter order; tokens of one adapter land in perm in an unspecified order (LDS atomics): no result
 // depends on the order of tokens within a segment.  Work items (`chunk` sorted rows of one segment) are
