@@ -288,14 +288,19 @@ __device__ __forceinline__ void prefill_main_body(
         offa[i] = (uint32_t)(min(r, rvx - 1) * H + p * 8) * 2u;
         offb[i] = (uint32_t)(min(r, rvw - 1) * H + p * 8) * 2u;
     }
-    auto dma = [&](int kt, uint16_t *stage) {
+    // half h of tile kt's loads (DPW each): h = 0 the x chunks, h = 1 the W chunks
+    auto dma_half = [&](int kt, uint16_t *stage, int h) {
         const int soff = kt * BK * 2;
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             uint16_t *dst = stage + 8 * (PF_WAVES * i + wave) * BK;
-            lds_load16(rx, (lds_void *)dst, offa[i], soff);
-            lds_load16(rw, (lds_void *)(dst + BM * BK), offb[i], soff);
+            if (h == 0) lds_load16(rx, (lds_void *)dst, offa[i], soff);
+            else lds_load16(rw, (lds_void *)(dst + BM * BK), offb[i], soff);
         }
+    };
+    auto dma = [&](int kt, uint16_t *stage) {
+        dma_half(kt, stage, 0);
+        dma_half(kt, stage, 1);
     };
     const int frow = lane & 31, fk = (lane >> 5) * 8;   // 32x32x16 operand: row lane%32, k 8*(lane/32)
     // the fragments of k-substep ks of a stage, in the order the MFMAs consume them
@@ -307,6 +312,21 @@ __device__ __forceinline__ void prefill_main_body(
         for (int ni = 0; ni < WNI; ++ni) fb[ni] = load16(Bs + swz(wn * WTN + ni * 32 + frow, pc));
 #pragma unroll
         for (int mi = 1; mi < WMI; ++mi) fa[mi] = load16(As + swz(wm * WTM + mi * 32 + frow, pc));
+    };
+
+    // one of those reads: u = 0 is fa[0], u = 1 .. WNI fb[u - 1], then fa[1 ..]
+    auto frag_one = [&](const uint16_t *stage, int ks, int u, u32x4_t *fa, u32x4_t *fb) {
+        const uint16_t *As = stage, *Bs = stage + BM * BK;
+        const int pc = ks * 2 + (fk >> 3);
+        if (u == 0) fa[0] = load16(As + swz(wm * WTM + frow, pc));
+        else if (u <= WNI) fb[u - 1] = load16(Bs + swz(wn * WTN + (u - 1) * 32 + frow, pc));
+        else fa[u - WNI] = load16(As + swz(wm * WTM + (u - WNI) * 32 + frow, pc));
+    };
+    // load i (< DPW) of half h of tile kt
+    auto dma_one = [&](int kt, uint16_t *stage, int h, int i) {
+        uint16_t *dst = stage + 8 * (PF_WAVES * i + wave) * BK;
+        if (h == 0) lds_load16(rx, (lds_void *)dst, offa[i], kt * BK * 2);
+        else lds_load16(rw, (lds_void *)(dst + BM * BK), offb[i], kt * BK * 2);
     };
 
     f32x16_t acc[WMI][WNI];
@@ -321,8 +341,8 @@ __device__ __forceinline__ void prefill_main_body(
     // k-substeps).  The one barrier of a step sits between substeps 2 and 3: each wave first waits for
     // its own loads of tile kt + 1 and for its last reads of stage kt & 1.  After it, substep 3 reads
     // the fragments of step kt + 1's first substep (so no MFMA waits for LDS at a step boundary) and
-    // starts the loads of tile kt + 2 into stage kt & 1, which no wave reads any more.  Steps past the
-    // end load a stand-in tile (step 0 again): it keeps the loop free of branches and is never read.
+    // starts the loads of tile kt + 2 into stage kt & 1, which no wave reads any more; the second half
+    // of those loads goes out in substep 0 of step kt + 1.
     const int nk = H / BK;
     u32x4_t af[2][WMI], bf[2][WNI];
     dma(0, sm);
@@ -389,13 +409,21 @@ __device__ __forceinline__ void prefill_main_body(
         const int idx = tid + PF_THREADS * k, row = idx >> 3, p = (idx & 7) ^ ((row >> 1) & 7);
         return v16 + (int64_t)min(m0 + row, T - 1) * R + min(8 * p, R - 8);
     };
+    // the first adapter's B rows (h = 0) or the tile's v rows (h = 1), LR_K = LR_V loads a thread
+    auto lr_half = [&](uint16_t *stg, int h) {
+#pragma unroll
+        for (int k = 0; k < LR_K; ++k) {
+            if (h == 0) lds_gload16(bsrc(pg0, k), (lds_void *)(stg + (PF_THREADS * k + 64 * wave) * 8));
+            else lds_gload16(vsrc(k), (lds_void *)(stg + 64 * BN + (PF_THREADS * k + 64 * wave) * 8));
+        }
+    };
+    auto lr_one = [&](uint16_t *stg, int h, int k) {
+        if (h == 0) lds_gload16(bsrc(pg0, k), (lds_void *)(stg + (PF_THREADS * k + 64 * wave) * 8));
+        else lds_gload16(vsrc(k), (lds_void *)(stg + 64 * BN + (PF_THREADS * k + 64 * wave) * 8));
+    };
     auto lr_dma = [&](uint16_t *stg) {
-#pragma unroll
-        for (int k = 0; k < LR_K; ++k)
-            lds_gload16(bsrc(pg0, k), (lds_void *)(stg + (PF_THREADS * k + 64 * wave) * 8));
-#pragma unroll
-        for (int k = 0; k < LR_V; ++k)
-            lds_gload16(vsrc(k), (lds_void *)(stg + 64 * BN + (PF_THREADS * k + 64 * wave) * 8));
+        lr_half(stg, 0);
+        lr_half(stg, 1);
     };
     // The K-extension of adapter li: rp / 16 substeps of 32x32x16 MFMAs on the accumulators.  The v
     // operand (the tile's v rows, all adapters, in Vs) is masked in registers: rows of other adapters and
@@ -480,38 +508,49 @@ __device__ __forceinline__ void prefill_main_body(
     if (nk > 1) dma(1, sm + STAGE);
     else lr_dma(sm + STAGE);   // a single K step: stage 1 is the low-rank stage from the start
     frag(sm, 0, af[0], bf[0]);
-    // One K step.  MODE 0: starts the loads of tile kt + 2 in substep 3; MODE 1 (step nk - 2): the
-    // low-rank operands instead; MODE 2 (the last step): no loads, and its barrier waits for none.
-    auto step = [&](int kt, auto mode) {
-        constexpr int MODE = decltype(mode)::value;
+    // One K step.  A tile's loads go out in two halves, so that the load path takes them over 16
+    // MFMAs instead of 8: the x half of tile kt + 2 in substep 3 of step kt (the stage of tile kt is
+    // free once the step's barrier is passed), its W half in substep 0 of step kt + 1.  Both have
+    // landed at the barrier of step kt + 1.  The low-rank operands take the place of tile nk: the B
+    // rows in substep 3 of step nk - 2, the v rows in substep 0 of step nk - 1.
+    //   D0: the loads of substep 0 -- 0 none, 1 the W half of tile kt + 1, 2 the v rows;
+    //   D3: the loads of substep 3 -- 0 none, 1 the x half of tile kt + 2, 2 the B rows;
+    //   LAST: the last step (no fragments of a next step; its barrier waits for no load).
+    auto step = [&](int kt, auto d0, auto d3, auto last) {
+        constexpr int D0 = decltype(d0)::value, D3 = decltype(d3)::value;
+        constexpr bool LAST = decltype(last)::value;
         uint16_t *cur = sm + (kt & 1) * STAGE, *oth = sm + ((kt + 1) & 1) * STAGE;
         __builtin_amdgcn_sched_barrier(0);
-        // per k-substep (WMI x WNI MFMAs, operands in buffer ks & 1): the next WMI + WNI fragment reads
-        // into the other buffer and, in substep 3, the 2 DPW loads, one after each MFMA
+        // per k-substep (WMI x WNI MFMAs, operands in buffer ks & 1), in this issue order: MFMA g, the
+        // next substep's fragment read g (g < WMI + WNI, into the other buffer), and in substeps 0 and 3
+        // after every other MFMA one load of a half.  The order is fixed by scheduling fences: left to
+        // the scheduler, the loads and reads of a substep went out together after its first MFMA.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) frag(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-            else if (MODE != 2) frag(oth, 0, af[0], bf[0]);
-            if (ks == 3) {
-                if constexpr (MODE == 0) dma(kt + 2, cur);
-                if constexpr (MODE == 1) lr_dma(cur);
-            }
-#pragma unroll
-            for (int mi = 0; mi < WMI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < WNI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mi]),
-                                                                          __builtin_bit_cast(bf16x8_t, bf[ks & 1][ni]),
-                                                                          acc[mi][ni], 0, 0, 0);
 #pragma unroll
             for (int g = 0; g < WMI * WNI; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (g < WMI + WNI && (ks < 3 || MODE != 2)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (ks == 3 && MODE != 2 && g < 2 * DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                const int mi = g / WNI, ni = g % WNI;
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mi]),
+                                                                      __builtin_bit_cast(bf16x8_t, bf[ks & 1][ni]),
+                                                                      acc[mi][ni], 0, 0, 0);
+                if (g < WMI + WNI) {
+                    if (ks < 3) frag_one(cur, ks + 1, g, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+                    else if (!LAST) frag_one(oth, 0, g, af[0], bf[0]);
+                }
+                if ((g & 1) == 0 && g / 2 < DPW) {
+                    if (ks == 0) {
+                        if constexpr (D0 == 1) dma_one(kt + 1, oth, 1, g / 2);
+                        if constexpr (D0 == 2) lr_one(oth, 1, g / 2);
+                    }
+                    if (ks == 3) {
+                        if constexpr (D3 == 1) dma_one(kt + 2, cur, 0, g / 2);
+                        if constexpr (D3 == 2) lr_one(cur, 0, g / 2);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
             if (ks == 2) {
-                if constexpr (MODE == 2)
+                if constexpr (LAST)
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // only the low-rank loads are in flight
                 else
                     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -521,9 +560,22 @@ __device__ __forceinline__ void prefill_main_body(
             }
         }
     };
-    for (int kt = 0; kt + 2 < nk; ++kt) step(kt, std::integral_constant<int, 0>());
-    if (nk >= 2) step(nk - 2, std::integral_constant<int, 1>());
-    step(nk - 1, std::integral_constant<int, 2>());
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using NL = std::false_type;
+    using LS = std::true_type;
+    if (nk >= 3) {
+        step(0, I0(), I1(), NL());   // tile 1 went out whole before the loop
+        for (int kt = 1; kt + 2 < nk; ++kt) step(kt, I1(), I1(), NL());
+        step(nk - 2, I1(), I2(), NL());
+        step(nk - 1, I2(), I0(), LS());
+    } else if (nk == 2) {
+        step(0, I0(), I2(), NL());
+        step(1, I2(), I0(), LS());
+    } else {
+        step(0, I0(), I0(), LS());   // every low-rank load went out before the loop
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every load, the low-rank operands' included, has landed
 
     // ---- low-rank term: one K-extension per adapter owning rows of this tile.  Adapter 0's B rows and
