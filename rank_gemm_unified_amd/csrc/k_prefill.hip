@@ -522,9 +522,9 @@ __device__ __forceinline__ void prefill_main_body(
         uint16_t *cur = sm + (kt & 1) * STAGE, *oth = sm + ((kt + 1) & 1) * STAGE;
         __builtin_amdgcn_sched_barrier(0);
         // per k-substep (WMI x WNI MFMAs, operands in buffer ks & 1), in this issue order: MFMA g, the
-        // next substep's fragment read g (g < WMI + WNI, into the other buffer), and in substeps 0 and 3
-        // after every other MFMA one load of a half.  The order is fixed by scheduling fences: left to
-        // the scheduler, the loads and reads of a substep went out together after its first MFMA.
+        // next substep's fragment reads 2g and 2g + 1 (into the other buffer), and in substeps 0 and 3
+        // load g of a half (g < DPW).  The order is fixed by scheduling fences: left to the scheduler,
+        // the loads and reads of a substep went out together after its first MFMA.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -533,18 +533,20 @@ __device__ __forceinline__ void prefill_main_body(
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mi]),
                                                                       __builtin_bit_cast(bf16x8_t, bf[ks & 1][ni]),
                                                                       acc[mi][ni], 0, 0, 0);
-                if (g < WMI + WNI) {
-                    if (ks < 3) frag_one(cur, ks + 1, g, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-                    else if (!LAST) frag_one(oth, 0, g, af[0], bf[0]);
-                }
-                if ((g & 1) == 0 && g / 2 < DPW) {
+#pragma unroll
+                for (int u = 2 * g; u < 2 * g + 2; ++u)
+                    if (u < WMI + WNI) {
+                        if (ks < 3) frag_one(cur, ks + 1, u, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+                        else if (!LAST) frag_one(oth, 0, u, af[0], bf[0]);
+                    }
+                if (g < DPW) {
                     if (ks == 0) {
-                        if constexpr (D0 == 1) dma_one(kt + 1, oth, 1, g / 2);
-                        if constexpr (D0 == 2) lr_one(oth, 1, g / 2);
+                        if constexpr (D0 == 1) dma_one(kt + 1, oth, 1, g);
+                        if constexpr (D0 == 2) lr_one(oth, 1, g);
                     }
                     if (ks == 3) {
-                        if constexpr (D3 == 1) dma_one(kt + 2, cur, 0, g / 2);
-                        if constexpr (D3 == 2) lr_one(cur, 0, g / 2);
+                        if constexpr (D3 == 1) dma_one(kt + 2, cur, 0, g);
+                        if constexpr (D3 == 2) lr_one(cur, 0, g);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
