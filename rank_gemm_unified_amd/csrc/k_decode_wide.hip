@@ -491,7 +491,7 @@ __device__ __forceinline__ void decode_wide_body(
             if (t < T) {
                 const int q = g.pos[t];
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) ypart[((int64_t)split * T + q) * H + n0 + 16 * nb + lrow] = acc[m][nb][i];
+                for (int nb = 0; nb < 4; ++nb) store4_wt(ypart + ((int64_t)split * T + q) * H + n0 + 16 * nb + lrow, __float_as_uint(acc[m][nb][i]));
             }
         }
 
