@@ -480,10 +480,14 @@ __device__ __forceinline__ void prefill_main_body(
             }
         }
     };
-    // B rows of adapter li straight into a buffer of [64][BN]: the rows below its rank rounded up to 16
-    // (load k of a thread covers rows 16 k .. 16 k + 15, so nb_of(li) loads per thread; rows from r to
-    // that bound are stand-ins, rows past it are left as they are and never read)
-    auto nb_of = [&](int li) { return min(max(__builtin_amdgcn_readfirstlane((s_lr[li] + 15) >> 4), 1), LR_K); };
+    // B rows of adapter li straight into a buffer of [64][BN]: the rows below its rank rounded up to 16,
+    // the rows its MFMAs read (load k of a thread covers rows RPL k .. RPL k + RPL - 1, RPL = PF_THREADS
+    // / 32, so nb_of(li) loads per thread; rows from r to that bound are stand-ins, rows past it are left
+    // as they are and never read)
+    constexpr int RPL = PF_THREADS / 32;
+    auto nb_of = [&](int li) {
+        return min(max(__builtin_amdgcn_readfirstlane((((s_lr[li] + 15) & ~15) + RPL - 1) / RPL), 1), LR_K);
+    };
     auto lr_issue_b = [&](uint16_t *buf, const int32_t *pg, int nb) {
 #pragma unroll
         for (int k = 0; k < LR_K; ++k)
