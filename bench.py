@@ -16,8 +16,9 @@ timed loop rotates through enough independent replicas (pool, page table, W, x, 
 Prints one JSON line: the throughput, the dominant kernel's roofline fraction (its algorithmic
 bytes or flops over its average device time, from HIP events recorded on its launch stream) with
 the whole call's fraction beside it (roofline.call), and the fp64 CPU oracle timed on this host as a
-baseline.  The default run also times the prefill batch (MFMA-bound) and the 2000-adapter batch
-(HBM-bound, its q/k/v/o in one call) and adds their lines' figures under "more_workloads".  The
+baseline.  The default run also times the prefill batch (MFMA-bound), the 2000-adapter batch
+(HBM-bound, its q/k/v/o in one call) and the 40-layer 13B-shaped stack (one call per layer) and adds
+their lines' figures under "more_workloads".  The
 roofline's "traffic" (HBM bytes per launch from committed rocprofv3 counters) is given when the
 counters were taken on the current kernel source, the same workload and the same slots per launch;
 null otherwise.  With --fuse-slots a layer's q, k, v
@@ -510,7 +511,7 @@ def main():
                     help="project up to 4 consecutive slots (a layer's q, k, v and o, each with its own x) in one "
                          "lora_project_slots_x call instead of one lora_project call per slot")
     ap.add_argument("--no-more", action="store_true",
-                    help="default workload only: skip the extra prefill and many-adapter blocks")
+                    help="default workload only: skip the extra prefill, many-adapter and stack blocks")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to touch >= 1 GiB between reuses")
     ap.add_argument("--profile-calls", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -565,11 +566,12 @@ def main():
     del w
     torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_more:
-        # the prefill (MFMA-bound) and many-adapter (HBM-bound) workloads, timed in the same run
+        # the prefill (MFMA-bound) and many-adapter (HBM-bound) workloads, timed in the same run,
         more = {}
         # (the many-adapter layer as a user projects it: q, k, v and o in one lora_project_slots_x call)
-        for name, n_steps, fuse in (("prefill", 300, False), ("many", 300, True)):
-            w2, r2 = measure(rg, torch, name, n_steps, 30, fuse, args.profile_calls)
+        # and the whole 40-layer 13B-shaped stack, one lora_project_slots_x call per layer
+        for name, n_steps, n_warm, fuse in (("prefill", 300, 30, False), ("many", 300, 30, True), ("stack13b", 10, 2, True)):
+            w2, r2 = measure(rg, torch, name, n_steps, n_warm, fuse, args.profile_calls)
             more[name] = {k: r2[k] for k in ("value", "unit", "ms_per_step", "steps", "config", "step_hbm_frac",
                                              "roofline")}
             w2.drop_cache()
