@@ -392,6 +392,51 @@ __device__ __forceinline__ void decode_stream_body(
     };
     f32x4_t pacc0[MB];
     asm volatile("" ::"v"(ent[0]), "v"(ent[1]));   // the publisher's row has landed: keep its loads at S2
+    // ---- publish (wave 0): segments s = blockIdx.x + k gridDim.x -- check the page-table row, then
+    // write the segment's sorted-token records and B page ids; workgroup 0 also writes the
+    // ungrouped tokens.  It needs only the grouping and the row, so it goes out here, while the
+    // block's A pages are still in flight, and not after the reduction (the publishing workgroups
+    // were the last to end: 0.5 us less per call at 64 tokens)
+    if (wave == 0) {
+        for (int s = blockIdx.x; s < nseg; s += gridDim.x) {
+            const int32_t a = __shfl(seg_a, s, 64), rs = __shfl(seg_r, s, 64);
+            const int32_t q0 = __shfl(toff, s, 64), qn = __shfl(seg_n, s, 64);
+            const int lim = min(2 * rs + 1, stride);
+            if (s != (int)blockIdx.x) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) ent[u] = pt[(int64_t)a * stride + min(lane + 64 * u, lim - 1)];
+            }
+            int bad = 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int j = lane + 64 * u;
+                if (j >= lim) continue;
+                if (j < 2 * rs) {
+                    if (ent[u] == -1) bad |= DEV_ERR_TABLE;
+                    else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad |= DEV_ERR_PAGE;
+                } else if (ent[u] != -1) {
+                    bad |= DEV_ERR_TABLE;
+                }
+            }
+            for (int off = 32; off > 0; off >>= 1) bad |= __shfl_xor(bad, off, 64);
+            err |= bad;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int j = lane + 64 * u;
+                if (j >= rs && j < 2 * rs)
+                    for (int q = q0; q < q0 + qn; ++q) spages[(int64_t)q * RP + (j - rs)] = ent[u];
+            }
+            if (key == a) sorted_tok[my_pos] = int4{lane, bad ? -1 : a, bad ? 0 : rs, 0};
+        }
+        // id/rank faults are per lane and every workgroup sees them: workgroup 0 reports them; page-table
+        // faults were already OR-reduced over the wave by the workgroup that checked the row
+        for (int off = 32; off > 0; off >>= 1) err |= __shfl_xor(err, off, 64);
+        if (blockIdx.x == 0 && lane < T && key < 0) sorted_tok[my_pos] = int4{lane, -1, 0, 0};
+        if (lane == 0) {
+            const int mine = blockIdx.x == 0 ? err : err & (DEV_ERR_TABLE | DEV_ERR_PAGE);
+            if (mine) atomicOr(err_word, mine);
+        }
+    }
     page_mfma(pv, sc, pacc0, true);
     // further blocks (more pages than 16 n_tiles: rare) while x is still in LDS, through their own buffer
     for (int b = tile + n_tiles; b * 16 < npages; b += n_tiles) {
@@ -462,48 +507,6 @@ __device__ __forceinline__ void decode_stream_body(
         page_store(red + TP * RS, WS, PS, plive, pa, pj, pid);
     }
 
-    // ---- publish (wave 0): segments s = blockIdx.x + k gridDim.x -- check the page-table row, then
-    // write the segment's sorted-token records and B page ids; workgroup 0 also writes the
-    // ungrouped tokens
-    if (wave != 0) return;
-    for (int s = blockIdx.x; s < nseg; s += gridDim.x) {
-        const int32_t a = __shfl(seg_a, s, 64), rs = __shfl(seg_r, s, 64);
-        const int32_t q0 = __shfl(toff, s, 64), qn = __shfl(seg_n, s, 64);
-        const int lim = min(2 * rs + 1, stride);
-        if (s != (int)blockIdx.x) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) ent[u] = pt[(int64_t)a * stride + min(lane + 64 * u, lim - 1)];
-        }
-        int bad = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = lane + 64 * u;
-            if (j >= lim) continue;
-            if (j < 2 * rs) {
-                if (ent[u] == -1) bad |= DEV_ERR_TABLE;
-                else if (ent[u] < 0 || (int64_t)ent[u] >= num_pages) bad |= DEV_ERR_PAGE;
-            } else if (ent[u] != -1) {
-                bad |= DEV_ERR_TABLE;
-            }
-        }
-        for (int off = 32; off > 0; off >>= 1) bad |= __shfl_xor(bad, off, 64);
-        err |= bad;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = lane + 64 * u;
-            if (j >= rs && j < 2 * rs)
-                for (int q = q0; q < q0 + qn; ++q) spages[(int64_t)q * RP + (j - rs)] = ent[u];
-        }
-        if (key == a) sorted_tok[my_pos] = int4{lane, bad ? -1 : a, bad ? 0 : rs, 0};
-    }
-    // id/rank faults are per lane and every workgroup sees them: workgroup 0 reports them; page-table
-    // faults were already OR-reduced over the wave by the workgroup that checked the row
-    for (int off = 32; off > 0; off >>= 1) err |= __shfl_xor(err, off, 64);
-    if (blockIdx.x == 0 && lane < T && key < 0) sorted_tok[my_pos] = int4{lane, -1, 0, 0};
-    if (lane == 0) {
-        const int mine = blockIdx.x == 0 ? err : err & (DEV_ERR_TABLE | DEV_ERR_PAGE);
-        if (mine) atomicOr(err_word, mine);
-    }
 }
 
 // The stream kernel for one slot, and for the n slots of one call (blockIdx.z = the slot; the slots
