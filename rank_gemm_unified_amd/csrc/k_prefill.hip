@@ -643,12 +643,37 @@ __device__ __forceinline__ void prefill_main_body(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stand-in loads past the end have landed
     }
 
-    // ---- one rounding, and each lane stores its own elements with 2-byte streaming stores (the 32
-    //      lanes of a half-wave cover 64 contiguous bytes of a row).  Every tile ends at about the same
-    //      time, so y (T x H) leaves in one burst at the write rate; stores that keep their lines in
-    //      the caches made it about 4 us longer at 4096 x 4096, and staging the tile through LDS for
-    //      16-byte stores cost 0.5 us more.  32x32 block layout: lane holds column lane%32 and, in
-    //      register e, row 8*(e/4) + 4*(lane/32) + e%4.
+    // ---- one rounding (the hardware's round-to-nearest-even convert), and each lane stores its own
+    //      elements with 2-byte streaming stores (the 32 lanes of a half-wave cover 64 contiguous bytes
+    //      of a row).  32x32 block layout: lane holds column lane%32 and, in register e, row 8*(e/4) +
+    //      4*(lane/32) + e%4.  A tile wholly inside y takes a path with no bounds test: each row's
+    //      address is a scalar base plus one lane offset worked out once (a per-store 64-bit multiply
+    //      and exec-mask branch made the stores take 8.5 us of a tile at the 13B stack's shapes, 2.6 us
+    //      without).  At 4096 x 4096 every tile ends at about the same time and y leaves in one burst
+    //      at the write rate: stores that keep their lines in the caches made that about 4 us longer,
+    //      and 8-byte stores of the transposed block (MFMA operands swapped) 50 us longer.
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    if (m0 + BM <= T && n0 + BN <= H) {
+        const uint32_t loff = (uint32_t)(4 * (lane >> 5)) * (uint32_t)H + (uint32_t)(lane & 31);
+#pragma unroll
+        for (int mi = 0; mi < WMI; ++mi)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    // registers e and e + 1: rows 8 g + 2 e2 and the next of the block (+ 4 in the upper half-wave)
+                    uint16_t *rb = y + (int64_t)(m0 + wm * WTM + mi * 32 + 8 * g + 2 * e2) * H + n0 + wn * WTN;
+                    const int e = 4 * g + 2 * e2;
+#pragma unroll
+                    for (int ni = 0; ni < WNI; ++ni) {
+                        const bf16x2_t pv = {(__bf16)acc[mi][ni][e], (__bf16)acc[mi][ni][e + 1]};
+                        const uint32_t w = __builtin_bit_cast(uint32_t, pv);
+                        __builtin_nontemporal_store((uint16_t)w, rb + loff + ni * 32);
+                        __builtin_nontemporal_store((uint16_t)(w >> 16), rb + H + loff + ni * 32);
+                    }
+                }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
@@ -658,7 +683,8 @@ __device__ __forceinline__ void prefill_main_body(
                 const int row = wm * WTM + mi * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
                 const int col = wn * WTN + ni * 32 + (lane & 31);
                 if (m0 + row < T && n0 + col < H)
-                    __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(acc[mi][ni][e]), y + (int64_t)(m0 + row) * H + n0 + col);
+                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)acc[mi][ni][e]),
+                                                y + (int64_t)(m0 + row) * H + n0 + col);
             }
 }
 
