@@ -26,32 +26,38 @@ constexpr int VSPLIT = 4;     // K-splits of the shrink
 // workgroup per CU) when the work items fit one round of the chip (T <= 4096), else four (two per
 // CU): measured best at 4096 and at 8448 rows.
 //
-// Grid (work items + spare, VSPLIT), 256 threads.  Work item = up to 64 tokens of one adapter
-// segment, read as one record; split = a K range of H / VSPLIT.  A small tiled GEMM: per K tile of
-// 64, the item's x rows (gathered through perm) and the adapter's A pages (<= 64, one per column of
-// v) go from global memory straight into a ring of SNS LDS stages, SNS - 1 tiles ahead (the whole
-// item chain is two round trips: the record, then perm and the page-table row); four waves
-// compute 32x32 blocks (rows 32 wm.., pages 32 wn..) with 32x32x16 MFMAs.  Writes float32 partials
-// vpart[split][t][0..r); k_v_finalize adds them in split order.  (No in-kernel cross-workgroup
-// reduction: on this chip a device-scope fence writes back and invalidates the whole L2.)
+// Work unit = (work item, split, slot): item = up to 64 tokens of one adapter segment, read as one
+// record; split = a K range of H / VSPLIT; slot = a projection of the call.  A persistent grid (as
+// many workgroups of 256 threads as the chip holds at once) walks the units in item order and stops
+// at the first record past the last item (adapter -1): the item bound the host knows follows from the
+// number of tokens, so a grid over it was mostly workgroups that read a record and left -- about
+// 14,500 of 18,000 at the 13B stack's shapes, each holding an LDS slot for a round trip.  The slots of one
+// (item, split) are consecutive units on one XCD, so the slots that share x (q, k and v) read its
+// rows there at about the same time and share its L2.
+//
+// Per unit, a small tiled GEMM: per K tile of 64, the item's x rows (gathered through perm) and the
+// adapter's A pages (<= 64, one per column of v) go from global memory straight into a ring of SNS
+// LDS stages, SNS - 1 tiles ahead (the unit's chain is two round trips: the record, then perm and the
+// page-table row); four waves compute 32x32 blocks (rows 32 wm.., pages 32 wn..) with 32x32x16 MFMAs.
+// (Loading only the 8-row groups below the item's row count and rank -- one group of x rows for a
+// decode-row item -- made the 4096-token shrink 1.8 us slower and the 13B stack's 1 us faster.)
+// Writes float32 partials vpart[split][t][0..r); k_v_finalize adds
+// them in split order.  (No in-kernel cross-workgroup reduction: on this chip a device-scope fence
+// writes back and invalidates the whole L2.)
 constexpr int SK = 64;                                  // K tile
 constexpr int SH_STAGE = (SH_ROWS + 64) * SK;           // x rows + page rows, elements (16 KiB)
 __device__ __forceinline__ int sswz(int r, int p) { return r * SK + ((p ^ ((r >> 1) & 7)) << 3); }   // as swz
 
+// One work unit (item, split) of one slot.  Ends with every load landed and a barrier, so that the
+// workgroup's next unit may reuse the stages and s_perm.
 template <int SNS, bool DBG>
-__device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H,
-                                              const int32_t *__restrict__ pt, int32_t stride,
-                                              const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
-                                              float *__restrict__ vpart, int32_t T, int32_t R,
-                                              const DebugOut dbg = DebugOut{}) {
-    const int4 rec = item_rec[blockIdx.x];
-    if (rec.x < 0) return;   // past the last work item
-    extern __shared__ __align__(16) uint16_t st[];   // SNS stages
-    __shared__ int32_t s_perm[SH_ROWS];
-    __shared__ int32_t s_pid[DBG ? SH_ROWS : 1];     // debug: the page of each column of v
+__device__ __forceinline__ void shrink_unit(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H,
+                                            const int32_t *__restrict__ pt, int32_t stride,
+                                            const int32_t *__restrict__ perm, const int4 rec, int split,
+                                            float *__restrict__ vpart, int32_t T, int32_t R, uint16_t *st,
+                                            int32_t *s_perm, int32_t *s_pid, const DebugOut dbg) {
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int32_t a = rec.x, r = rec.y, row0 = rec.z, n = rec.w;   // 1 <= r, 1 <= n <= 64
-    const int split = blockIdx.y;
     const int ktiles = H / SK;
     const int kt0 = (int)((int64_t)ktiles * split / VSPLIT), kt1 = (int)((int64_t)ktiles * (split + 1) / VSPLIT);
     // Loads: one fills 1 KiB of a stage, rows 8d .. 8d + 7 (d < 8: x rows, d >= 8: page rows d - 8);
@@ -100,8 +106,8 @@ __device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, cons
                                                           __builtin_bit_cast(bf16x8_t, fb), acc, 0, 0, 0);
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads have landed before the kernel ends
-    __syncthreads();   // s_perm
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stand-in loads have landed
+    __syncthreads();   // s_perm; every wave is past its last fragment read
     // 32x32 block layout: lane holds column (page) lane%32 and, in register e, row 8 (e/4) + 4 (lane/32) + e%4
     float *vout = vpart + (int64_t)split * T * R;
     const int j = wn * 32 + (lane & 31);
@@ -119,16 +125,47 @@ __device__ __forceinline__ void shrink_body(const uint16_t *__restrict__ x, cons
             dbg_put(dbg.order + 2 * (row0 + tid) + 1, a);
         }
     }
+    __syncthreads();   // s_perm and s_pid are read above; the next unit rewrites them
 }
 
-// One slot per launch, and the n slots of one call (blockIdx.z = the slot; the slots share x and the
-// token grouping); the one-slot kernel keeps the short argument block.
+// The units of n slots, walked by a persistent grid (gridDim.x a multiple of 8).  Unit u: XCD lane u % 8
+// (the XCD of every workgroup that takes it), slot (u / 8) % n, and (item, split) q = (u / 8n) 8 + u % 8
+// as item q / VSPLIT, split q % VSPLIT.  A workgroup's units have non-decreasing items, so the first
+// one past the last item ends its walk.
+template <int SNS, bool DBG>
+__device__ __forceinline__ void shrink_walk(const SlotPtrs &sp, int n, const uint16_t *__restrict__ pages, int32_t H,
+                                            int32_t stride, const int32_t *__restrict__ perm,
+                                            const int4 *__restrict__ item_rec, int32_t n_items_max,
+                                            int32_t T, int32_t R, const DebugOut dbg = DebugOut{}) {
+    extern __shared__ __align__(16) uint16_t st[];   // SNS stages
+    __shared__ int32_t s_perm[SH_ROWS];
+    __shared__ int32_t s_pid[DBG ? SH_ROWS : 1];     // debug: the page of each column of v
+    for (int64_t u = blockIdx.x;; u += gridDim.x) {
+        const int xl = (int)(u & 7), z = (int)((u >> 3) % n);
+        const int64_t q = (u >> 3) / n * 8 + xl;
+        const int64_t item = q / VSPLIT;
+        const int split = (int)(q % VSPLIT);
+        if (item >= n_items_max) break;
+        const int4 rec = item_rec[item];
+        if (rec.x < 0) break;   // past the last item
+        shrink_unit<SNS, DBG>((const uint16_t *)sp.x[z], pages, H, sp.pt[z], stride, perm, rec, split, sp.v[z], T, R,
+                              st, s_perm, s_pid, dbg);
+    }
+}
+
+// One slot (the short argument block), its debug instantiation, and the n slots of one call (the
+// slots share the token grouping).
 template <int SNS>
 __global__ __launch_bounds__(256) void k_shrink_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ pages, int32_t H,
                                                      const int32_t *__restrict__ pt, int32_t stride,
                                                      const int32_t *__restrict__ perm, const int4 *__restrict__ item_rec,
-                                                     float *__restrict__ vpart, int32_t T, int32_t R) {
-    shrink_body<SNS, false>(x, pages, H, pt, stride, perm, item_rec, vpart, T, R);
+                                                     int32_t n_items_max, float *__restrict__ vpart,
+                                                     int32_t T, int32_t R) {
+    SlotPtrs sp{};
+    sp.x[0] = x;
+    sp.pt[0] = pt;
+    sp.v[0] = vpart;
+    shrink_walk<SNS, false>(sp, 1, pages, H, stride, perm, item_rec, n_items_max, T, R);
 }
 
 template <int SNS>
@@ -136,18 +173,23 @@ __global__ __launch_bounds__(256) void k_shrink_mfma_dbg(const uint16_t *__restr
                                                          const uint16_t *__restrict__ pages, int32_t H,
                                                          const int32_t *__restrict__ pt, int32_t stride,
                                                          const int32_t *__restrict__ perm,
-                                                         const int4 *__restrict__ item_rec, float *__restrict__ vpart,
+                                                         const int4 *__restrict__ item_rec,
+                                                         int32_t n_items_max, float *__restrict__ vpart,
                                                          int32_t T, int32_t R, const DebugOut dbg) {
-    shrink_body<SNS, true>(x, pages, H, pt, stride, perm, item_rec, vpart, T, R, dbg);
+    SlotPtrs sp{};
+    sp.x[0] = x;
+    sp.pt[0] = pt;
+    sp.v[0] = vpart;
+    shrink_walk<SNS, true>(sp, 1, pages, H, stride, perm, item_rec, n_items_max, T, R, dbg);
 }
 
 template <int SNS>
 __global__ __launch_bounds__(256) void k_shrink_mfma_slots(const uint16_t *__restrict__ pages, int32_t H,
-                                                           const SlotPtrs sp, int32_t stride,
+                                                           const SlotPtrs sp, int32_t n, int32_t stride,
                                                            const int32_t *__restrict__ perm,
-                                                           const int4 *__restrict__ item_rec, int32_t T, int32_t R) {
-    shrink_body<SNS, false>((const uint16_t *)sp.x[blockIdx.z], pages, H, sp.pt[blockIdx.z], stride, perm, item_rec,
-                            sp.v[blockIdx.z], T, R);
+                                                           const int4 *__restrict__ item_rec,
+                                                           int32_t n_items_max, int32_t T, int32_t R) {
+    shrink_walk<SNS, false>(sp, n, pages, H, stride, perm, item_rec, n_items_max, T, R);
 }
 
 // v16[t][j] = bf16(s_a * sum_split vpart[split][t][j]) for tokens with an adapter; zero for
@@ -753,30 +795,40 @@ hipError_t launch_prefill(const lora_pool *p, const Plan &plan, const Ws &ws, co
     if (plan.vsplit != VSPLIT) return hipErrorInvalidValue;
     const uint16_t *xh = (const uint16_t *)x, *pages = (const uint16_t *)p->pages;
     const int32_t stride = 2 * p->max_rank, T = (int32_t)plan.T;
-    dim3 g1(plan.n_items_max, VSPLIT, n);
+    // the persistent shrink grid: as many workgroups as the chip holds at once (one per CU with six
+    // stages, two with four), a multiple of 8
     const int sns = plan.T <= 4096 ? 6 : 4;
     const size_t sh_lds = (size_t)sns * SH_STAGE * 2;
+    static int n_cu[64] = {};
+    if (p->device < 0 || p->device >= 64) return hipErrorInvalidDevice;
+    if (n_cu[p->device] == 0) {
+        int c = 0;
+        const hipError_t e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, p->device);
+        if (e != hipSuccess) return e;
+        n_cu[p->device] = c > 0 ? c : 1;
+    }
+    const dim3 g1((unsigned)((n_cu[p->device] * (sns == 6 ? 1 : 2) + 7) / 8 * 8));
     if (dbg) {
         if (sns == 6)
-            hipLaunchKernelGGL(k_shrink_mfma_dbg<6>, dim3(g1.x, g1.y), dim3(256), sh_lds, s, xh, pages, p->hidden,
-                               sp.pt[0], stride, ws.perm, ws.item_rec, sp.v[0], T, plan.rp, *dbg);
+            hipLaunchKernelGGL(k_shrink_mfma_dbg<6>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
+                               ws.perm, ws.item_rec, plan.n_items_max, sp.v[0], T, plan.rp, *dbg);
         else
-            hipLaunchKernelGGL(k_shrink_mfma_dbg<4>, dim3(g1.x, g1.y), dim3(256), sh_lds, s, xh, pages, p->hidden,
-                               sp.pt[0], stride, ws.perm, ws.item_rec, sp.v[0], T, plan.rp, *dbg);
+            hipLaunchKernelGGL(k_shrink_mfma_dbg<4>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
+                               ws.perm, ws.item_rec, plan.n_items_max, sp.v[0], T, plan.rp, *dbg);
     } else if (n == 1) {
         if (sns == 6)
             hipLaunchKernelGGL(k_shrink_mfma<6>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
-                               ws.perm, ws.item_rec, sp.v[0], T, plan.rp);
+                               ws.perm, ws.item_rec, plan.n_items_max, sp.v[0], T, plan.rp);
         else
             hipLaunchKernelGGL(k_shrink_mfma<4>, g1, dim3(256), sh_lds, s, xh, pages, p->hidden, sp.pt[0], stride,
-                               ws.perm, ws.item_rec, sp.v[0], T, plan.rp);
+                               ws.perm, ws.item_rec, plan.n_items_max, sp.v[0], T, plan.rp);
     } else {
         if (sns == 6)
-            hipLaunchKernelGGL(k_shrink_mfma_slots<6>, g1, dim3(256), sh_lds, s, pages, p->hidden, sp, stride,
-                               ws.perm, ws.item_rec, T, plan.rp);
+            hipLaunchKernelGGL(k_shrink_mfma_slots<6>, g1, dim3(256), sh_lds, s, pages, p->hidden, sp, (int32_t)n,
+                               stride, ws.perm, ws.item_rec, plan.n_items_max, T, plan.rp);
         else
-            hipLaunchKernelGGL(k_shrink_mfma_slots<4>, g1, dim3(256), sh_lds, s, pages, p->hidden, sp, stride,
-                               ws.perm, ws.item_rec, T, plan.rp);
+            hipLaunchKernelGGL(k_shrink_mfma_slots<4>, g1, dim3(256), sh_lds, s, pages, p->hidden, sp, (int32_t)n,
+                               stride, ws.perm, ws.item_rec, plan.n_items_max, T, plan.rp);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
