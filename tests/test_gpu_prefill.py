@@ -101,6 +101,29 @@ def test_prefill_integer_exact(T, H, pieces):
     assert not bad, (bad[:10], ids[bad[:10]])
 
 
+def test_prefill_many_adapters_integer_exact():
+    """2000 tokens over 300 adapters (some tokens with none): about 330 shrink work items, so each
+    workgroup of the persistent shrink grid takes several (item, split) units and stops at the first
+    record past the last item.  Integer inputs: the output must equal the oracle's exact result
+    rounded once to bfloat16, on every row."""
+    T, H, n_ad = 2000, 256, 300
+    rng = np.random.default_rng(2000)
+    ranks = [[4, 1, 0, 16, 2, 64, 33, 8][i % 8] for i in range(n_ad)]
+    ids = rng.integers(-1, n_ad, T).astype(np.int32)
+    w = custom(H, ranks, ids, values="int", scales=[1] * n_ad, device="cuda", seed=T)
+    say("case prefill int-exact many adapters", T, H, n_ad)
+    pool = device_pool(w)
+    y = run(pool, w, 0)
+    torch.cuda.synchronize()
+    assert rg.lora_check_device_errors(pool.handle, check=False) == 0, rg.lora_last_error()
+    ref = oracle_y(w, 0)
+    assert np.all(ref == np.round(ref))
+    got = y.cpu().view(torch.int16)
+    want = bf16_round_f64(ref).view(torch.int16)
+    bad = (got != want).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, (bad[:10], ids[bad[:10]])
+
+
 @pytest.mark.parametrize("T,H", [(700, 192), (300, 64)])
 def test_prefill_small_max_rank_integer_exact(T, H):
     """A pool whose largest rank is 16: v rows hold 16 entries, so the low-rank operand loads clamp
